@@ -1,0 +1,69 @@
+"""Seeded synthetic inputs for a layer shard.
+
+This module only draws random numbers and rounds them to the storage dtype;
+it holds none of the layer's arithmetic.  Both the HIP path and the CPU
+oracle take their inputs from here.
+
+Recipe: a torch CPU ``Generator`` seeded with ``1000 * cid + k``, where k is
+the tensor's index in TENSOR_ORDER; values are drawn as float32 ``randn`` and
+scaled (activations and the upstream gradient N(0, 1), weights N(0, 0.02),
+biases 0 unless ``bias_std`` is given), then rounded to bfloat16 with
+round-to-nearest-even for bf16 workloads.  The oracle receives the same
+(rounded) values widened to float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import LayerConfig
+
+TENSOR_ORDER = ["X", "A", "b1", "B", "b2", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo", "bo", "dZ"]
+
+WEIGHT_STD = 0.02
+
+
+def tensor_shapes(cfg: LayerConfig) -> dict:
+    T, h, F = cfg.tokens, cfg.hidden, cfg.ffn
+    return {
+        "X": (T, h), "A": (h, F), "b1": (F,), "B": (F, h), "b2": (h,),
+        "Wq": (h, h), "Wk": (h, h), "Wv": (h, h),
+        "bq": (h,), "bk": (h,), "bv": (h,),
+        "Wo": (h, h), "bo": (h,), "dZ": (T, h),
+    }
+
+
+def storage_dtype(cfg: LayerConfig) -> torch.dtype:
+    return torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+
+
+def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,
+                seed_base: int | None = None) -> dict:
+    """Return {name: CPU tensor in the storage dtype} for the requested tensors."""
+    shapes = tensor_shapes(cfg)
+    base = 1000 * cfg.cid if seed_base is None else seed_base
+    dt = storage_dtype(cfg)
+    out = {}
+    for k, name in enumerate(TENSOR_ORDER):
+        if names is not None and name not in names:
+            continue
+        shape = shapes[name]
+        if name in ("X", "dZ"):
+            std = 1.0
+        elif name.startswith("b"):
+            std = bias_std
+        else:
+            std = WEIGHT_STD
+        if std == 0.0:
+            t = torch.zeros(shape, dtype=torch.float32)
+        else:
+            g = torch.Generator().manual_seed(base + k)
+            t = torch.randn(shape, generator=g, dtype=torch.float32)
+            t.mul_(std)
+        out[name] = t.to(dt)
+    return out
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a stored tensor to a contiguous float64 numpy array."""
+    return np.ascontiguousarray(t.to(torch.float64).numpy())
