@@ -1,0 +1,229 @@
+/*
+ * tpshard.h -- C ABI of libtpshard.so: one rank's shard of a Megatron-style
+ * tensor-parallel transformer layer, forward and backward, on an MI355X
+ * (gfx950) GPU.
+ *
+ * The operations (page "Megatron-LM: what the tensor parallelism paper
+ * actually says"):
+ *   - FFN shard, section "How transformer layers actually decompose": the
+ *     FFN computes GeLU(x W1) W2 with W1 = A [h, F] split by columns and
+ *     W2 = B [F, h] split by rows.  Shard i owns the columns / rows
+ *     C_i = [i*F/t, (i+1)*F/t) and produces a partial sum of the output;
+ *     the t partials add up to the unsharded FFN output.
+ *   - Attention shard, section "The attention heads split": shard i owns
+ *     the H/t heads G_i = [i*H/t, (i+1)*H/t); the Q, K, V projections
+ *     ([h, h] each) are split by the columns of those heads, each head
+ *     runs softmax attention locally, and the output projection Wo [h, h]
+ *     is split by the rows of those heads, giving a partial output.
+ *   - The backward of both (chain rule).  The input-gradient partials of
+ *     the t shards add up to the full input gradient; weight gradients
+ *     land in disjoint blocks.
+ * On one GPU the cross-shard sum (an all-reduce on a real TP group) is
+ * done by tp_sum_partials, for verification.
+ *
+ * Conventions
+ *   - Matrices are row-major and oriented [in, out] as in x*W.  Tokens are
+ *     rows: T = batch*seq, token r = b*seq + j.
+ *   - Weights are passed as the FULL matrices; the library reads only the
+ *     shard's slice (A columns C_i with row stride F, B rows C_i, Wq/Wk/Wv
+ *     columns of G_i, Wo rows of G_i).  Head g owns columns [g*d, (g+1)*d),
+ *     d = h/H.
+ *   - Column-parallel biases (b1, bq, bk, bv) are added inside the shard.
+ *     Row-parallel biases (b2, bo) are NOT added by the shard functions
+ *     (they would be counted t times); tp_sum_partials adds them once.
+ *   - GeLU is the exact form u * Phi(u); attention scores are scaled by
+ *     1/sqrt(d); the causal mask allows key m for query j iff m <= j.
+ *   - Data types: dims.act = TP_BF16: X, weights, biases, activations,
+ *     saved tensors and partial outputs are bfloat16; GEMMs and softmax
+ *     accumulate in fp32; weight and bias gradients are fp32.
+ *     dims.act = TP_FP32: everything is fp32 (fp32 FMA arithmetic).
+ *   - Gradients are written (overwritten), never accumulated, into the
+ *     shard's block of the full-size caller buffers; entries outside the
+ *     block are not touched.
+ *   - Ownership: the caller allocates every buffer (device memory),
+ *     including `saved` (written by fwd, read by bwd; size from
+ *     tp_*_saved_bytes) and `work` (scratch of the backward; size from
+ *     tp_*_work_bytes).  The library allocates no device memory; its only
+ *     mutable global state is the measurement hook (tp_profile_enable).
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream) and the call returns without synchronising.
+ *     Execution faults surface at the caller's next synchronisation.
+ *   - Errors: every argument is validated on the host BEFORE any HIP call
+ *     or enqueue; on failure nothing is written and a tp_status is
+ *     returned.  A failed launch returns TP_EHIP.  No C++ exception
+ *     crosses this boundary.
+ *   - Alignment: every device pointer must be 16-byte aligned; hidden,
+ *     F/t and (H/t)*d must be multiples of 8.  Supported head dims:
+ *     32, 64, 96, 128 (bf16) and 8..128 in steps of 8 (fp32).
+ *   - Calls on different streams may run concurrently if their output
+ *     buffers do not overlap.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_EINVAL = 1,        /* NULL required pointer, non-positive size, NULL dims      */
+    TP_EDIVIDE = 2,       /* t does not divide H or F, or H does not divide h         */
+    TP_ESHARD = 3,        /* shard index outside [0, t) or t < 1                      */
+    TP_EALIGN = 4,        /* pointer not 16-byte aligned or size not a multiple of 8  */
+    TP_EDTYPE = 5,        /* dims.act is neither TP_FP32 nor TP_BF16                  */
+    TP_EUNSUPPORTED = 6,  /* head dimension not supported                             */
+    TP_EHIP = 7,          /* a kernel launch failed                                   */
+    TP_ESIZE = 8          /* work buffer smaller than tp_*_work_bytes                 */
+} tp_status;
+
+typedef enum { TP_FP32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef struct {
+    int64_t batch, seq;      /* T = batch * seq tokens                         */
+    int64_t hidden;          /* h                                              */
+    int64_t heads;           /* H (full, unsharded)                            */
+    int64_t ffn;             /* F (full, unsharded; 4h in the pages' models)   */
+    int32_t causal;          /* 1: causal mask, 0: none                        */
+    int32_t act;             /* tp_dtype of activations / weights / partials   */
+} tp_dims;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int tp_version(void);
+
+/* Human-readable text of a tp_status (static storage, never NULL). */
+const char* tp_status_string(int status);
+
+/*
+ * Validate dims / shard / degree only (no pointers, no HIP call).
+ * Returns TP_OK or the tp_status the entry points would return.
+ */
+int tp_check_dims(const tp_dims* dims, int shard, int degree);
+
+/*
+ * Bytes of the `saved` buffer.  Layout (each region 256-byte aligned, in
+ * this order, elements of dims.act unless noted):
+ *   MLP:       U [T, F/t]  (pre-GeLU),  Y [T, F/t]  (post-GeLU)
+ *   attention: QKV [T, 3w] (columns [0,w) = Q, [w,2w) = K, [2w,3w) = V of
+ *              the shard's heads, w = (H/t)*d, head-local column c of
+ *              local head g at g*d + c), O [T, w], LSE [batch, H/t, seq]
+ *              fp32 (natural-log log-sum-exp of each query's scaled scores)
+ * Returns 0 if the dims are invalid.
+ */
+size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree);
+size_t tp_attn_saved_bytes(const tp_dims* dims, int shard, int degree);
+
+/* Bytes of the `work` buffer the backward needs (0 if the dims are invalid). */
+size_t tp_mlp_work_bytes(const tp_dims* dims, int shard, int degree);
+size_t tp_attn_work_bytes(const tp_dims* dims, int shard, int degree);
+
+/*
+ * FFN shard forward ("How transformer layers actually decompose"):
+ *   U = X A[:, C_i] + b1[C_i],  Y = GeLU(U),  Z_part = Y B[C_i, :].
+ * X [T, h]; A [h, F]; b1 [F] or NULL (zero); B [F, h]; Z_part [T, h] out;
+ * saved: see tp_mlp_saved_bytes.
+ */
+int tp_mlp_shard_fwd(const tp_dims* dims, int shard, int degree,
+                     const void* X, const void* A, const void* b1, const void* B,
+                     void* Z_part, void* saved, void* stream);
+
+/*
+ * FFN shard backward, given G = dZ [T, h] (the same G reaches every shard):
+ *   dY = G B[C_i, :]^T,  dU = dY * GeLU'(U),
+ *   dB[C_i, :] = Y^T G,  dA[:, C_i] = X^T dU,  db1[C_i] = column sums of dU,
+ *   dX_part = dU A[:, C_i]^T.
+ * dA [h, F], db1 [F] (NULL: skipped), dB [F, h] are full-size fp32 buffers;
+ * only the shard's block is written.  dX_part [T, h] in dims.act.
+ * saved: as written by tp_mlp_shard_fwd with the same arguments.
+ */
+int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree,
+                     const void* X, const void* A, const void* B,
+                     const void* saved, const void* dZ,
+                     void* dX_part, float* dA, float* db1, float* dB,
+                     void* work, size_t work_bytes, void* stream);
+
+/*
+ * Attention shard forward ("The attention heads split"), for every batch
+ * element and each local head g of G_i:
+ *   Q/K/V = X W{q,k,v}[:, head cols] + b{q,k,v}[head cols],
+ *   S = Q K^T / sqrt(d) (+ causal mask), P = row softmax(S), O = P V,
+ *   Z_part = O Wo[rows of G_i, :].
+ * X [T, h]; Wq, Wk, Wv, Wo [h, h]; bq, bk, bv [h] or NULL; Z_part [T, h] out.
+ */
+int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv,
+                      const void* bq, const void* bk, const void* bv, const void* Wo,
+                      void* Z_part, void* saved, void* stream);
+
+/*
+ * Attention shard backward, given G = dZ [T, h]:
+ *   dWo[rows of G_i] = O^T G, dO = G Wo[rows of G_i]^T,
+ *   per head: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *             dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d),
+ *   dW{q,k,v}[:, head cols] = X^T d{Q,K,V}, db{q,k,v} = column sums,
+ *   dX_part = dQ Wq[:, cols]^T + dK Wk[:, cols]^T + dV Wv[:, cols]^T.
+ * dWq, dWk, dWv, dWo [h, h] and dbq, dbk, dbv [h] (each NULL: all three
+ * bias gradients skipped) are full-size fp32 buffers; only the shard's
+ * block is written.
+ */
+int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree,
+                      const void* X, const void* Wq, const void* Wk, const void* Wv,
+                      const void* Wo, const void* saved, const void* dZ,
+                      void* dX_part, float* dWq, float* dWk, float* dWv,
+                      float* dbq, float* dbk, float* dbv, float* dWo,
+                      void* work, size_t work_bytes, void* stream);
+
+/*
+ * Measurement hook.  Steps of the path, in launch order:
+ */
+enum {
+    TP_STEP_MLP_UP = 0,      /* U = X A_i + b1, Y = GeLU(U)         (column-parallel GEMM) */
+    TP_STEP_MLP_DOWN = 1,    /* Z_part = Y B_i                      (row-parallel GEMM)    */
+    TP_STEP_QKV = 2,         /* QKV = X W{q,k,v}_i + b               (column-parallel GEMM) */
+    TP_STEP_ATTN_CORE = 3,   /* softmax attention forward -> O, LSE                          */
+    TP_STEP_ATTN_OUT = 4,    /* Z_part = O Wo_i                     (row-parallel GEMM)    */
+    TP_STEP_MLP_DU = 5,      /* dU = (dZ B_i^T) * GeLU'(U)                                  */
+    TP_STEP_MLP_DB = 6,      /* dB_i = Y^T dZ                                               */
+    TP_STEP_MLP_DA = 7,      /* dA_i = X^T dU                                               */
+    TP_STEP_MLP_DB1 = 8,     /* db1_i = column sums of dU                                   */
+    TP_STEP_MLP_DX = 9,      /* dX_part = dU A_i^T                                          */
+    TP_STEP_ATTN_DO = 10,    /* dO = dZ Wo_i^T                                              */
+    TP_STEP_ATTN_DWO = 11,   /* dWo_i = O^T dZ                                              */
+    TP_STEP_ATTN_CORE_BWD = 12, /* softmax attention backward -> dQ, dK, dV                 */
+    TP_STEP_ATTN_DW = 13,    /* dW{q,k,v}_i = X^T d{Q,K,V}                                  */
+    TP_STEP_ATTN_DBIAS = 14, /* db{q,k,v}_i = column sums                                   */
+    TP_STEP_ATTN_DX = 15,    /* dX_part = d{Q,K,V} W{q,k,v}_i^T                             */
+    TP_NUM_STEPS = 16
+};
+
+/*
+ * While enabled, every launch of step s is bracketed by
+ * hipEventRecord(events[2*(s*npairs + k)], stream) and
+ * hipEventRecord(events[2*(s*npairs + k) + 1], stream), where k counts that
+ * step's launches modulo npairs.  `events` is a host array of
+ * 2*TP_NUM_STEPS*npairs hipEvent_t handles created by the caller and must stay
+ * valid until the hook is disabled (events == NULL or npairs == 0).
+ * tp_profile_count(s) returns how many launches of step s were recorded.
+ * For measurement only: the hook is process-wide and not thread-safe.
+ */
+int tp_profile_enable(void* const* events, int npairs);
+int tp_profile_count(int step);
+
+/*
+ * Verification-only local sum that stands in for the all-reduce on one GPU
+ * ("To get the correct final output, you sum the partial results"):
+ *   out[r, c] = sum_p parts[p][r, c] + (bias ? bias[c] : 0), fp32 out.
+ * parts: host array of `nparts` device pointers, each [rows, cols] of
+ * `dtype`; bias [cols] of `dtype` or NULL.
+ */
+int tp_sum_partials(int dtype, int64_t rows, int64_t cols,
+                    const void* const* parts, int nparts, const void* bias,
+                    float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPSHARD_H */

@@ -1,0 +1,435 @@
+// C ABI of the tensor-parallel layer shard (declared in include/tpshard.h).
+//
+// Each entry point validates every argument on the host first (no HIP call
+// before validation passes, nothing written on failure), then enqueues its
+// kernels on the caller's stream:
+//   tp_mlp_shard_fwd : [X*A_i + b1 -> U, GeLU -> Y]  [Y*B_i -> Z_part]
+//   tp_mlp_shard_bwd : [dZ*B_i^T (*) GeLU'(U) -> dU]  [Y^T dZ -> dB_i]
+//                      [X^T dU -> dA_i]  [colsum dU -> db1_i]  [dU*A_i^T -> dX_part]
+//   tp_attn_shard_fwd: [X*[Wq|Wk|Wv]_i + b -> QKV]  [fused attention -> O, LSE]
+//                      [O*Wo_i -> Z_part]
+//   tp_attn_shard_bwd: [dZ*Wo_i^T -> dO]  [O^T dZ -> dWo_i]  [fused attention bwd -> dQKV]
+//                      [X^T dQKV -> dW{q,k,v}_i]  [colsum -> db{q,k,v}_i]
+//                      [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]
+// The shard slices follow page "Megatron-LM: what the tensor parallelism paper
+// actually says": FFN columns/rows C_i ("How transformer layers actually
+// decompose"), head columns/rows G_i ("The attention heads split").
+#include "../../include/tpshard.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <type_traits>
+
+#include "tp_kernels.h"
+
+namespace {
+
+constexpr int SEG_NONE = 1 << 30;
+
+struct Shape {
+    int64_t T, b, s, h, H, F, t, i, Fs, Hs, d, w;
+    bool causal, bf16;
+    int64_t e;  // bytes per element of dims.act
+};
+
+int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
+    if (!dims) return TP_EINVAL;
+    if (dims->act != TP_FP32 && dims->act != TP_BF16) return TP_EDTYPE;
+    if (dims->batch <= 0 || dims->seq <= 0 || dims->hidden <= 0 || dims->heads <= 0 || dims->ffn <= 0)
+        return TP_EINVAL;
+    if (dims->causal != 0 && dims->causal != 1) return TP_EINVAL;
+    if (degree < 1 || shard < 0 || shard >= degree) return TP_ESHARD;
+    if (dims->hidden % dims->heads) return TP_EDIVIDE;
+    if (dims->heads % degree || dims->ffn % degree) return TP_EDIVIDE;
+    Shape s;
+    s.b = dims->batch; s.s = dims->seq; s.T = s.b * s.s;
+    s.h = dims->hidden; s.H = dims->heads; s.F = dims->ffn;
+    s.t = degree; s.i = shard;
+    s.Fs = s.F / degree; s.Hs = s.H / degree; s.d = s.h / s.H; s.w = s.Hs * s.d;
+    s.causal = dims->causal != 0;
+    s.bf16 = dims->act == TP_BF16;
+    s.e = s.bf16 ? 2 : 4;
+    if (s.h % 8 || s.Fs % 8 || s.w % 8) return TP_EALIGN;
+    if (s.bf16) {
+        if (s.d != 32 && s.d != 64 && s.d != 96 && s.d != 128) return TP_EUNSUPPORTED;
+        if (s.w % 64) return TP_EUNSUPPORTED;  // K-segment of the fused QKV backward GEMM
+    } else {
+        if (s.d % 8 || s.d > 128) return TP_EUNSUPPORTED;
+    }
+    // Launch-grid limits (grid y <= 65535 with 64-row tiles; int indices).
+    if (s.T > (int64_t)65535 * 64 || s.b * s.Hs > 65535) return TP_EUNSUPPORTED;
+    if (s.h > INT_MAX / 4 || s.F > INT_MAX / 4) return TP_EUNSUPPORTED;
+    if (o) *o = s;
+    return TP_OK;
+}
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename P>
+inline P* at(P* base, int64_t elems, int64_t esize) {
+    using C = typename std::conditional<std::is_const<P>::value, const char, char>::type;
+    return reinterpret_cast<P*>(reinterpret_cast<C*>(base) + elems * esize);
+}
+
+struct MlpSaved {
+    int64_t U, Y, total;
+};
+MlpSaved mlp_saved(const Shape& s) {
+    const int64_t u = align256(s.T * s.Fs * s.e);
+    return {0, u, 2 * u};
+}
+
+struct AttnSaved {
+    int64_t QKV, O, LSE, total;
+};
+AttnSaved attn_saved(const Shape& s) {
+    const int64_t q = align256(s.T * 3 * s.w * s.e);
+    const int64_t o = align256(s.T * s.w * s.e);
+    const int64_t l = align256(s.b * s.Hs * s.s * 4);
+    return {0, q, q + o, q + o + l};
+}
+
+struct MlpWork {
+    int64_t dU, cs, total;
+};
+MlpWork mlp_work(const Shape& s) {
+    const int64_t du = align256(s.T * s.Fs * s.e);
+    const int64_t cs = align256(tp::colsum_work_floats(s.Fs) * 4);
+    return {0, du, du + cs};
+}
+
+struct AttnWork {
+    int64_t dO, dQKV, Dq, cs, total;
+};
+AttnWork attn_work(const Shape& s) {
+    const int64_t dO = align256(s.T * s.w * s.e);
+    const int64_t dq = align256(s.T * 3 * s.w * s.e);
+    const int64_t D = align256(s.b * s.Hs * s.s * 4);
+    const int64_t cs = align256(tp::colsum_work_floats(3 * s.w) * 4);
+    return {0, dO, dO + dq, dO + dq + D, dO + dq + D + cs};
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_EHIP; }
+
+// Measurement hook (tp_profile_enable): event pairs around each step's launches.
+struct Prof {
+    void* const* events = nullptr;
+    int npairs = 0;
+    int count[TP_NUM_STEPS] = {};
+};
+Prof g_prof;
+
+struct StepTimer {
+    int step;
+    hipStream_t st;
+    hipEvent_t stop = nullptr;
+    StepTimer(int s, hipStream_t stream) : step(s), st(stream) {
+        if (!g_prof.events || g_prof.npairs <= 0) return;
+        const int k = g_prof.count[s] % g_prof.npairs;
+        const int base = 2 * (s * g_prof.npairs + k);
+        hipEventRecord(static_cast<hipEvent_t>(g_prof.events[base]), st);
+        stop = static_cast<hipEvent_t>(g_prof.events[base + 1]);
+        g_prof.count[s]++;
+    }
+    ~StepTimer() {
+        if (stop) hipEventRecord(stop, st);
+    }
+};
+
+inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
+    StepTimer t(step, st);
+    return s.bf16 ? tp::gemm_bf16(g, st) : tp::gemm_f32(g, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_version(void) { return 100; }
+
+const char* tp_status_string(int status) {
+    switch (status) {
+        case TP_OK: return "ok";
+        case TP_EINVAL: return "invalid argument (NULL pointer, non-positive size or bad flag)";
+        case TP_EDIVIDE: return "degree must divide heads and ffn, and heads must divide hidden";
+        case TP_ESHARD: return "shard index out of range [0, degree)";
+        case TP_EALIGN: return "pointer not 16-byte aligned or size not a multiple of 8";
+        case TP_EDTYPE: return "unknown dtype";
+        case TP_EUNSUPPORTED: return "unsupported shape (head dimension or size limit)";
+        case TP_EHIP: return "HIP kernel launch failed";
+        case TP_ESIZE: return "work buffer smaller than required";
+        default: return "unknown status";
+    }
+}
+
+int tp_check_dims(const tp_dims* dims, int shard, int degree) { return derive(dims, shard, degree, nullptr); }
+
+int tp_profile_enable(void* const* events, int npairs) {
+    if (events && npairs > 0) {
+        for (int i = 0; i < 2 * TP_NUM_STEPS * npairs; ++i)
+            if (!events[i]) return TP_EINVAL;
+        g_prof.events = events;
+        g_prof.npairs = npairs;
+    } else {
+        g_prof.events = nullptr;
+        g_prof.npairs = 0;
+    }
+    for (int i = 0; i < TP_NUM_STEPS; ++i) g_prof.count[i] = 0;
+    return TP_OK;
+}
+
+int tp_profile_count(int step) { return (step >= 0 && step < TP_NUM_STEPS) ? g_prof.count[step] : -1; }
+
+size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)mlp_saved(s).total : 0;
+}
+
+size_t tp_attn_saved_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)attn_saved(s).total : 0;
+}
+
+size_t tp_mlp_work_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)mlp_work(s).total : 0;
+}
+
+size_t tp_attn_work_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)attn_work(s).total : 0;
+}
+
+int tp_mlp_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, const void* A, const void* b1,
+                     const void* B, void* Z_part, void* saved, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !A || !B || !Z_part || !saved) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Z_part) || !aligned16(saved) ||
+        (b1 && !aligned16(b1)))
+        return TP_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const MlpSaved L = mlp_saved(s);
+    void* U = at(saved, L.U, 1);
+    void* Y = at(saved, L.Y, 1);
+    const int64_t c0 = s.i * s.Fs;
+
+    tp::GemmDesc g1;  // U = X A[:, C_i] + b1[C_i];  Y = GeLU(U)
+    g1.M = (int)s.T; g1.N = (int)s.Fs; g1.K = (int)s.h;
+    g1.A = X; g1.lda = s.h; g1.a_kcontig = true;
+    g1.B[0] = at(A, c0, s.e); g1.ldb = s.F; g1.b_kcontig = false;
+    g1.C[0] = U; g1.ldc = s.Fs; g1.C2 = Y; g1.ldc2 = s.Fs;
+    g1.bias[0] = b1 ? at(b1, c0, s.e) : nullptr;
+    g1.epi = tp::EPI_BIAS_GELU;
+    hipError_t e = gemm(s, g1, st, TP_STEP_MLP_UP);
+    if (e != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc g2;  // Z_part = Y B[C_i, :]
+    g2.M = (int)s.T; g2.N = (int)s.h; g2.K = (int)s.Fs;
+    g2.A = Y; g2.lda = s.Fs; g2.a_kcontig = true;
+    g2.B[0] = at(B, c0 * s.h, s.e); g2.ldb = s.h; g2.b_kcontig = false;
+    g2.C[0] = Z_part; g2.ldc = s.h;
+    g2.epi = tp::EPI_STORE;
+    return hip_status(gemm(s, g2, st, TP_STEP_MLP_DOWN));
+}
+
+int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, const void* A, const void* B,
+                     const void* saved, const void* dZ, void* dX_part, float* dA, float* db1, float* dB, void* work,
+                     size_t work_bytes, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !A || !B || !saved || !dZ || !dX_part || !dA || !dB || !work) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(saved) || !aligned16(dZ) ||
+        !aligned16(dX_part) || !aligned16(dA) || !aligned16(dB) || !aligned16(work) || (db1 && !aligned16(db1)))
+        return TP_EALIGN;
+    const MlpWork W = mlp_work(s);
+    if (work_bytes < (size_t)W.total) return TP_ESIZE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const MlpSaved L = mlp_saved(s);
+    const void* U = at(saved, L.U, 1);
+    const void* Y = at(saved, L.Y, 1);
+    void* dU = at(work, W.dU, 1);
+    float* cs = static_cast<float*>(at(work, W.cs, 1));
+    const int64_t c0 = s.i * s.Fs;
+
+    tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * GeLU'(U)
+    g.M = (int)s.T; g.N = (int)s.Fs; g.K = (int)s.h;
+    g.A = dZ; g.lda = s.h; g.a_kcontig = true;
+    g.B[0] = at(B, c0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
+    g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
+    g.epi = tp::EPI_GELU_BWD;
+    if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc gb;  // dB[C_i, :] = Y^T dZ
+    gb.M = (int)s.Fs; gb.N = (int)s.h; gb.K = (int)s.T;
+    gb.A = Y; gb.lda = s.Fs; gb.a_kcontig = false;
+    gb.B[0] = dZ; gb.ldb = s.h; gb.b_kcontig = false;
+    gb.C[0] = dB + c0 * s.h; gb.ldc = s.h; gb.out_f32 = true;
+    if (gemm(s, gb, st, TP_STEP_MLP_DB) != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc ga;  // dA[:, C_i] = X^T dU
+    ga.M = (int)s.h; ga.N = (int)s.Fs; ga.K = (int)s.T;
+    ga.A = X; ga.lda = s.h; ga.a_kcontig = false;
+    ga.B[0] = dU; ga.ldb = s.Fs; ga.b_kcontig = false;
+    ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
+    if (gemm(s, ga, st, TP_STEP_MLP_DA) != hipSuccess) return TP_EHIP;
+
+    if (db1) {  // db1[C_i] = column sums of dU
+        float* outs[3] = {db1 + c0, nullptr, nullptr};
+        StepTimer t(TP_STEP_MLP_DB1, st);
+        if (tp::colsum(s.bf16, dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, st) != hipSuccess) return TP_EHIP;
+    }
+
+    tp::GemmDesc gx;  // dX_part = dU A[:, C_i]^T
+    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)s.Fs;
+    gx.A = dU; gx.lda = s.Fs; gx.a_kcontig = true;
+    gx.B[0] = at(A, c0, s.e); gx.ldb = s.F; gx.b_kcontig = true;
+    gx.C[0] = dX_part; gx.ldc = s.h;
+    return hip_status(gemm(s, gx, st, TP_STEP_MLP_DX));
+}
+
+int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq, const void* Wk,
+                      const void* Wv, const void* bq, const void* bk, const void* bv, const void* Wo, void* Z_part,
+                      void* saved, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !Wq || !Wk || !Wv || !Wo || !Z_part || !saved) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wo) ||
+        !aligned16(Z_part) || !aligned16(saved) || (bq && !aligned16(bq)) || (bk && !aligned16(bk)) ||
+        (bv && !aligned16(bv)))
+        return TP_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const AttnSaved L = attn_saved(s);
+    void* QKV = at(saved, L.QKV, 1);
+    void* O = at(saved, L.O, 1);
+    float* lse = static_cast<float*>(at(saved, L.LSE, 1));
+    const int64_t col0 = s.i * s.w;
+
+    tp::GemmDesc g;  // QKV = X [Wq|Wk|Wv][:, cols of G_i] + [bq|bk|bv]
+    g.M = (int)s.T; g.N = (int)(3 * s.w); g.K = (int)s.h;
+    g.A = X; g.lda = s.h; g.a_kcontig = true;
+    const void* W3[3] = {Wq, Wk, Wv};
+    const void* b3[3] = {bq, bk, bv};
+    for (int z = 0; z < 3; ++z) {
+        g.B[z] = at(W3[z], col0, s.e);
+        g.C[z] = at(QKV, z * s.w, s.e);
+        g.bias[z] = b3[z] ? at(b3[z], col0, s.e) : nullptr;
+    }
+    g.ldb = s.h; g.b_kcontig = false; g.bseg = (int)s.w;
+    g.ldc = 3 * s.w; g.cseg = (int)s.w;
+    g.epi = tp::EPI_BIAS;
+    if (gemm(s, g, st, TP_STEP_QKV) != hipSuccess) return TP_EHIP;
+
+    tp::AttnDesc ad;
+    ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
+    ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = O; ad.ld_o = s.w; ad.lse = lse;
+    {
+        StepTimer t(TP_STEP_ATTN_CORE, st);
+        if ((s.bf16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st)) != hipSuccess) return TP_EHIP;
+    }
+
+    tp::GemmDesc go;  // Z_part = O Wo[rows of G_i, :]
+    go.M = (int)s.T; go.N = (int)s.h; go.K = (int)s.w;
+    go.A = O; go.lda = s.w; go.a_kcontig = true;
+    go.B[0] = at(Wo, col0 * s.h, s.e); go.ldb = s.h; go.b_kcontig = false;
+    go.C[0] = Z_part; go.ldc = s.h;
+    return hip_status(gemm(s, go, st, TP_STEP_ATTN_OUT));
+}
+
+int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq, const void* Wk,
+                      const void* Wv, const void* Wo, const void* saved, const void* dZ, void* dX_part, float* dWq,
+                      float* dWk, float* dWv, float* dbq, float* dbk, float* dbv, float* dWo, void* work,
+                      size_t work_bytes, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !Wq || !Wk || !Wv || !Wo || !saved || !dZ || !dX_part || !dWq || !dWk || !dWv || !dWo || !work)
+        return TP_EINVAL;
+    const bool bias_grads = dbq && dbk && dbv;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wo) ||
+        !aligned16(saved) || !aligned16(dZ) || !aligned16(dX_part) || !aligned16(dWq) || !aligned16(dWk) ||
+        !aligned16(dWv) || !aligned16(dWo) || !aligned16(work) ||
+        (bias_grads && (!aligned16(dbq) || !aligned16(dbk) || !aligned16(dbv))))
+        return TP_EALIGN;
+    const AttnWork W = attn_work(s);
+    if (work_bytes < (size_t)W.total) return TP_ESIZE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const AttnSaved L = attn_saved(s);
+    const void* QKV = at(saved, L.QKV, 1);
+    const void* O = at(saved, L.O, 1);
+    const float* lse = static_cast<const float*>(at(saved, L.LSE, 1));
+    void* dO = at(work, W.dO, 1);
+    void* dQKV = at(work, W.dQKV, 1);
+    float* Dq = static_cast<float*>(at(work, W.Dq, 1));
+    float* cs = static_cast<float*>(at(work, W.cs, 1));
+    const int64_t col0 = s.i * s.w;
+
+    tp::GemmDesc g;  // dO = dZ Wo[rows of G_i, :]^T
+    g.M = (int)s.T; g.N = (int)s.w; g.K = (int)s.h;
+    g.A = dZ; g.lda = s.h; g.a_kcontig = true;
+    g.B[0] = at(Wo, col0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
+    g.C[0] = dO; g.ldc = s.w;
+    if (gemm(s, g, st, TP_STEP_ATTN_DO) != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc gw;  // dWo[rows of G_i, :] = O^T dZ
+    gw.M = (int)s.w; gw.N = (int)s.h; gw.K = (int)s.T;
+    gw.A = O; gw.lda = s.w; gw.a_kcontig = false;
+    gw.B[0] = dZ; gw.ldb = s.h; gw.b_kcontig = false;
+    gw.C[0] = dWo + col0 * s.h; gw.ldc = s.h; gw.out_f32 = true;
+    if (gemm(s, gw, st, TP_STEP_ATTN_DWO) != hipSuccess) return TP_EHIP;
+
+    tp::AttnDesc ad;
+    ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
+    ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = const_cast<void*>(O); ad.ld_o = s.w;
+    ad.lse = const_cast<float*>(lse); ad.dO = dO; ad.Dq = Dq; ad.dqkv = dQKV;
+    {
+        StepTimer t(TP_STEP_ATTN_CORE_BWD, st);
+        if ((s.bf16 ? tp::attn_bwd_bf16(ad, st) : tp::attn_bwd_f32(ad, st)) != hipSuccess) return TP_EHIP;
+    }
+
+    tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV
+    gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
+    gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
+    gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
+    float* dW3[3] = {dWq, dWk, dWv};
+    for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
+    gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
+    if (gemm(s, gq, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
+
+    if (bias_grads) {  // db{q,k,v}[cols of G_i] = column sums of dQKV
+        float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
+        StepTimer t(TP_STEP_ATTN_DBIAS, st);
+        if (tp::colsum(s.bf16, dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, st) != hipSuccess) return TP_EHIP;
+    }
+
+    tp::GemmDesc gx;  // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T
+    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)(3 * s.w);
+    gx.A = dQKV; gx.lda = 3 * s.w; gx.a_kcontig = true;
+    const void* W3[3] = {Wq, Wk, Wv};
+    for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
+    gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
+    gx.C[0] = dX_part; gx.ldc = s.h;
+    return hip_status(gemm(s, gx, st, TP_STEP_ATTN_DX));
+}
+
+int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts, const void* bias,
+                    float* out, void* stream) {
+    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (rows <= 0 || cols <= 0 || nparts < 1 || !parts || !out) return TP_EINVAL;
+    for (int k = 0; k < nparts; ++k) {
+        if (!parts[k]) return TP_EINVAL;
+        if (!aligned16(parts[k])) return TP_EALIGN;
+    }
+    if (!aligned16(out) || (bias && !aligned16(bias))) return TP_EALIGN;
+    return hip_status(tp::sum_partials(dtype == TP_BF16, rows, cols, parts, nparts, bias, out,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Small memory-bound kernels of the shard: bias-gradient column sums and the
+// verification-only sum of shard partials that stands in for the all-reduce
+// on one GPU (page "Megatron-LM: what the tensor parallelism paper actually
+// says", section "How transformer layers actually decompose": the partial
+// results are summed to get the output).
+#include "tp_common.h"
+#include "tp_kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr int COLSUM_SPLITS = 64;
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_partial_kernel(const T* __restrict__ X, int64_t rows, int64_t cols,
+                                                             int64_t ld, float* __restrict__ work) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= cols) return;
+    const int64_t chunk = (rows + COLSUM_SPLITS - 1) / COLSUM_SPLITS;
+    const int64_t r0 = blockIdx.y * chunk, r1 = min(rows, r0 + chunk);
+    float acc = 0.f;
+    for (int64_t r = r0; r < r1; ++r) acc += to_f<T>(X[r * ld + c]);
+    work[(int64_t)blockIdx.y * cols + c] = acc;
+}
+
+struct Out3 {
+    float* p[3];
+};
+
+__global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restrict__ work, int64_t cols,
+                                                           Out3 out, int seg) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= cols) return;
+    float acc = 0.f;
+    for (int i = 0; i < COLSUM_SPLITS; ++i) acc += work[(int64_t)i * cols + c];
+    const int sg = (int)(c / seg);
+    out.p[sg][c - (int64_t)sg * seg] = acc;
+}
+
+constexpr int MAXP = 16;
+struct Parts {
+    const void* p[MAXP];
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) sum_partials_kernel(int64_t rows, int64_t cols, Parts parts, int n,
+                                                           const T* __restrict__ bias, int accumulate,
+                                                           float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * cols) return;
+    float acc = accumulate ? out[i] : (bias ? to_f<T>(bias[i % cols]) : 0.f);
+    for (int k = 0; k < n; ++k) acc += to_f<T>(static_cast<const T*>(parts.p[k])[i]);
+    out[i] = acc;
+}
+
+}  // namespace
+
+int64_t colsum_work_floats(int64_t cols) { return (int64_t)COLSUM_SPLITS * cols; }
+
+hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t ld, float* const out[3],
+                  int seg, float* work, hipStream_t s) {
+    if (cols <= 0) return hipSuccess;
+    dim3 g1((unsigned)((cols + 255) / 256), COLSUM_SPLITS);
+    if (bf16)
+        hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, g1, dim3(256), 0, s, static_cast<const bf16_t*>(X), rows,
+                           cols, ld, work);
+    else
+        hipLaunchKernelGGL(colsum_partial_kernel<float>, g1, dim3(256), 0, s, static_cast<const float*>(X), rows,
+                           cols, ld, work);
+    Out3 o;
+    for (int i = 0; i < 3; ++i) o.p[i] = out[i] ? out[i] : out[0];
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(work), cols, o, seg);
+    return hipGetLastError();
+}
+
+hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const* parts, int nparts,
+                        const void* bias, float* out, hipStream_t s) {
+    const int64_t n = rows * cols;
+    if (n <= 0) return hipSuccess;
+    dim3 grid((unsigned)((n + 255) / 256));
+    for (int k0 = 0; k0 < nparts || k0 == 0; k0 += MAXP) {
+        Parts P;
+        const int cnt = nparts - k0 < MAXP ? nparts - k0 : MAXP;
+        for (int i = 0; i < MAXP; ++i) P.p[i] = i < cnt ? parts[k0 + i] : nullptr;
+        if (bf16)
+            hipLaunchKernelGGL(sum_partials_kernel<bf16_t>, grid, dim3(256), 0, s, rows, cols, P, cnt,
+                               static_cast<const bf16_t*>(bias), k0 > 0 ? 1 : 0, out);
+        else
+            hipLaunchKernelGGL(sum_partials_kernel<float>, grid, dim3(256), 0, s, rows, cols, P, cnt,
+                               static_cast<const float*>(bias), k0 > 0 ? 1 : 0, out);
+        if (nparts == 0) break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tp

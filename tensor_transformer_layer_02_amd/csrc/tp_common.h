@@ -1,0 +1,59 @@
+// Shared device-side definitions of the gfx950 kernels: storage types,
+// bf16 rounding, GeLU, MFMA vector types and launch plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+typedef uint16_t bf16_t;  // bfloat16 storage (raw bits)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Two fp32 -> packed pair of bf16 (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// GeLU(u) = u * Phi(u) with Phi(u) = (1 + erf(u / sqrt 2)) / 2 (exact form).
+__device__ __forceinline__ float gelu_f(float u) {
+    return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+}
+
+// d/du GeLU(u) = Phi(u) + u * phi(u), phi(u) = exp(-u^2/2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_prime_f(float u) {
+    const float Phi = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
+    const float phi = 0.39894228040143268f * __expf(-0.5f * u * u);
+    return Phi + u * phi;
+}
+
+// Bit-level reinterpretations between 16-byte vector types.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+}  // namespace tp

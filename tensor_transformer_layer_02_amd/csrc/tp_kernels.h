@@ -1,0 +1,80 @@
+// Host-side launch descriptors of the gfx950 kernels (shared by the C-ABI
+// implementation and the kernel translation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+enum Epi : int {
+    EPI_STORE = 0,      // C = acc (act dtype, or fp32 when out_f32)
+    EPI_BIAS = 1,       // C = acc + bias[n]
+    EPI_BIAS_GELU = 2,  // C = U = acc + bias[n]; C2 = Y = GeLU(U)
+    EPI_GELU_BWD = 3,   // C = acc * GeLU'(aux[m, n])
+};
+
+// C[M, N] (+epilogue) = sum_k A(m, k) B(k, n).
+//   A(m, k) = A[m*lda + k]   if a_kcontig, else A[k*lda + m]
+//   B(k, n) = Bp[n*ldb + k]  if b_kcontig, else Bp[k*ldb + n]
+// B may be split into up to 3 segments of length bseg, along N (b_kseg = 0)
+// or along K (b_kseg = 1); the index inside a segment is local to it.
+// C (and bias) may be split into up to 3 segments of length cseg along N.
+struct GemmDesc {
+    int M = 0, N = 0, K = 0;
+    const void* A = nullptr;
+    int64_t lda = 0;
+    bool a_kcontig = true;
+    const void* B[3] = {nullptr, nullptr, nullptr};
+    int64_t ldb = 0;
+    bool b_kcontig = false;
+    bool b_kseg = false;
+    int bseg = 1 << 30;
+    void* C[3] = {nullptr, nullptr, nullptr};
+    int64_t ldc = 0;
+    int cseg = 1 << 30;
+    bool out_f32 = false;         // C stored as fp32 (weight gradients)
+    void* C2 = nullptr;           // Y of EPI_BIAS_GELU
+    int64_t ldc2 = 0;
+    const void* bias[3] = {nullptr, nullptr, nullptr};
+    const void* aux = nullptr;    // U of EPI_GELU_BWD
+    int64_t ldaux = 0;
+    int epi = EPI_STORE;
+};
+
+// bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
+hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s);
+// fp32 operands and outputs, fp32 FMA arithmetic.
+hipError_t gemm_f32(const GemmDesc& d, hipStream_t s);
+
+struct AttnDesc {
+    int batch = 0, seq = 0, heads = 0;  // heads of this shard (H/t)
+    int dh = 0;                         // head dim
+    int causal = 1;
+    const void* qkv = nullptr;          // [T, 3w]
+    int64_t ld_qkv = 0;                 // 3w
+    void* O = nullptr;                  // [T, w]
+    int64_t ld_o = 0;                   // w
+    float* lse = nullptr;               // [batch, heads, seq]
+    // backward
+    const void* dO = nullptr;           // [T, w]
+    float* Dq = nullptr;                // [batch, heads, seq]
+    void* dqkv = nullptr;               // [T, 3w]
+};
+
+hipError_t attn_fwd_bf16(const AttnDesc& a, hipStream_t s);
+hipError_t attn_bwd_bf16(const AttnDesc& a, hipStream_t s);
+hipError_t attn_fwd_f32(const AttnDesc& a, hipStream_t s);
+hipError_t attn_bwd_f32(const AttnDesc& a, hipStream_t s);
+
+// out[c] = sum_r X[r*ld + c] over rows, fp32, into up to 3 column segments of length seg.
+// Deterministic two-pass reduction; `work` holds colsum_work_floats(cols) floats.
+int64_t colsum_work_floats(int64_t cols);
+hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t ld,
+                  float* const out[3], int seg, float* work, hipStream_t s);
+
+// out = sum_p parts[p] + bias (fp32 out).
+hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const* parts,
+                        int nparts, const void* bias, float* out, hipStream_t s);
+
+}  // namespace tp

@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from tensor_transformer_layer_02_amd.configs import LayerConfig
+from tensor_transformer_layer_02_amd.inputs import as_f64
+
+# max |gpu - oracle| / max |oracle| per output tensor
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def relerr(gpu, ref) -> float:
+    g = gpu.detach().to("cpu", torch.float64).numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.all(np.isfinite(g)), "non-finite values in GPU output"
+    den = np.max(np.abs(r))
+    return float(np.max(np.abs(g - r)) / den) if den > 0 else float(np.max(np.abs(g)))
+
+
+def oracle_inputs(inp: dict) -> dict:
+    return {k: as_f64(v) for k, v in inp.items()}
+
+
+def oracle_shard(cfg: LayerConfig, p: dict, i: int, degree: int | None = None,
+                 grads: dict | None = None) -> dict:
+    """Oracle forward + backward of shard i (float64)."""
+    t = cfg.degree if degree is None else degree
+    d = cfg.dims()
+    args = [p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")]
+    mf = oracle.mlp_shard_fwd(d, i, t, p["X"], p["A"], p["b1"], p["B"])
+    af = oracle.attn_shard_fwd(d, i, t, *args)
+    out = {"Z_mlp": mf["Z"], "U": mf["U"], "Y": mf["Y"], "Z_attn": af["Z"],
+           "QKV": np.concatenate([af["Q"], af["K"], af["V"]], axis=1), "O": af["O"], "LSE": af["lse"]}
+    if cfg.backward or grads is not None:
+        g = grads if grads is not None else {}
+        mb = oracle.mlp_shard_bwd(d, i, t, p["X"], p["A"], p["b1"], p["B"], p["dZ"],
+                                  dA=g.get("dA"), db1=g.get("db1"), dB=g.get("dB"))
+        ab = oracle.attn_shard_bwd(d, i, t, *args, p["dZ"], out=g)
+        g.update({"dA": mb["dA"], "db1": mb["db1"], "dB": mb["dB"]})
+        out["dX_mlp"] = mb["dX"]
+        out["dX_attn"] = ab["dX"]
+        out["grads"] = g
+    return out
+
+
+def check(name, gpu, ref, tol, report):
+    e = relerr(gpu, ref)
+    report.append((name, e))
+    assert e <= tol, f"{name}: max rel err {e:.3e} > {tol:.0e}"

@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/tpshard.h declares, sizes the saved/work buffers as documented, and
+rejects bad arguments with the documented status before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_transformer_layer_02_amd import tpshard as tp
+from tensor_transformer_layer_02_amd.configs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tp.LIB_PATH):
+        from tensor_transformer_layer_02_amd import build
+        build.build()
+    return tp.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in tpshard.h but not exported"
+    assert sorted(tp.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for code in range(9):
+        assert tp.tp_status_string(code)
+    assert tp.tp_status_string(99) == "unknown status"
+
+
+def d(batch=2, seq=64, hidden=128, heads=4, ffn=512, causal=1, act=tp.TP_BF16):
+    return tp.tp_dims(batch, seq, hidden, heads, ffn, causal, act)
+
+
+@pytest.mark.parametrize("dims,shard,degree,code", [
+    (d(), 0, 2, 0),
+    (d(), 2, 2, 3),
+    (d(), -1, 2, 3),
+    (d(), 0, 0, 3),
+    (d(heads=3), 0, 1, 2),            # 128 % 3
+    (d(heads=4, ffn=510), 0, 4, 2),   # 510 % 4
+    (d(heads=4), 0, 8, 2),            # 4 % 8
+    (d(batch=0), 0, 1, 1),
+    (d(causal=2), 0, 1, 1),
+    (d(act=7), 0, 1, 5),
+    (d(hidden=120, heads=4), 0, 1, 6),   # d = 30: bf16 head dims are 32/64/96/128
+    (d(hidden=128, heads=2), 0, 2, 0),   # d = 64, w = 64
+    (d(hidden=96, heads=3, ffn=384), 0, 3, 6),  # w = 32 is not a multiple of 64 (bf16)
+    (d(hidden=96, heads=3, ffn=384, act=tp.TP_FP32), 0, 3, 0),
+    (d(hidden=132, heads=4, act=tp.TP_FP32), 0, 1, 4),  # hidden % 8
+])
+def test_check_dims(L, dims, shard, degree, code):
+    assert tp.tp_check_dims(dims, shard, degree) == code
+
+
+def test_saved_and_work_sizes_follow_documented_layout(L):
+    for name, cfg in CONFIGS.items():
+        dims = tp.dims_of(cfg)
+        T, Fs, w, e = cfg.tokens, cfg.ffn_per_shard, cfg.attn_width, (4 if cfg.dtype == "fp32" else 2)
+        a = lambda x: (x + 255) // 256 * 256
+        assert tp.tp_mlp_saved_bytes(dims, 0, cfg.degree) == 2 * a(T * Fs * e), name
+        assert tp.tp_attn_saved_bytes(dims, 0, cfg.degree) == (a(T * 3 * w * e) + a(T * w * e)
+                                                               + a(cfg.batch * cfg.heads_per_shard * cfg.seq * 4))
+        assert tp.tp_mlp_work_bytes(dims, 0, cfg.degree) >= T * Fs * e
+        assert tp.tp_attn_work_bytes(dims, 0, cfg.degree) >= 4 * T * w * e
+    bad = d(heads=3)
+    assert tp.tp_mlp_saved_bytes(bad, 0, 1) == 0 and tp.tp_attn_work_bytes(bad, 0, 1) == 0
+
+
+def _fake(addr=0x10000):
+    return addr  # a host integer standing in for a device address; never dereferenced
+
+
+def test_entry_points_reject_before_any_launch(L):
+    """Errors come back synchronously; these calls never reach HIP (no GPU here)."""
+    good = d()
+    P = _fake()
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_fwd(d(heads=3), 0, 1, P, P, None, P, P, P, stream=0)
+    assert e.value.code == 2
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_fwd(good, 5, 2, P, P, None, P, P, P, stream=0)
+    assert e.value.code == 3
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_fwd(good, 0, 2, None, P, None, P, P, P, stream=0)
+    assert e.value.code == 1
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_fwd(good, 0, 2, P + 2, P, None, P, P, P, stream=0)
+    assert e.value.code == 4
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_attn_shard_fwd(good, 0, 2, P, P, P, P, P + 8, None, None, P, P, P, stream=0)
+    assert e.value.code == 4
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_attn_shard_bwd(good, 0, 2, P, P, P, P, P, P, P, P, P, P, P, None, None, None, None, P, stream=0)
+    assert e.value.code == 1   # dWo NULL
+    # work buffer too small -> TP_ESIZE (work passed as an int: size 0)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_bwd(good, 0, 2, P, P, P, P, P, P, P, P, P, P, stream=0)
+    assert e.value.code == 8
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_sum_partials(3, 4, 4, [P], None, P, stream=0)
+    assert e.value.code == 5
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_sum_partials(tp.TP_BF16, 4, 4, [P, None], None, P, stream=0)
+    assert e.value.code == 1
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_sum_partials(tp.TP_BF16, 0, 4, [P], None, P, stream=0)
+    assert e.value.code == 1
+
+
+def test_null_dims_pointer(L):
+    assert L.tp_check_dims(None, 0, 1) == 1
+    assert L.tp_mlp_saved_bytes(None, 0, 1) == 0
