@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of one tensor-parallel layer shard, forward + backward, on one MI355X.
+
+Workload (default): the GPT-2 8.3B-shape layer, one t = 8 shard (shard 0):
+batch 8 x seq 1024 tokens, hidden 3072, 32 heads (4 per shard, d = 96), FFN 12288
+(1536 per shard), causal, bf16 with fp32 accumulation; synthetic seeded inputs.
+One step = MLP forward, attention forward, MLP backward, attention backward of
+the shard through the C ABI, with inputs already resident in HBM.
+
+Prints ONE JSON line on stdout:
+  value            whole-job throughput, algorithmic TFLOP/s (2*M*N*K per GEMM,
+                   causal-halved attention, no recompute counted)
+  roofline         the dominant kernel's algorithmic TFLOP/s against the bf16
+                   dense MFMA peak, timed live with HIP events on its stream
+  cpu_baseline     the float64 CPU oracle timed on this host on a bounded sample
+                   of the same workload (a baseline, not a target)
+  kernels          per-step breakdown (average duration, TFLOP/s or GB/s)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shard-layer fwd+bwd TFLOP/s and % of bf16 MFMA peak, 8.3B-shape t=8 shard"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_costs(cfg):
+    """Algorithmic FLOPs and minimum HBM bytes of each hook step (one launch each)."""
+    from tensor_transformer_layer_02_amd.configs import causal_pairs
+    T, h, Fs, w, d = cfg.tokens, cfg.hidden, cfg.ffn_per_shard, cfg.attn_width, cfg.head_dim
+    e = 2
+    pairs = cfg.batch * cfg.heads_per_shard * causal_pairs(cfg.seq, cfg.causal)
+    g = lambda m, n, k: 2 * m * n * k
+    # bytes: operands read once + outputs written once
+    return {
+        "MLP_UP": (g(T, Fs, h), (T * h + h * Fs + 2 * T * Fs) * e),
+        "MLP_DOWN": (g(T, h, Fs), (T * Fs + Fs * h + T * h) * e),
+        "QKV": (g(T, 3 * w, h), (T * h + 3 * h * w + 3 * T * w) * e),
+        "ATTN_CORE": (2 * 2 * d * pairs, 4 * T * w * e + cfg.batch * cfg.heads_per_shard * cfg.seq * 4),
+        "ATTN_OUT": (g(T, h, w), (T * w + w * h + T * h) * e),
+        "MLP_DU": (g(T, Fs, h), (T * h + Fs * h + 2 * T * Fs) * e),
+        "MLP_DB": (g(Fs, h, T), (T * Fs + T * h) * e + Fs * h * 4),
+        "MLP_DA": (g(h, Fs, T), (T * h + T * Fs) * e + h * Fs * 4),
+        "MLP_DB1": (0, T * Fs * e + Fs * 4),
+        "MLP_DX": (g(T, h, Fs), (T * Fs + h * Fs + T * h) * e),
+        "ATTN_DO": (g(T, w, h), (T * h + w * h + T * w) * e),
+        "ATTN_DWO": (g(w, h, T), (T * w + T * h) * e + w * h * 4),
+        "ATTN_CORE_BWD": (4 * 2 * d * pairs, 9 * T * w * e),
+        "ATTN_DW": (g(h, 3 * w, T), (T * h + 3 * T * w) * e + 3 * h * w * 4),
+        "ATTN_DBIAS": (0, 3 * T * w * e + 3 * w * 4),
+        "ATTN_DX": (g(T, h, 3 * w), (3 * T * w + 3 * w * h + T * h) * e),
+    }
+
+
+# Steps that are a single kernel launch (usable for the roofline of "the dominant kernel").
+SINGLE_KERNEL = {"MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DB", "MLP_DA",
+                 "MLP_DX", "ATTN_DO", "ATTN_DWO", "ATTN_DW", "ATTN_DX"}
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (same soname)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.ev[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def cpu_baseline(cfg, inp, nseq):
+    """The float64 oracle, as it stands, on the first `nseq` sequences of the same inputs."""
+    import oracle
+    from tensor_transformer_layer_02_amd.configs import shard_flops
+    from tensor_transformer_layer_02_amd.inputs import as_f64
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    sub = cfg.with_(batch=nseq)
+    rows = sub.tokens
+    p = {k: as_f64(v) for k, v in inp.items()}
+    p["X"] = p["X"][:rows].copy()
+    p["dZ"] = p["dZ"][:rows].copy()
+    d = sub.dims()
+    args = [p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")]
+    t0 = time.perf_counter()
+    oracle.mlp_shard_fwd(d, 0, cfg.degree, p["X"], p["A"], p["b1"], p["B"])
+    oracle.attn_shard_fwd(d, 0, cfg.degree, *args)
+    oracle.mlp_shard_bwd(d, 0, cfg.degree, p["X"], p["A"], p["b1"], p["B"], p["dZ"])
+    oracle.attn_shard_bwd(d, 0, cfg.degree, *args, p["dZ"])
+    dt = time.perf_counter() - t0
+    fl = shard_flops(sub, backward=True)["total"]
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"shard 0 fwd+bwd on the first {nseq} of {cfg.batch} sequences "
+                      f"({rows} of {cfg.tokens} tokens; {fl / 1e9:.1f} GFLOP algorithmic), float64 C loops "
+                      f"with OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt8b")
+    ap.add_argument("--shard", type=int, default=0)
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU's shard; runs on more than one GPU "
+                                   "are not supported (the cross-shard all-reduce is out of scope)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from tensor_transformer_layer_02_amd import tpshard as tp
+    from tensor_transformer_layer_02_amd.configs import CONFIGS, shard_flops
+    from tensor_transformer_layer_02_amd.inputs import make_inputs
+    from tensor_transformer_layer_02_amd.shard import ShardRun
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    cfg = CONFIGS[args.config]
+    if not cfg.backward:
+        cfg = cfg.with_(backward=True)
+    K, W = args.steps, args.warmup
+    log(f"[bench] {cfg.note}: T={cfg.tokens} h={cfg.hidden} F/t={cfg.ffn_per_shard} H/t={cfg.heads_per_shard} "
+        f"d={cfg.head_dim} shard={args.shard}")
+    inp = make_inputs(cfg)
+    run = ShardRun(cfg, inp, shards=[args.shard])
+    flops = shard_flops(cfg, backward=True)["total"]
+    prop = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {prop.name} CUs={prop.multi_processor_count} peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
+
+    for _ in range(W):
+        run.step(args.shard)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps on the current stream ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        run.step(args.shard)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / K
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)"
+        f"  wall {wall:.3f}s")
+
+    # ---- per-kernel timing: HIP event pairs around each step's launch, same stream ----
+    kernels, roof = [], None
+    if not args.no_kernel_timing:
+        nst = len(tp.STEPS)
+        ev = HipEvents(2 * nst * K)
+        tp.tp_profile_enable(ev.ev, K)
+        e0.record()
+        for _ in range(K):
+            run.step(args.shard)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_hooked = e0.elapsed_time(e1) / K
+        counts = [tp.tp_profile_count(s) for s in range(nst)]
+        tp.tp_profile_enable(None, 0)
+        costs = step_costs(cfg)
+        for s, name in enumerate(tp.STEPS):
+            n = min(counts[s], K)
+            if n == 0:
+                continue
+            durs = [ev.elapsed_ms(2 * (s * K + k), 2 * (s * K + k) + 1) for k in range(n)]
+            avg = sum(durs) / n
+            fl, by = costs[name]
+            kernels.append({"step": name, "avg_us": round(avg * 1e3, 2), "launches": n,
+                            "tflops": round(fl / (avg * 1e-3) / 1e12, 1) if fl else None,
+                            "gbs": round(by / (avg * 1e-3) / 1e9, 1)})
+        ev.close()
+        tot = sum(k["avg_us"] for k in kernels)
+        for k in kernels:
+            k["share"] = round(k["avg_us"] / tot, 3)
+        log(f"[bench] with per-step events: {ms_hooked:.4f} ms/step")
+        for k in kernels:
+            log(f"  {k['step']:<14} {k['avg_us']:9.2f} us  {k['share'] * 100:5.1f}%  "
+                f"{(str(k['tflops']) + ' TF/s') if k['tflops'] else '':>14}  {k['gbs']:8.1f} GB/s")
+        dom = max((k for k in kernels if k["step"] in SINGLE_KERNEL), key=lambda k: k["avg_us"])
+        fl, by = costs[dom["step"]]
+        ach = fl / (dom["avg_us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": dom["step"], "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": fl, "avg_us": dom["avg_us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequence(s) ...")
+        cpu = cpu_baseline(cfg, inp, args.cpu_seqs)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['seconds']} s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": cfg.batch, "seq": cfg.seq,
+                   "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn,
+                   "degree": cfg.degree, "shard": args.shard, "causal": cfg.causal,
+                   "flops_per_step": flops, "parallelism": "one tp shard on one GPU (no collectives)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,115 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times
+(shard 0, full batch), checked on outputs the float64 oracle can compute in seconds:
+
+- FFN rows: rows are independent in the FFN forward and in its input gradient, so a row
+  sample is an exact sub-problem (the oracle runs on those rows only);
+- FFN weight-gradient columns: an 8-column block of shard 0 is itself a shard of degree F/8,
+  so the oracle's shard function on ALL tokens gives dA, db1 and dB for exactly those columns;
+- attention rows: sequences are independent, so one whole sequence (batch 1) gives that
+  sequence's partial outputs and input-gradient partials exactly;
+- attention weight gradients: one head g of shard 0 is shard g of degree H, so the oracle on
+  ALL tokens gives dWq/dWk/dWv columns, dbq/dbv entries and dWo rows of that head.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, check
+from tensor_transformer_layer_02_amd.configs import CONFIGS
+from tensor_transformer_layer_02_amd.inputs import as_f64, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cpu(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+@pytest.mark.parametrize("name,nrows,seq_idx,head_idx", [
+    ("gpt8b", 24, 5, 3),
+    ("bert4b", 24, 11, 4),
+    ("g30b_t4", 8, 2, 13),
+    ("g30b_t1", 6, 1, 40),
+])
+def test_full_size_sampled(name, nrows, seq_idx, head_idx):
+    from tensor_transformer_layer_02_amd.shard import ShardRun
+    cfg = CONFIGS[name].with_(backward=True)
+    _say(f"[{name}] full size: T={cfg.tokens} h={cfg.hidden} F={cfg.ffn} H={cfg.heads} t={cfg.degree} shard 0")
+    inp = make_inputs(cfg)
+    run = ShardRun(cfg, inp, shards=[0])
+    run.step(0)
+    torch.cuda.synchronize()
+    sv = run.saved(0)
+    tol = TOL["bf16"]
+    rep = []
+    T, h, F, t, s = cfg.tokens, cfg.hidden, cfg.ffn, cfg.degree, cfg.seq
+    p = {k: as_f64(v) for k, v in inp.items()}
+    rng = np.random.default_rng(cfg.cid)
+
+    # ---- FFN rows
+    rows = np.sort(rng.choice(T, size=nrows, replace=False))
+    dr = dict(batch=1, seq=nrows, hidden=h, heads=cfg.heads, ffn=F, causal=int(cfg.causal))
+    Xr, Gr = p["X"][rows].copy(), p["dZ"][rows].copy()
+    mf = oracle.mlp_shard_fwd(dr, 0, t, Xr, p["A"], p["b1"], p["B"])
+    mb = oracle.mlp_shard_bwd(dr, 0, t, Xr, p["A"], p["b1"], p["B"], Gr)
+    check("U rows", _cpu(sv["U"])[rows], mf["U"], tol, rep)
+    check("Y rows", _cpu(sv["Y"])[rows], mf["Y"], tol, rep)
+    check("Z_mlp rows", _cpu(run.buf[0]["Z_mlp"])[rows], mf["Z"], tol, rep)
+    check("dX_mlp rows", _cpu(run.buf[0]["dX_mlp"])[rows], mb["dX"], tol, rep)
+    _say(f"[{name}] ffn rows ok")
+
+    # ---- FFN weight-gradient column blocks (8 columns = shard k of degree F/8)
+    d = cfg.dims()
+    nblk = cfg.ffn_per_shard // 8
+    for k in (0, nblk // 2 + 1, nblk - 1):
+        ob = oracle.mlp_shard_bwd(d, k, F // 8, p["X"], p["A"], p["b1"], p["B"], p["dZ"])
+        c = slice(8 * k, 8 * k + 8)
+        check(f"dA[:, {8 * k}:+8]", _cpu(run.grads["dA"][:, c]), ob["dA"][:, c], tol, rep)
+        check(f"db1[{8 * k}:+8]", _cpu(run.grads["db1"][c]), ob["db1"][c], tol, rep)
+        check(f"dB[{8 * k}:+8, :]", _cpu(run.grads["dB"][c, :]), ob["dB"][c, :], tol, rep)
+    _say(f"[{name}] ffn weight-gradient columns ok")
+
+    # ---- attention: one whole sequence (exact sub-problem for rows and the per-row outputs)
+    names = ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")
+    w, Hs, dh = cfg.attn_width, cfg.heads_per_shard, cfg.head_dim
+    if cfg.hidden * 3 * w * s <= 2e10:   # the whole shard fits in a few seconds of oracle time
+        r = slice(seq_idx * s, (seq_idx + 1) * s)
+        q = {k: v for k, v in p.items()}
+        q["X"], q["dZ"] = p["X"][r].copy(), p["dZ"][r].copy()
+        d1 = dict(d, batch=1)
+        af = oracle.attn_shard_fwd(d1, 0, t, *[q[n] for n in names])
+        ab = oracle.attn_shard_bwd(d1, 0, t, *[q[n] for n in names], q["dZ"])
+        check("QKV seq", _cpu(sv["QKV"])[r], np.concatenate([af["Q"], af["K"], af["V"]], 1), tol, rep)
+        check("O seq", _cpu(sv["O"])[r], af["O"], tol, rep)
+        check("LSE seq", _cpu(sv["LSE"])[seq_idx], af["lse"][0], tol, rep)
+        check("Z_attn seq", _cpu(run.buf[0]["Z_attn"])[r], af["Z"], tol, rep)
+        check("dX_attn seq", _cpu(run.buf[0]["dX_attn"])[r], ab["dX"], tol, rep)
+        _say(f"[{name}] attention sequence {seq_idx} ok")
+
+    # ---- attention: one head of shard 0 (shard g of degree H) over ALL tokens
+    g = head_idx % Hs
+    gh = g  # global head index inside shard 0
+    hf = oracle.attn_shard_fwd(d, gh, cfg.heads, *[p[n] for n in names])
+    hb = oracle.attn_shard_bwd(d, gh, cfg.heads, *[p[n] for n in names], p["dZ"])
+    cols = slice(gh * dh, (gh + 1) * dh)
+    QKV = sv["QKV"]
+    check(f"Q head {gh}", _cpu(QKV[:, g * dh:(g + 1) * dh]), hf["Q"], tol, rep)
+    check(f"V head {gh}", _cpu(QKV[:, 2 * w + g * dh:2 * w + (g + 1) * dh]), hf["V"], tol, rep)
+    check(f"O head {gh}", _cpu(sv["O"][:, g * dh:(g + 1) * dh]), hf["O"], tol, rep)
+    check(f"LSE head {gh}", _cpu(sv["LSE"][:, g, :]), hf["lse"][:, 0, :], tol, rep)
+    for n in ("Wq", "Wk", "Wv"):
+        check(f"d{n}[:, head {gh}]", _cpu(run.grads["d" + n][:, cols]), hb["d" + n][:, cols], tol, rep)
+    for n in ("bq", "bv"):
+        check(f"d{n}[head {gh}]", _cpu(run.grads["d" + n][cols]), hb["d" + n][cols], tol, rep)
+    check(f"dWo[head {gh} rows]", _cpu(run.grads["dWo"][cols, :]), hb["dWo"][cols, :], tol, rep)
+    _say(f"[{name}] " + "; ".join(f"{n}={e:.1e}" for n, e in rep))
