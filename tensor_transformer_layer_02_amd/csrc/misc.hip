@@ -10,18 +10,51 @@ namespace tp {
 
 namespace {
 
-constexpr int COLSUM_SPLITS = 64;
+constexpr int COLSUM_SPLITS = 32;   // row bands; partial sums land in work[band][col]
+constexpr int CS_COLS = 64;         // columns per workgroup (8 groups of 8)
 
+// Partial column sums of a [rows, cols] matrix over one band of rows.  Thread
+// (row lane rl, column group cg) reads 8 consecutive columns per row with a
+// 16-byte load (bf16) or two (fp32); a wave covers 8 rows x 64 columns.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_partial_kernel(const T* __restrict__ X, int64_t rows, int64_t cols,
                                                              int64_t ld, float* __restrict__ work) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= cols) return;
-    const int64_t chunk = (rows + COLSUM_SPLITS - 1) / COLSUM_SPLITS;
-    const int64_t r0 = blockIdx.y * chunk, r1 = min(rows, r0 + chunk);
-    float acc = 0.f;
-    for (int64_t r = r0; r < r1; ++r) acc += to_f<T>(X[r * ld + c]);
-    work[(int64_t)blockIdx.y * cols + c] = acc;
+    __shared__ float red[32][CS_COLS + 1];
+    const int cg = threadIdx.x % 8, rl = threadIdx.x / 8;
+    const int64_t c0 = (int64_t)blockIdx.x * CS_COLS + cg * 8;
+    const int64_t band = (rows + COLSUM_SPLITS - 1) / COLSUM_SPLITS;
+    const int64_t r0 = blockIdx.y * band, r1 = min(rows, r0 + band);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c0 < cols) {
+        for (int64_t r = r0 + rl; r < r1; r += 32) {
+            const T* src = X + r * ld + c0;
+            if constexpr (sizeof(T) == 2) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += __uint_as_float(v[q] << 16);
+                    acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+                }
+            } else {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[q] += a[q];
+                    acc[4 + q] += b[q];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) red[rl][cg * 8 + q] = acc[q];
+    __syncthreads();
+    if (threadIdx.x < CS_COLS) {
+        float sum = 0.f;
+        for (int i = 0; i < 32; ++i) sum += red[i][threadIdx.x];
+        const int64_t c = (int64_t)blockIdx.x * CS_COLS + threadIdx.x;
+        if (c < cols) work[(int64_t)blockIdx.y * cols + c] = sum;
+    }
 }
 
 struct Out3 {
@@ -61,7 +94,7 @@ int64_t colsum_work_floats(int64_t cols) { return (int64_t)COLSUM_SPLITS * cols;
 hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t ld, float* const out[3],
                   int seg, float* work, hipStream_t s) {
     if (cols <= 0) return hipSuccess;
-    dim3 g1((unsigned)((cols + 255) / 256), COLSUM_SPLITS);
+    dim3 g1((unsigned)((cols + CS_COLS - 1) / CS_COLS), COLSUM_SPLITS);
     if (bf16)
         hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, g1, dim3(256), 0, s, static_cast<const bf16_t*>(X), rows,
                            cols, ld, work);

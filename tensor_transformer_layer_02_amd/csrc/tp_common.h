@@ -48,6 +48,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// 32x32x16 bf16 MFMA.  A: lane l holds row l%32, k = 8*(l/32) .. +7;
+// B: lane l holds column l%32, same k; D: lane l holds column l%32, rows
+// 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }

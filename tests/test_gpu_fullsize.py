@@ -70,9 +70,12 @@ def test_full_size_sampled(name, nrows, seq_idx, head_idx):
 
     # ---- FFN weight-gradient column blocks (8 columns = shard k of degree F/8)
     d = cfg.dims()
+    # the oracle also checks heads % degree; heads play no part in the FFN, and F = 4h makes
+    # F/8 a divisor of h, so the sub-problem takes F/8 heads
+    dm = dict(d, heads=F // 8)
     nblk = cfg.ffn_per_shard // 8
     for k in (0, nblk // 2 + 1, nblk - 1):
-        ob = oracle.mlp_shard_bwd(d, k, F // 8, p["X"], p["A"], p["b1"], p["B"], p["dZ"])
+        ob = oracle.mlp_shard_bwd(dm, k, F // 8, p["X"], p["A"], p["b1"], p["B"], p["dZ"])
         c = slice(8 * k, 8 * k + 8)
         check(f"dA[:, {8 * k}:+8]", _cpu(run.grads["dA"][:, c]), ob["dA"][:, c], tol, rep)
         check(f"db1[{8 * k}:+8]", _cpu(run.grads["db1"][c]), ob["db1"][c], tol, rep)
