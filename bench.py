@@ -53,22 +53,20 @@ def step_costs(cfg):
         "ATTN_CORE": (2 * 2 * d * pairs, 4 * T * w * e + cfg.batch * cfg.heads_per_shard * cfg.seq * 4),
         "ATTN_OUT": (g(T, h, w), (T * w + w * h + T * h) * e),
         "MLP_DU": (g(T, Fs, h), (T * h + Fs * h + 2 * T * Fs) * e),
-        "MLP_DB": (g(Fs, h, T), (T * Fs + T * h) * e + Fs * h * 4),
-        "MLP_DA": (g(h, Fs, T), (T * h + T * Fs) * e + h * Fs * 4),
+        "MLP_DW": (g(Fs, h, T) + g(h, Fs, T), (2 * T * Fs + 2 * T * h) * e + 2 * Fs * h * 4),
         "MLP_DB1": (0, T * Fs * e + Fs * 4),
         "MLP_DX": (g(T, h, Fs), (T * Fs + h * Fs + T * h) * e),
         "ATTN_DO": (g(T, w, h), (T * h + w * h + T * w) * e),
-        "ATTN_DWO": (g(w, h, T), (T * w + T * h) * e + w * h * 4),
         "ATTN_CORE_BWD": (4 * 2 * d * pairs, 9 * T * w * e),
-        "ATTN_DW": (g(h, 3 * w, T), (T * h + 3 * T * w) * e + 3 * h * w * 4),
+        "ATTN_DW": (g(h, 3 * w, T) + g(w, h, T), (T * h + 3 * T * w + T * w + T * h) * e + 4 * h * w * 4),
         "ATTN_DBIAS": (0, 3 * T * w * e + 3 * w * 4),
         "ATTN_DX": (g(T, h, 3 * w), (3 * T * w + 3 * w * h + T * h) * e),
     }
 
 
 # Steps that are a single kernel launch (usable for the roofline of "the dominant kernel").
-SINGLE_KERNEL = {"MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DB", "MLP_DA",
-                 "MLP_DX", "ATTN_DO", "ATTN_DWO", "ATTN_DW", "ATTN_DX"}
+SINGLE_KERNEL = {"MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DX",
+                 "ATTN_DO", "ATTN_DX"}
 
 
 class HipEvents:

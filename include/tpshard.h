@@ -186,17 +186,15 @@ enum {
     TP_STEP_ATTN_CORE = 3,   /* softmax attention forward -> O, LSE                          */
     TP_STEP_ATTN_OUT = 4,    /* Z_part = O Wo_i                     (row-parallel GEMM)    */
     TP_STEP_MLP_DU = 5,      /* dU = (dZ B_i^T) * GeLU'(U)                                  */
-    TP_STEP_MLP_DB = 6,      /* dB_i = Y^T dZ                                               */
-    TP_STEP_MLP_DA = 7,      /* dA_i = X^T dU                                               */
-    TP_STEP_MLP_DB1 = 8,     /* db1_i = column sums of dU                                   */
-    TP_STEP_MLP_DX = 9,      /* dX_part = dU A_i^T                                          */
-    TP_STEP_ATTN_DO = 10,    /* dO = dZ Wo_i^T                                              */
-    TP_STEP_ATTN_DWO = 11,   /* dWo_i = O^T dZ                                              */
-    TP_STEP_ATTN_CORE_BWD = 12, /* softmax attention backward -> dQ, dK, dV                 */
-    TP_STEP_ATTN_DW = 13,    /* dW{q,k,v}_i = X^T d{Q,K,V}                                  */
-    TP_STEP_ATTN_DBIAS = 14, /* db{q,k,v}_i = column sums                                   */
-    TP_STEP_ATTN_DX = 15,    /* dX_part = d{Q,K,V} W{q,k,v}_i^T                             */
-    TP_NUM_STEPS = 16
+    TP_STEP_MLP_DW = 6,      /* dB_i = Y^T dZ and dA_i = X^T dU (one launch)                */
+    TP_STEP_MLP_DB1 = 7,     /* db1_i = column sums of dU                                   */
+    TP_STEP_MLP_DX = 8,      /* dX_part = dU A_i^T                                          */
+    TP_STEP_ATTN_DO = 9,     /* dO = dZ Wo_i^T                                              */
+    TP_STEP_ATTN_CORE_BWD = 10, /* softmax attention backward -> dQ, dK, dV                 */
+    TP_STEP_ATTN_DW = 11,    /* dW{q,k,v}_i = X^T d{Q,K,V} and dWo_i = O^T dZ (one launch)  */
+    TP_STEP_ATTN_DBIAS = 12, /* db{q,k,v}_i = column sums                                   */
+    TP_STEP_ATTN_DX = 13,    /* dX_part = d{Q,K,V} W{q,k,v}_i^T                             */
+    TP_NUM_STEPS = 14
 };
 
 /*

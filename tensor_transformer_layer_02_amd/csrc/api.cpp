@@ -145,6 +145,15 @@ inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, in
     return s.bf16 ? tp::gemm_bf16(g, st) : tp::gemm_f32(g, st);
 }
 
+// Two independent weight-gradient GEMMs of the same layout in one launch
+// (bf16 path; may split K in two with zeroed outputs), or one after the other.
+inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, int step) {
+    StepTimer t(step, st);
+    if (s.bf16) return tp::gemm_bf16_batch(g, 2, true, nullptr, st);
+    hipError_t e = tp::gemm_f32(g[0], st);
+    return e != hipSuccess ? e : tp::gemm_f32(g[1], st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,19 +275,18 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     g.epi = tp::EPI_GELU_BWD;
     if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
 
-    tp::GemmDesc gb;  // dB[C_i, :] = Y^T dZ
+    tp::GemmDesc gw[2];  // one launch: dB[C_i, :] = Y^T dZ and dA[:, C_i] = X^T dU
+    tp::GemmDesc& gb = gw[0];
     gb.M = (int)s.Fs; gb.N = (int)s.h; gb.K = (int)s.T;
     gb.A = Y; gb.lda = s.Fs; gb.a_kcontig = false;
     gb.B[0] = dZ; gb.ldb = s.h; gb.b_kcontig = false;
     gb.C[0] = dB + c0 * s.h; gb.ldc = s.h; gb.out_f32 = true;
-    if (gemm(s, gb, st, TP_STEP_MLP_DB) != hipSuccess) return TP_EHIP;
-
-    tp::GemmDesc ga;  // dA[:, C_i] = X^T dU
+    tp::GemmDesc& ga = gw[1];
     ga.M = (int)s.h; ga.N = (int)s.Fs; ga.K = (int)s.T;
     ga.A = X; ga.lda = s.h; ga.a_kcontig = false;
     ga.B[0] = dU; ga.ldb = s.Fs; ga.b_kcontig = false;
     ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
-    if (gemm(s, ga, st, TP_STEP_MLP_DA) != hipSuccess) return TP_EHIP;
+    if (gemm2(s, gw, st, TP_STEP_MLP_DW) != hipSuccess) return TP_EHIP;
 
     if (db1) {  // db1[C_i] = column sums of dU
         float* outs[3] = {db1 + c0, nullptr, nullptr};
@@ -378,12 +386,6 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     g.C[0] = dO; g.ldc = s.w;
     if (gemm(s, g, st, TP_STEP_ATTN_DO) != hipSuccess) return TP_EHIP;
 
-    tp::GemmDesc gw;  // dWo[rows of G_i, :] = O^T dZ
-    gw.M = (int)s.w; gw.N = (int)s.h; gw.K = (int)s.T;
-    gw.A = O; gw.lda = s.w; gw.a_kcontig = false;
-    gw.B[0] = dZ; gw.ldb = s.h; gw.b_kcontig = false;
-    gw.C[0] = dWo + col0 * s.h; gw.ldc = s.h; gw.out_f32 = true;
-    if (gemm(s, gw, st, TP_STEP_ATTN_DWO) != hipSuccess) return TP_EHIP;
 
     tp::AttnDesc ad;
     ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
@@ -394,14 +396,20 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
         if ((s.bf16 ? tp::attn_bwd_bf16(ad, st) : tp::attn_bwd_f32(ad, st)) != hipSuccess) return TP_EHIP;
     }
 
-    tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV
+    tp::GemmDesc gw[2];  // one launch: dW{q,k,v}[:, cols of G_i] = X^T dQKV and dWo[rows of G_i, :] = O^T dZ
+    tp::GemmDesc& gq = gw[0];
     gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
     gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
     gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
     float* dW3[3] = {dWq, dWk, dWv};
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
-    if (gemm(s, gq, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
+    tp::GemmDesc& go = gw[1];
+    go.M = (int)s.w; go.N = (int)s.h; go.K = (int)s.T;
+    go.A = O; go.lda = s.w; go.a_kcontig = false;
+    go.B[0] = dZ; go.ldb = s.h; go.b_kcontig = false;
+    go.C[0] = dWo + col0 * s.h; go.ldc = s.h; go.out_f32 = true;
+    if (gemm2(s, gw, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
 
     if (bias_grads) {  // db{q,k,v}[cols of G_i] = column sums of dQKV
         float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};

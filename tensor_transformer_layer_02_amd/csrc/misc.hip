@@ -71,6 +71,20 @@ __global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restri
     out.p[sg][c - (int64_t)sg * seg] = acc;
 }
 
+__global__ void __launch_bounds__(256) zero_f32_2d_kernel(float* __restrict__ p, int64_t rows, int64_t cols,
+                                                          int64_t ld) {
+    const int64_t c4 = (cols + 3) / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * c4) return;
+    const int64_t r = i / c4, c = (i % c4) * 4;
+    float* q = p + r * ld + c;
+    if (c + 4 <= cols && ((reinterpret_cast<uintptr_t>(q) & 15) == 0)) {
+        *reinterpret_cast<f32x4*>(q) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t k = c; k < cols && k < c + 4; ++k) p[r * ld + k] = 0.f;
+    }
+}
+
 constexpr int MAXP = 16;
 struct Parts {
     const void* p[MAXP];
@@ -105,6 +119,13 @@ hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t 
     for (int i = 0; i < 3; ++i) o.p[i] = out[i] ? out[i] : out[0];
     hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(work), cols, o, seg);
+    return hipGetLastError();
+}
+
+hipError_t zero_f32_2d(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
+    const int64_t n = rows * ((cols + 3) / 4);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_f32_2d_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, cols, ld);
     return hipGetLastError();
 }
 

@@ -44,6 +44,14 @@ struct GemmDesc {
 
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
 hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s);
+// One launch for n (1 or 2) independent problems of the same layout and
+// epilogue.  With allow_split, fp32-output (weight-gradient) problems may be
+// split in two along K (*ksplit_out reports it); the output blocks are then
+// zeroed first by a kernel on the same stream and the halves added atomically.
+hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s);
+
+// Zero a [rows, cols] fp32 block with row stride ld (a kernel, so it can be captured).
+hipError_t zero_f32_2d(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 // fp32 operands and outputs, fp32 FMA arithmetic.
 hipError_t gemm_f32(const GemmDesc& d, hipStream_t s);
 

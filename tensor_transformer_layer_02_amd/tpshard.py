@@ -25,8 +25,8 @@ EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_byte
            "tp_profile_count"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
-STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DB", "MLP_DA", "MLP_DB1",
-         "MLP_DX", "ATTN_DO", "ATTN_DWO", "ATTN_CORE_BWD", "ATTN_DW", "ATTN_DBIAS", "ATTN_DX"]
+STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
+         "ATTN_DO", "ATTN_CORE_BWD", "ATTN_DW", "ATTN_DBIAS", "ATTN_DX"]
 
 
 class TpError(RuntimeError):
