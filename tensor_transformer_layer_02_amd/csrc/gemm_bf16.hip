@@ -44,8 +44,8 @@ namespace tp {
 namespace {
 
 constexpr int NT = 256;
-constexpr int BK = 32;      // K elements per pipeline stage
-constexpr int STAGES = 3;   // LDS slots: one being read, one written, one free to write
+constexpr int BK = 64;      // K elements per pipeline stage (128-byte rows)
+constexpr int STAGES = 2;   // LDS slots
 constexpr uint32_t OOB = 0x80000000u;  // voffset past any buffer: the load returns zeros
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -84,11 +84,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Swizzle of a [rows][32] K-contiguous tile (4 chunks of 16 B per 64-byte row):
-// the fragment read of 16 consecutive rows at one logical chunk is conflict-free.
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+// Swizzle of a [rows][64] K-contiguous tile (8 chunks of 16 B per 128-byte
+// row): rows 2r and 2r+1 sit in the two halves of the banks, and the XOR
+// spreads 8 row pairs over the 8 chunk positions, so the fragment read of 16
+// consecutive rows at one logical chunk is conflict-free.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
-// Swizzle of a [32][cols] M/N-contiguous tile, by k-row.  One transposed
+// Swizzle of a [64][cols] M/N-contiguous tile, by k-row.  One transposed
 // fragment read touches rows 8g + r (+4), g, r in 0..3; the XOR spreads those
 // 16 rows over all banks (rows of a multiple of 256 B) or, with the row
 // parity, over both halves of the banks (rows of an odd multiple of 128 B).
@@ -100,31 +102,31 @@ __device__ __forceinline__ int swz_mn(int k) {
         return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));  // 0..6, within 8-chunk groups
 }
 
-// One stage of a K-contiguous operand, [ROWS][32]: instruction q fills LDS
-// bytes [q*1024, (q+1)*1024) = rows 16q..16q+15.  The per-lane source offset
-// (relative to the stage's k0, which moves the buffer base) is fixed.
+// One stage of a K-contiguous operand, [ROWS][64]: instruction q fills LDS
+// bytes [q*1024, (q+1)*1024) = rows 8q..8q+7, eight lanes per 128-byte row.
+// The per-lane source offset (relative to the stage's k0, which moves the
+// buffer base) is fixed; so is the lane's k chunk, since q = wave + 4i keeps
+// the swizzle of its rows independent of i.
 template <int ROWS>
 struct KOperand {
-    static constexpr int NI = ROWS / 64;  // instructions per wave
-    static_assert(ROWS % 64 == 0, "rows must be a multiple of 64");
+    static constexpr int NI = ROWS / 32;  // instructions per wave
+    static_assert(ROWS % 32 == 0, "rows must be a multiple of 32");
     uint32_t off[NI];
-    int koff[NI];
+    int koff;
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int rows_valid) {
+        koff = ((lane & 7) ^ swz_k(8 * wave + (lane >> 3))) * 8;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int q = wave + 4 * i;
-            const int row = 16 * q + (lane >> 2);
-            koff[i] = ((lane & 3) ^ swz_k(row)) * 8;
-            off[i] = row < rows_valid ? (uint32_t)(((int64_t)row * ld + koff[i]) * 2) : OOB;
+            const int row = 8 * (wave + 4 * i) + (lane >> 3);
+            off[i] = row < rows_valid ? (uint32_t)(((int64_t)row * ld + koff) * 2) : OOB;
         }
     }
-    // base of the stage: element (0, k0) of the tile
-    __device__ __forceinline__ static int64_t stage_elems(int k0, int64_t /*ld*/) { return k0; }
     // Load this thread's chunks of the stage into registers (zeros past the edges).
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int krem, u32x4 (&v)[NI]) const {
+        const bool kin = krem >= BK || koff < krem;  // K tail reads zeros
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t o = (krem >= BK || koff[i] < krem) ? off[i] : OOB;  // K tail reads zeros
+            const uint32_t o = kin ? off[i] : OOB;
             v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
         }
     }
@@ -134,29 +136,31 @@ struct KOperand {
     }
 };
 
-// One stage of an M/N-contiguous operand, [32][COLS] (k rows).
+// One stage of an M/N-contiguous operand, [64][COLS] (k rows).
 template <int COLS>
 struct MNOperand {
     static constexpr int ROWB = COLS * 2;
-    static constexpr int NI = COLS / 64;  // instructions per wave
-    static_assert(COLS % 64 == 0, "cols must be a multiple of 64");
+    static constexpr int NI = COLS / 32;  // instructions per wave
+    static_assert(COLS % 32 == 0, "cols must be a multiple of 32");
     uint32_t off[NI];
-    int krow[NI];
+    int o0;  // LDS byte offset of this lane's first chunk; chunk i is at o0 + 4096 i
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int cols_valid) {
+        o0 = wave * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int o = (wave + 4 * i) * 1024 + lane * 16;
-            krow[i] = o / ROWB;
+            const int o = o0 + 4096 * i;
+            const int krow = o / ROWB;
             const int p = (o % ROWB) / 16;
-            const int col = (p ^ swz_mn<COLS>(krow[i])) * 8;
-            off[i] = col < cols_valid ? (uint32_t)(((int64_t)krow[i] * ld + col) * 2) : OOB;
+            const int col = (p ^ swz_mn<COLS>(krow)) * 8;
+            off[i] = col < cols_valid ? (uint32_t)(((int64_t)krow * ld + col) * 2) : OOB;
         }
     }
-    __device__ __forceinline__ static int64_t stage_elems(int k0, int64_t ld) { return (int64_t)k0 * ld; }
+    // The chunk's k row is recomputed rather than kept: registers are scarce.
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int krem, u32x4 (&v)[NI]) const {
+        const int klim = krem >= BK ? BK : krem;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t o = (krem >= BK || krow[i] < krem) ? off[i] : OOB;
+            const uint32_t o = (o0 + 4096 * i) / ROWB < klim ? off[i] : OOB;
             v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
         }
     }
@@ -171,10 +175,10 @@ struct MNOperand {
 __device__ __forceinline__ u32x4 frag_k(const char* t, int rb, int kk, int lane) {
     const int r = rb + (lane & 31);
     const int c = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const u32x4*>(t + r * 64 + ((c ^ swz_k(r)) * 16));
+    return *reinterpret_cast<const u32x4*>(t + r * (BK * 2) + ((c ^ swz_k(r)) * 16));
 }
 
-// Same fragment from an M/N-contiguous [32][COLS] tile via two transposed
+// Same fragment from an M/N-contiguous [64][COLS] tile via two transposed
 // reads.  ds_read_b64_tr_b16 works on 16-lane groups: lane j of a group
 // supplies row j/4, columns 4*(j%4)..+3 of a 4x16 block and lane i receives
 // column i, i.e. 4 consecutive k of one row.  Group G = l/16 covers rows
@@ -236,20 +240,36 @@ __device__ __forceinline__ void tile_of(int b, int mt, int nt, int& mtile, int& 
     ntile = in / gm;
 }
 
-// Fragments of one k-step (two k16 halves) for one wave.
+// Fragments of one k16 sub-step for one wave.
 template <int FM, int FN>
-struct Frags {
-    u32x4 a[2][FM];
-    u32x4 b[2][FN];
+struct Half {
+    u32x4 a[FM];
+    u32x4 b[FN];
 };
 
-// MFMAs number FROM..TO-1 of a k-step (index = kk*FM*FN + i*FN + j).
+// MFMAs number FROM..TO-1 of a sub-step (index = i*FN + j).
 template <int FROM, int TO, int FM, int FN>
-__device__ __forceinline__ void run_mfmas(f32x16 (&acc)[FM][FN], const Frags<FM, FN>& F) {
+__device__ __forceinline__ void run_mfmas(f32x16 (&acc)[FM][FN], const Half<FM, FN>& F) {
 #pragma unroll
     for (int idx = FROM; idx < TO; ++idx) {
-        const int kk = idx / (FM * FN), i = (idx % (FM * FN)) / FN, j = idx % FN;
-        acc[i][j] = mfma32x32x16(F.a[kk][i], F.b[kk][j], acc[i][j]);
+        const int i = idx / FN, j = idx % FN;
+        acc[i][j] = mfma32x32x16(F.a[i], F.b[j], acc[i][j]);
+    }
+}
+
+// Scheduling hint for one scheduling region: pair each MFMA with one memory
+// instruction, taking first NR LDS reads, then NW LDS writes, then NL global
+// loads.
+template <int NMFMA, int NR, int NW, int NL>
+__device__ __forceinline__ void interleave() {
+    constexpr int NOPS = NR + NW + NL;
+    constexpr int N = NMFMA > NOPS ? NMFMA : NOPS;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
+        else if (i < NR + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        else if (i < NOPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+        if (i < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
     }
 }
 
@@ -257,6 +277,24 @@ __device__ __forceinline__ void run_mfmas(f32x16 (&acc)[FM][FN], const Frags<FM,
 // accumulators.  (Written as a struct rather than lambdas inside the kernel:
 // closure types in a kernel template defeat the host-side stub emission of
 // later instantiations with this compiler.)
+//
+// Pipeline.  A k-step (64 of K) is four k16 sub-steps of FM*FN MFMAs each,
+// with one barrier per step, before the last sub-step.  Step kt lives in LDS
+// slot kt&1; fragments alternate between two register sets Fa/Fb; operand
+// data travels global -> registers (two sets per operand, by step parity) ->
+// LDS:
+//   sub-step 0: read k16 #1 of step kt; store A of step kt+1 to slot (kt+1)&1;
+//               load A of step kt+1+NSET into the registers just stored;
+//   sub-step 1: read #2; the same for B;
+//   sub-step 2: read #3; wait for this wave's LDS operations; barrier;
+//   sub-step 3: read #0 of step kt+1 (slot (kt+1)&1).
+// A store to a slot comes after the barrier that follows every read of its
+// previous contents (step kt-1, read up to sub-step 2 of step kt-1), and
+// before the barrier that precedes every read of the new contents.  Global
+// loads are issued NSET steps before their data is stored.  Steps past the end
+// of the K range load from an empty buffer range (zeros, no memory access);
+// their stores and fragment reads are never consumed, so the steady state has
+// no branches for the scheduler to work around.
 template <int BM, int BN, bool AK, bool BKC, bool BKSEG>
 struct GemmCore {
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
@@ -266,45 +304,68 @@ struct GemmCore {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be made of 32x32 blocks");
     using LA = typename std::conditional<AK, KOperand<BM>, MNOperand<BM>>::type;
     using LB = typename std::conditional<BKC, KOperand<BN>, MNOperand<BN>>::type;
-    using FR = Frags<FM, FN>;
-    static constexpr int NMF = 2 * FM * FN;     // MFMAs per k-step
-    static constexpr int HEAD = NMF < 4 ? NMF : 4;  // MFMAs kept in flight across the barrier
+    using HF = Half<FM, FN>;
+    static constexpr int NM = FM * FN;           // MFMAs per sub-step
+    static constexpr int PRE = NM < 2 ? NM : 2;  // last-sub-step MFMAs issued before the barrier
+    static constexpr int NRD = (AK ? 1 : 2) * FM + (BKC ? 1 : 2) * FN;  // LDS reads per sub-step
+    static_assert(BK == 64, "four k16 sub-steps per step");
+    // Register sets per operand for data on its way to LDS: two let the
+    // global loads run two steps ahead; the 256 x 256 tile has no room for
+    // the second set (except with two plain K-contiguous operands) and loads
+    // one step ahead.
+    static constexpr int NSET = (BM == 256 && BN == 256 && !(AK && BKC && !BKSEG)) ? 1 : 2;
 
-    const GemmArgs& p;
     char* smem;
     int lane, wave, wm, wn, nk;
+    int kbase;  // first k-step of this workgroup's K range
+    int kend;   // end of this workgroup's K range (elements)
     const bf16_t* abase;
     uint32_t abytes;
-    int bsg;
-    int64_t boff;
+    int64_t lda, ldb, boff;
+    int bseg;
+    uint64_t bsel[3];   // B base address selection (see load_b)
+    uint32_t bbsel[3];
     LA la;
     LB lb;
-    u32x4 ra[LA::NI], rb[LB::NI];  // one k-step of operand data on its way to LDS
+    u32x4 ra[NSET][LA::NI], rb[NSET][LB::NI];  // operand data on its way to LDS
     f32x16 acc[FM][FN];
 
-    int kbase;  // first k-step of this workgroup's K range
-
-    __device__ __forceinline__ GemmCore(const GemmArgs& args, char* sm, int m0, int n0, int kb, int kn)
-        : p(args), smem(sm) {
+    __device__ __forceinline__ GemmCore(const GemmArgs& p, char* sm, int m0, int n0, int kb, int kn) : smem(sm) {
         const int tid = threadIdx.x;
         lane = tid & 63;
         wave = tid >> 6;
         wm = wave >> 1;
         wn = wave & 1;
-        const int64_t aoff = AK ? (int64_t)m0 * p.lda : m0;
+        lda = p.lda;
+        ldb = p.ldb;
+        bseg = p.bseg;
+        const int64_t aoff = AK ? (int64_t)m0 * lda : m0;
         abase = p.A + aoff;
         abytes = p.a_bytes - (uint32_t)(aoff * 2);
-        bsg = 0;
         int nb0 = n0;
-        if constexpr (!BKSEG) {
-            bsg = n0 / p.bseg;
-            nb0 = n0 - bsg * p.bseg;
+        bsel[1] = bsel[2] = 0;
+        bbsel[1] = bbsel[2] = 0;
+        if constexpr (BKSEG) {
+            // segment q's base and extent = entry 0 + entry q (wrapping arithmetic)
+            bsel[0] = reinterpret_cast<uint64_t>(p.B[0]);
+            bbsel[0] = p.b_bytes[0];
+#pragma unroll
+            for (int q = 1; q < 3; ++q) {
+                bsel[q] = reinterpret_cast<uint64_t>(p.B[q]) - bsel[0];
+                bbsel[q] = p.b_bytes[q] - bbsel[0];
+            }
+        } else {
+            const int sg = n0 / bseg;
+            nb0 = n0 - sg * bseg;
+            bsel[0] = reinterpret_cast<uint64_t>(p.B[sg]);
+            bbsel[0] = p.b_bytes[sg];
         }
-        boff = BKC ? (int64_t)nb0 * p.ldb : nb0;
-        la.init(wave, lane, p.lda, p.M - m0);
-        lb.init(wave, lane, p.ldb, p.N - n0);
+        boff = BKC ? (int64_t)nb0 * ldb : nb0;
+        la.init(wave, lane, lda, p.M - m0);
+        lb.init(wave, lane, ldb, p.N - n0);
         kbase = kb;
         nk = kn;
+        kend = min(p.K, (kb + kn) * BK);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -318,88 +379,104 @@ struct GemmCore {
     }
 
     // Global loads of k-step kt into registers.  The k advance moves the
-    // buffer base (scalar arithmetic); the lane offsets stay fixed.
-    __device__ __forceinline__ void load_stage(int kt) {
-        const int k0 = (kbase + kt) * BK;
-        const int krem = p.K - k0;
-        const int64_t ea = kadv(AK, k0, p.lda);
-        la.load(make_rsrc(abase + ea, abytes - (uint32_t)(ea * 2)), krem, ra);
-        int sg = bsg, kl = k0;
+    // buffer base (scalar arithmetic); the lane offsets stay fixed.  Past the
+    // K range every lane takes the out-of-range offset; the base then stays
+    // at k = 0 (no branch: a conditional 64-bit multiply would become one and
+    // split the scheduling region).
+    __device__ __forceinline__ void load_a(int kt, u32x4 (&v)[LA::NI]) const {
+        const int k0 = (kbase + kt) * BK, krem = kend - k0;
+        const int kc = krem > 0 ? k0 : 0;
+        const int64_t e = kadv(AK, kc, lda);
+        la.load(make_rsrc(abase + e, abytes - (uint32_t)(e * 2)), krem, v);
+    }
+    __device__ __forceinline__ void load_b(int kt, u32x4 (&v)[LB::NI]) const {
+        const int k0 = (kbase + kt) * BK, krem = kend - k0;
+        const int kc = krem > 0 ? k0 : 0;
+        int sg = 0, kl = kc;
         if constexpr (BKSEG) {
-            sg = k0 / p.bseg;
-            kl = k0 - sg * p.bseg;
+            sg = kc / bseg;
+            kl = kc - sg * bseg;
         }
-        const int64_t eb = boff + kadv(BKC, kl, p.ldb);
-        lb.load(make_rsrc(p.B[sg] + eb, p.b_bytes[sg] - (uint32_t)(eb * 2)), krem, rb);
+        const int64_t e = boff + kadv(BKC, kl, ldb);
+        // Segment base by arithmetic: a select between two loads of members
+        // is folded into one indexed load, which keeps the object in scratch.
+        const uint64_t s1 = sg == 1, s2 = sg == 2;
+        const bf16_t* b = reinterpret_cast<const bf16_t*>(bsel[0] + s1 * bsel[1] + s2 * bsel[2]);
+        const uint32_t nb = bbsel[0] + (uint32_t)s1 * bbsel[1] + (uint32_t)s2 * bbsel[2];
+        lb.load(make_rsrc(b + e, nb - (uint32_t)(e * 2)), krem, v);
     }
 
-    // Registers of k-step kt -> LDS slot kt % STAGES (swizzled layouts).
-    __device__ __forceinline__ void store_stage(int kt) {
-        char* base = smem + (kt % STAGES) * STAGE;
-        la.store(base, wave, lane, ra);
-        lb.store(base + A_BYTES, wave, lane, rb);
+    // Registers -> LDS slot (swizzled layouts).
+    __device__ __forceinline__ void store_a(int slot, const u32x4 (&v)[LA::NI]) const {
+        la.store(smem + slot * STAGE, wave, lane, v);
+    }
+    __device__ __forceinline__ void store_b(int slot, const u32x4 (&v)[LB::NI]) const {
+        lb.store(smem + slot * STAGE + A_BYTES, wave, lane, v);
     }
 
-    __device__ __forceinline__ void read_frags(int slot, FR& F) const {
+    __device__ __forceinline__ void read_sub(int slot, int kk, HF& F) const {
         const char* as = smem + slot * STAGE;
         const char* bs = as + A_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int i = 0; i < FM; ++i) {
+            if constexpr (AK) F.a[i] = frag_k(as, wm * WTM + i * 32, kk, lane);
+            else F.a[i] = frag_mn<BM>(as, wm * WTM + i * 32, kk, lane);
+        }
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if constexpr (AK) F.a[kk][i] = frag_k(as, wm * WTM + i * 32, kk, lane);
-                else F.a[kk][i] = frag_mn<BM>(as, wm * WTM + i * 32, kk, lane);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if constexpr (BKC) F.b[kk][j] = frag_k(bs, wn * WTN + j * 32, kk, lane);
-                else F.b[kk][j] = frag_mn<BN>(bs, wn * WTN + j * 32, kk, lane);
-            }
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (BKC) F.b[j] = frag_k(bs, wn * WTN + j * 32, kk, lane);
+            else F.b[j] = frag_mn<BN>(bs, wn * WTN + j * 32, kk, lane);
         }
     }
 
-    // One k-step, software-pipelined: the MFMAs of step kt run from registers
-    // (Fc) while step kt+2's data goes registers -> LDS, step kt+3's global
-    // loads are issued, and step kt+1's fragments are read into Fn.
-    // Slot safety: slot (kt+2)%3 held step kt-1, whose fragments every wave
-    // read before the barrier of step kt-1; slot (kt+1)%3 was written before
-    // this step's barrier.
-    __device__ __forceinline__ void step(int kt, FR& Fc, FR& Fn) {
-        run_mfmas<0, HEAD>(acc, Fc);
-        if (kt + 2 < nk) {
-            wait_vm_lgkm<0>();
-            store_stage(kt + 2);
-        }
-        if (kt + 3 < nk) load_stage(kt + 3);
-        if (kt + 1 < nk) {
-            wait_lgkm();
-            stage_barrier();
-            read_frags((kt + 1) % STAGES, Fn);
-        }
-        run_mfmas<HEAD, NMF>(acc, Fc);
+    // Step kt, kt & 1 == P; on entry Fa holds k16 #0 of step kt (possibly in flight).
+    template <int P>
+    __device__ __forceinline__ void step(int kt, HF& Fa, HF& Fb) {
+        constexpr int R = (P ^ 1) % NSET;  // registers holding step kt+1
+        run_mfmas<0, NM>(acc, Fa);
+        read_sub(P, 1, Fb);
+        store_a(P ^ 1, ra[R]);
+        load_a(kt + 1 + NSET, ra[R]);
+        interleave<NM, NRD, LA::NI, LA::NI>();
+        run_mfmas<0, NM>(acc, Fb);
+        read_sub(P, 2, Fa);
+        store_b(P ^ 1, rb[R]);
+        load_b(kt + 1 + NSET, rb[R]);
+        interleave<NM, NRD, LB::NI, LB::NI>();
+        run_mfmas<0, NM>(acc, Fa);
+        read_sub(P, 3, Fb);
+        interleave<NM, NRD, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm();
+        run_mfmas<0, PRE>(acc, Fb);
+        stage_barrier();
+        run_mfmas<PRE, NM>(acc, Fb);
+        read_sub(P ^ 1, 0, Fa);
+        interleave<NM - PRE, NRD, 0, 0>();
     }
 
     __device__ __forceinline__ void run() {
         if (nk <= 0) return;
-        load_stage(0);
-        wait_vm_lgkm<0>();
-        store_stage(0);
-        if (nk > 1) {
-            load_stage(1);
-            wait_vm_lgkm<0>();
-            store_stage(1);
+        load_a(0, ra[0]);
+        load_b(0, rb[0]);
+        if constexpr (NSET == 2) {
+            load_a(1, ra[1]);
+            load_b(1, rb[1]);
         }
-        if (nk > 2) load_stage(2);
+        store_a(0, ra[0]);
+        store_b(0, rb[0]);
+        load_a(NSET, ra[0]);
+        load_b(NSET, rb[0]);
         wait_lgkm();
         stage_barrier();
-        FR F0, F1;
-        read_frags(0, F0);
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            step(kt, F0, F1);
-            step(kt + 1, F1, F0);
+        HF Fa, Fb;
+        read_sub(0, 0, Fa);
+        // An odd step count gets one more step: its operands were loaded past
+        // the K range, so they are zeros and add nothing.
+        for (int kt = 0; kt < nk; kt += 2) {
+            step<0>(kt, Fa, Fb);
+            step<1>(kt + 1, Fa, Fb);
         }
-        if (kt < nk) step(kt, F0, F1);
         wait_vm_lgkm<0>();
     }
 };
