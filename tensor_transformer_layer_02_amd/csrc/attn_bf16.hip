@@ -5,22 +5,36 @@
 // section "The attention heads split").  Scores are Q K^T / sqrt(d) with an
 // optional causal mask (key m allowed for query j iff m <= j).
 //
-// Forward: a workgroup owns 64 queries of one (sequence, head); each wave64
-// owns 16 of them.  Keys and values stream through LDS in blocks of 64.  The
-// score tile is formed transposed, S^T = K Q^T, so that each lane holds ONE
-// query (lane % 16) and 16 of its keys: the running max and sum of the online
-// softmax are lane-local plus a 4-lane butterfly.  O^T = V^T P^T keeps the same
-// lane<->query mapping, so rescaling O by the softmax correction is
-// lane-local too.  The kernel writes O token-major and the per-query
-// log-sum-exp (natural log) for the backward.
+// All products use v_mfma_f32_32x32x16_bf16.  For an operand tile the lane
+// l holds row (or column) l % 32 and, per k16 chunk, the 8 k-slots
+// 8*(l/32) .. +7; the 32x32 result gives lane l column l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
+//
+// Forward: a workgroup owns 128 queries of one (sequence, head), a wave 32 of
+// them.  Scores are formed transposed, S^T = K Q^T, so that each lane holds
+// ONE query and 16 keys of a 32-key block: the online-softmax max and sum are
+// lane-local (plus one exchange between the lane pair l, l^32).  O^T = V^T P^T
+// takes P^T straight from those registers: the k-slots of a k16 chunk are
+// relabelled to the keys the lane already holds (slot s of chunk c is key
+// 16c + 8*(s/4) + 4*(l/32) + s%4), and the V^T fragment is read with the
+// same labelling by transposed LDS reads (ds_read_b64_tr_b16), which give a
+// lane 4 consecutive rows of one column.  K and V stream through LDS in
+// 64-key blocks, prefetched into registers one block ahead.
 //
 // Backward: P is recomputed from Q, K and the saved log-sum-exp.
 //   D_j = dO_j . O_j            (row sums, equal to sum_m P_jm dP_jm)
-//   dV = P^T dO, dK = dS^T Q / sqrt(d)     one workgroup per 64 keys
-//   dQ = dS K / sqrt(d)                    one workgroup per 64 queries
+//   dV = P^T dO, dK = dS^T Q / sqrt(d)     a workgroup per 128 keys
+//   dQ = dS K / sqrt(d)                    a workgroup per 128 queries
 // with dP = dO V^T and dS = P * (dP - D).  Splitting dQ into its own pass
 // keeps every output written by exactly one workgroup (no atomics; the result
-// is deterministic) at the price of recomputing S and dP once more.
+// is deterministic) at the price of recomputing S and dP once more.  The
+// dK/dV pass forms S and dP with rows = queries and lane = key, so P^T and
+// dS^T feed the next products from registers in the same way.
+//
+// LDS tiles are [rows][D] bf16 with the 16-byte chunks of each row permuted
+// by an XOR of row bits, chosen so that both the 16-byte fragment reads (16
+// rows, one chunk) and the transposed reads (8 rows x 4 chunks) hit every
+// bank at most once per half-wave.
 #include <cfloat>
 #include <cmath>
 
@@ -31,12 +45,13 @@ namespace tp {
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int BQ = 64;   // queries per workgroup
-constexpr int BKV = 64;  // keys per LDS block
-constexpr int LDT = BKV + 8;  // row stride of transposed ([d][64]) LDS tiles
+constexpr int NT = 256;   // 4 waves
+constexpr int BQ = 128;   // queries per workgroup (forward, dQ) / keys per workgroup (dK, dV)
+constexpr int BKV = 64;   // rows per streamed LDS block
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
+
+typedef __attribute__((ext_vector_type(4))) short v4i16;
 
 struct AttnArgs {
     int batch, seq, heads, causal;
@@ -54,159 +69,226 @@ struct AttnArgs {
 };
 
 __device__ __forceinline__ u32x4 ld16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 ld8(const bf16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int i) {
-    const uint32_t w = v[i >> 1];
-    return (i & 1) ? (w >> 16) : (w & 0xffffu);
+__device__ __forceinline__ int bit(int r, int i) { return (r >> i) & 1; }
+
+// 2^x on the hardware unit (no range fix-ups: inputs below -126 give 0 or a
+// denormal, which only ever scales softmax terms that are negligible).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// True on every lane iff `p` holds on some lane of the wave.
+__device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Chunk permutation of row r of a [rows][D] tile (16-byte chunks).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 64) return bit(r, 2) | (bit(r, 3) << 1) | (bit(r, 1) << 2);
+    else if constexpr (D == 128) return bit(r, 2) | (bit(r, 3) << 1) | (bit(r, 0) << 2) | (bit(r, 1) << 3);
+    else return (r >> 2) & 3;  // D = 32, 96
 }
 
-// Stage 64 rows x D columns of a row-major bf16 matrix (rows >= nvalid read
-// as zero) into LDS: STRAIGHT as [64][D + 8], TRANSP as [D][64 + 8].
-template <int D, bool STRAIGHT, bool TRANSP>
-__device__ __forceinline__ void stage_rows(const bf16_t* __restrict__ src, int64_t ld, int row0, int nvalid,
-                                           bf16_t* straight, bf16_t* transp, int tid) {
-    constexpr int LDK = D + 8;
-    constexpr int CH = D / 8;
-    for (int u = tid; u < 16 * CH; u += NT) {
-        const int dc = (u % CH) * 8, rq = (u / CH) * 4;
-        u32x4 v[4];
+// Byte offset of element (r, col) in a swizzled [rows][D] tile.
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+    return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + (col & 7) * 2;
+}
+
+// A 64-row block of a row-major bf16 matrix on its way global -> registers
+// -> LDS (rows >= nvalid are zeros).  Thread t moves chunks t + 256 i.
+template <int D>
+struct BlockLoader {
+    static constexpr int CH = D / 8;            // chunks per row
+    static constexpr int NI = BKV * CH / NT;    // chunks per thread
+    static_assert((BKV * CH) % NT == 0, "block must split evenly");
+    u32x4 v[NI];
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ src, int64_t ld, int row0, int nvalid, int tid) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = row0 + rq + j;
-            v[j] = (r < nvalid) ? ld16(src + (int64_t)r * ld + dc) : u32x4{0u, 0u, 0u, 0u};
-        }
-        if constexpr (STRAIGHT) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(straight + (rq + j) * LDK + dc) = v[j];
-        }
-        if constexpr (TRANSP) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                u32x2 t;
-                t[0] = half_of(v[0], i) | (half_of(v[1], i) << 16);
-                t[1] = half_of(v[2], i) | (half_of(v[3], i) << 16);
-                *reinterpret_cast<u32x2*>(transp + (dc + i) * LDT + rq) = t;
-            }
+        for (int i = 0; i < NI; ++i) {
+            const int u = tid + NT * i, r = u / CH, c = u % CH;
+            v[i] = (row0 + r < nvalid) ? ld16(src + (int64_t)(row0 + r) * ld + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = tid + NT * i, r = u / CH, c = u % CH;
+            *reinterpret_cast<u32x4*>(tile + toff<D>(r, c * 8)) = v[i];
+        }
+    }
+};
+
+// Operand fragment of rows rb .. rb+31 of a tile, k = d chunk c (16 wide):
+// lane l gets row rb + l%32, d = 16c + 8*(l/32) .. +7.
+template <int D>
+__device__ __forceinline__ u32x4 frag_rows(const char* tile, int rb, int c, int lane) {
+    return *reinterpret_cast<const u32x4*>(tile + toff<D>(rb + (lane & 31), 16 * c + 8 * (lane >> 5)));
 }
 
-// A-operand fragment from a transposed [d][64] LDS tile: row (lane % 16) of
-// subtile ds, the 8 keys (or queries) {32j + 4g .. +3, 32j + 16 + 4g .. +3},
-// g = lane / 16 -- the same 8 indices a lane holds in a 16x16 result pair.
-__device__ __forceinline__ u32x4 frag_t(const bf16_t* t, int ds, int j, int lane) {
-    const bf16_t* p = t + (ds * 16 + (lane & 15)) * LDT + 32 * j + (lane >> 4) * 4;
-    const u32x2 lo = ld8(p), hi = ld8(p + 16);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+// Operand fragment with rows = d (32db .. +31) and k = tile rows 16kc .. +15
+// in the relabelled order: slot s of lane l is tile row
+// 16kc + 8*(s/4) + 4*(l/32) + s%4.  Two transposed reads; in each 16-lane
+// group lane j addresses tile row base + j/4, d 4*(j%4) .. +3 of the group's
+// 16 columns, and lane i receives column i, 4 consecutive rows.
+template <int D>
+__device__ __forceinline__ u32x4 frag_tr(const char* tile, int db, int kc, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int col = 32 * db + 16 * (G & 1) + 4 * (j & 3);
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 16 * kc + 8 * h + 4 * (G >> 1) + (j >> 2);
+        const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(tile + toff<D>(r, col)));
+        const u32x2 w = __builtin_bit_cast(u32x2, t);
+        out[2 * h] = w[0];
+        out[2 * h + 1] = w[1];
+    }
+    return out;
 }
 
-// Pack the result-layout values of 16x16 subtiles 2j and 2j+1 into one
-// 8-element bf16 operand fragment (matching frag_t's index order).
-__device__ __forceinline__ u32x4 pack_pair(const f32x4& a, const f32x4& b) {
-    return u32x4{pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3])};
+// bf16 operand fragment (k16 chunk kc of a 64-row block) from the fp32
+// result registers of its 32-row half: slots s = values r = 8*(kc%2) + s.
+__device__ __forceinline__ u32x4 pack_chunk(const f32x16& v, int half) {
+    const int o = 8 * half;
+    return u32x4{pack_bf2(v[o], v[o + 1]), pack_bf2(v[o + 2], v[o + 3]), pack_bf2(v[o + 4], v[o + 5]),
+                 pack_bf2(v[o + 6], v[o + 7])};
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return z;
+}
+
+// Row index (within a 32-row result block) of value r for lane l.
+__device__ __forceinline__ int res_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Store a [D x 32] transposed fp32 accumulator (rows = d, lane column = one
+// token row of `out`) as bf16, times `mul`: 4 consecutive d per 8-byte store.
+template <int D>
+__device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x16 (&acc)[D / 32], float mul, int lane) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x2 t;
+            t[0] = pack_bf2(acc[db][4 * q] * mul, acc[db][4 * q + 1] * mul);
+            t[1] = pack_bf2(acc[db][4 * q + 2] * mul, acc[db][4 * q + 3] * mul);
+            *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * (lane >> 5)) = t;
+        }
 }
 
 template <int D>
-__global__ void __launch_bounds__(NT) attn_fwd_kernel(const AttnArgs a) {
-    constexpr int KS = D / 32, DS = D / 16, LDK = D + 8;
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[BKV * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[D * LDT];
+__global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(const AttnArgs a) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // 2 slots x (K, V)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
     const int nqb = (s + BQ - 1) / BQ;
     const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ;
-    const int qw = q0 + wave * 16 + (lane & 15);
+    const int q0 = qb * BQ, qw0 = q0 + 32 * wave;
+    const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
     const bf16_t* Vg = Qg + 2 * a.w;
 
-    u32x4 qf[KS];
+    u32x4 qf[KC];  // Q^T operand: column = query, k = d
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = (qw < s) ? ld16(Qg + (int64_t)qw * a.ld_qkv + ks * 32 + grp * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < KC; ++c)
+        qf[c] = (qw < s) ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
 
-    f32x4 oacc[DS];
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int i = 0; i < DS; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DB; ++i) oacc[i] = zero16();
     float mrow = -INFINITY, lsum = 0.f;
 
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
+    BlockLoader<D> lk, lv;
+    lk.load(Kg, a.ld_qkv, 0, s, tid);
+    lv.load(Vg, a.ld_qkv, 0, s, tid);
+    lk.store(smem, tid);
+    lv.store(smem + TILE, tid);
+    __syncthreads();
+
     for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = kb * BKV;
-        stage_rows<D, true, false>(Kg, a.ld_qkv, k0, s, Ks, nullptr, tid);
-        stage_rows<D, false, true>(Vg, a.ld_qkv, k0, s, nullptr, Vt, tid);
-        __syncthreads();
-
-        f32x4 sacc[4];
+        const bool more = kb + 1 < nkb;
+        if (more) {
+            lk.load(Kg, a.ld_qkv, k0 + BKV, s, tid);
+            lv.load(Vg, a.ld_qkv, k0 + BKV, s, tid);
+        }
+        const char* Kt = smem + (kb & 1) * 2 * TILE;
+        const char* Vt = Kt + TILE;
+        if (!(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
+            f32x16 sacc[2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < 2; ++h) {
+                sacc[h] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 af = ld16(Ks + (kt * 16 + (lane & 15)) * LDK + ks * 32 + grp * 8);
-                sacc[kt] = mfma16x16x32(af, qf[ks], sacc[kt]);
+                for (int c = 0; c < KC; ++c) sacc[h] = mfma32x32x16(frag_rows<D>(Kt, 32 * h, c, lane), qf[c], sacc[h]);
+            }
+            // Masks only where the block reaches past the diagonal or the
+            // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
+            // the max and the exponent.
+            if ((a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * h + res_row(r, lane);
+                        if (key >= s || (a.causal && key > qw)) sacc[h][r] = -INFINITY;
+                    }
+            }
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[h][r]);
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+            const float mnew = fmaxf(mrow, bmax * a.scale_log2);
+            const float msub = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = ex2(mrow - msub);
+            float psum = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -msub));
+                    sacc[h][r] = pv;
+                    psum += pv;
+                }
+            lsum = lsum * alpha + psum;
+            mrow = mnew;
+            if (any_lane(alpha != 1.f)) {
+#pragma unroll
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const u32x4 pf = pack_chunk(sacc[kc >> 1], kc & 1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(frag_tr<D>(Vt, db, kc, lane), pf, oacc[db]);
             }
         }
-        // lane: query qw, keys k0 + kt*16 + 4*grp + r
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kt * 16 + grp * 4 + r;
-                float x = sacc[kt][r] * a.scale_log2;
-                if (key >= s || (a.causal && key > qw)) x = -INFINITY;
-                sacc[kt][r] = x;
-                bmax = fmaxf(bmax, x);
-            }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float mnew = fmaxf(mrow, bmax);
-        const float msub = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(mrow - msub);
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pv = exp2f(sacc[kt][r] - msub);
-                sacc[kt][r] = pv;
-                psum += pv;
-            }
-        lsum = lsum * alpha + psum;
-        mrow = mnew;
-#pragma unroll
-        for (int i = 0; i < DS; ++i) oacc[i] *= alpha;
-
-        const u32x4 pf0 = pack_pair(sacc[0], sacc[1]);
-        const u32x4 pf1 = pack_pair(sacc[2], sacc[3]);
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            oacc[ds] = mfma16x16x32(frag_t(Vt, ds, 0, lane), pf0, oacc[ds]);
-            oacc[ds] = mfma16x16x32(frag_t(Vt, ds, 1, lane), pf1, oacc[ds]);
+        if (more) {  // slot (kb+1)&1 was last read in iteration kb-1, before its closing barrier
+            char* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+            lk.store(nxt, tid);
+            lv.store(nxt + TILE, tid);
         }
         __syncthreads();
     }
 
-    lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
     if (qw < s) {
-        const float inv = 1.f / lsum;
-        bf16_t* orow = a.O + ((int64_t)b * s + qw) * a.ld_o + g * D + grp * 4;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            u32x2 t;
-            t[0] = pack_bf2(oacc[ds][0] * inv, oacc[ds][1] * inv);
-            t[1] = pack_bf2(oacc[ds][2] * inv, oacc[ds][3] * inv);
-            *reinterpret_cast<u32x2*>(orow + ds * 16) = t;
-        }
-        if (grp == 0) a.lse[((int64_t)b * a.heads + g) * s + qw] = (mrow + log2f(lsum)) * LN2;
+        store_rowT<D>(a.O + ((int64_t)b * s + qw) * a.ld_o + g * D, oacc, 1.f / lsum, lane);
+        if (lane < 32) a.lse[((int64_t)b * a.heads + g) * s + qw] = (mrow + log2f(lsum)) * LN2;
     }
 }
 
@@ -225,28 +307,57 @@ __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
     for (int c = 0; c < D; c += 8) {
         const u32x4 ov = ld16(o + c), dv = ld16(d + c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += bf2f((bf16_t)half_of(ov, i)) * bf2f((bf16_t)half_of(dv, i));
+        for (int i = 0; i < 4; ++i) {
+            acc += __uint_as_float(ov[i] << 16) * __uint_as_float(dv[i] << 16);
+            acc += __uint_as_float(ov[i] & 0xffff0000u) * __uint_as_float(dv[i] & 0xffff0000u);
+        }
     }
     const int b = (int)(r / a.seq), j = (int)(r % a.seq);
     a.Dq[((int64_t)b * a.heads + g) * a.seq + j] = acc;
 }
 
+// One 64-query block for the dK/dV pass: Q and dO rows plus, for threads
+// < 64, one query's log2-scaled log-sum-exp and D.  (A struct, not lambdas:
+// closure types in a kernel template defeat the host-side stub emission of
+// later instantiations with this compiler.)
 template <int D>
-__global__ void __launch_bounds__(NT) attn_bwd_dkdv_kernel(const AttnArgs a) {
-    constexpr int KS = D / 32, DS = D / 16, LDK = D + 8;
-    __shared__ __attribute__((aligned(16))) bf16_t Qs[BQ * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t dOs[BQ * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Qt[D * LDT];
-    __shared__ __attribute__((aligned(16))) bf16_t dOt[D * LDT];
-    __shared__ float lse2s[BQ];
-    __shared__ float Dqs[BQ];
+struct QBlock {
+    static constexpr int TILE = BKV * D * 2;
+    static constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, log2-scaled LSE, D
+    BlockLoader<D> lq, lo;
+    float lsev = 0.f, dval = 0.f;
+    __device__ __forceinline__ void fetch(const AttnArgs& a, const bf16_t* Qg, const bf16_t* dOg, const float* lseg,
+                                          const float* Dg, int q0, int tid) {
+        lq.load(Qg, a.ld_qkv, q0, a.seq, tid);
+        lo.load(dOg, a.ld_o, q0, a.seq, tid);
+        if (tid < BKV) {
+            const int q = q0 + tid;
+            lsev = q < a.seq ? lseg[q] * LOG2E : 0.f;
+            dval = q < a.seq ? Dg[q] : 0.f;
+        }
+    }
+    __device__ __forceinline__ void put(char* slot, int tid) const {
+        lq.store(slot, tid);
+        lo.store(slot + TILE, tid);
+        if (tid < BKV) {
+            reinterpret_cast<float*>(slot + 2 * TILE)[tid] = lsev;
+            reinterpret_cast<float*>(slot + 2 * TILE + BKV * 4)[tid] = dval;
+        }
+    }
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+// dK, dV for 128 keys (32 per wave); query blocks of 64 stream through LDS.
+template <int D>
+__global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = QBlock<D>::TILE, SLOT = QBlock<D>::SLOT;
+    __shared__ __attribute__((aligned(16))) char smem[2 * SLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const int kb = blockIdx.x;
+    const int kblk = (int)blockIdx.x;  // causal: low keys see the most queries and go first
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int k0 = kb * BKV;
-    const int kw = k0 + wave * 16 + (lane & 15);  // this lane's key
+    const int k0 = kblk * BQ, kw0 = k0 + 32 * wave;
+    const int kw = kw0 + (lane & 31);  // this lane's key
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
@@ -255,162 +366,182 @@ __global__ void __launch_bounds__(NT) attn_bwd_dkdv_kernel(const AttnArgs a) {
     const float* lseg = a.lse + ((int64_t)b * a.heads + g) * s;
     const float* Dg = a.Dq + ((int64_t)b * a.heads + g) * s;
 
-    u32x4 kf[KS], vf[KS];
+    u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int c = 0; c < KC; ++c) {
         const bool ok = kw < s;
-        kf[ks] = ok ? ld16(Kg + (int64_t)kw * a.ld_qkv + ks * 32 + grp * 8) : u32x4{0u, 0u, 0u, 0u};
-        vf[ks] = ok ? ld16(Vg + (int64_t)kw * a.ld_qkv + ks * 32 + grp * 8) : u32x4{0u, 0u, 0u, 0u};
+        const int64_t o = (int64_t)kw * a.ld_qkv + 16 * c + 8 * (lane >> 5);
+        kf[c] = ok ? ld16(Kg + o) : u32x4{0u, 0u, 0u, 0u};
+        vf[c] = ok ? ld16(Vg + o) : u32x4{0u, 0u, 0u, 0u};
     }
-    f32x4 dk[DS], dv[DS];
+    f32x16 dk[DB], dv[DB];
 #pragma unroll
-    for (int i = 0; i < DS; ++i) dk[i] = dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
 
-    const int nqb = (s + BQ - 1) / BQ;
-    const int qb0 = a.causal ? (k0 / BQ) : 0;
+    const int nqb = (s + BKV - 1) / BKV;
+    const int qb0 = a.causal ? (k0 / BKV) : 0;
+    QBlock<D> nb;
+    if (qb0 < nqb) {
+        nb.fetch(a, Qg, dOg, lseg, Dg, qb0 * BKV, tid);
+        nb.put(smem, tid);
+    }
+    __syncthreads();
+
     for (int qb = qb0; qb < nqb; ++qb) {
-        const int q0 = qb * BQ;
-        stage_rows<D, true, true>(Qg, a.ld_qkv, q0, s, Qs, Qt, tid);
-        stage_rows<D, true, true>(dOg, a.ld_o, q0, s, dOs, dOt, tid);
-        if (tid < BQ) {
-            const int q = q0 + tid;
-            lse2s[tid] = q < s ? lseg[q] * LOG2E : 0.f;
-            Dqs[tid] = q < s ? Dg[q] : 0.f;
-        }
-        __syncthreads();
-
-        // S = Q K^T and dP = dO V^T: rows = queries (4 subtiles), column = this lane's key.
-        f32x4 sacc[4], pacc[4];
+        const int q0 = qb * BKV;
+        const bool more = qb + 1 < nqb;
+        if (more) nb.fetch(a, Qg, dOg, lseg, Dg, q0 + BKV, tid);
+        const char* slot = smem + ((qb - qb0) & 1) * SLOT;
+        const char* Qt = slot;
+        const char* dOt = slot + TILE;
+        const float* lse2 = reinterpret_cast<const float*>(slot + 2 * TILE);
+        const float* Dl = lse2 + BKV;
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-            sacc[qt] = pacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) {  // 32-query half of the block
+            const int qh0 = q0 + 32 * h;
+            if (a.causal && qh0 + 31 < kw0) continue;  // every query precedes every key of this wave
+            f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int off = (qt * 16 + (lane & 15)) * LDK + ks * 32 + grp * 8;
-                sacc[qt] = mfma16x16x32(ld16(Qs + off), kf[ks], sacc[qt]);
-                pacc[qt] = mfma16x16x32(ld16(dOs + off), vf[ks], pacc[qt]);
+            for (int c = 0; c < KC; ++c) {
+                sacc = mfma32x32x16(frag_rows<D>(Qt, 32 * h, c, lane), kf[c], sacc);
+                pacc = mfma32x32x16(frag_rows<D>(dOt, 32 * h, c, lane), vf[c], pacc);
+            }
+            // rows = queries qh0 + res_row(r), column = this lane's key
+            const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ql = 32 * h + 8 * r4 + 4 * (lane >> 5);
+                const f32x4 L = *reinterpret_cast<const f32x4*>(lse2 + ql);
+                const f32x4 Dd = *reinterpret_cast<const f32x4*>(Dl + ql);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * r4 + e, q = q0 + ql + e;
+                    float pv = ex2(fmaf(sacc[r], a.scale_log2, -L[e]));
+                    if (edge && !(q < s && kw < s && (!a.causal || kw <= q))) pv = 0.f;
+                    sacc[r] = pv;
+                    pacc[r] = pv * (pacc[r] - Dd[e]);
+                }
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const u32x4 pf = pack_chunk(sacc, half), sf = pack_chunk(pacc, half);
+                const int kc = 2 * h + half;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dv[db] = mfma32x32x16(pf, frag_tr<D>(dOt, db, kc, lane), dv[db]);
+                    dk[db] = mfma32x32x16(sf, frag_tr<D>(Qt, db, kc, lane), dk[db]);
+                }
             }
         }
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ql = qt * 16 + grp * 4 + r, q = q0 + ql;
-                const bool ok = q < s && kw < s && (!a.causal || kw <= q);
-                const float pv = ok ? exp2f(sacc[qt][r] * a.scale_log2 - lse2s[ql]) : 0.f;
-                sacc[qt][r] = pv;
-                pacc[qt][r] = pv * (pacc[qt][r] - Dqs[ql]);
-            }
-        const u32x4 pf0 = pack_pair(sacc[0], sacc[1]), pf1 = pack_pair(sacc[2], sacc[3]);
-        const u32x4 sf0 = pack_pair(pacc[0], pacc[1]), sf1 = pack_pair(pacc[2], pacc[3]);
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            dv[ds] = mfma16x16x32(pf0, frag_t(dOt, ds, 0, lane), dv[ds]);
-            dv[ds] = mfma16x16x32(pf1, frag_t(dOt, ds, 1, lane), dv[ds]);
-            dk[ds] = mfma16x16x32(sf0, frag_t(Qt, ds, 0, lane), dk[ds]);
-            dk[ds] = mfma16x16x32(sf1, frag_t(Qt, ds, 1, lane), dk[ds]);
-        }
+        if (more) nb.put(smem + ((qb + 1 - qb0) & 1) * SLOT, tid);
         __syncthreads();
     }
 
-    // result layout: keys k0 + wave*16 + 4*grp + r, column ds*16 + lane % 16
+    // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
     bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
     bf16_t* dVg = dKg + a.w;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int key = k0 + wave * 16 + grp * 4 + r;
+    for (int r = 0; r < 16; ++r) {
+        const int key = kw0 + res_row(r, lane);
         if (key >= s) continue;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            const int c = ds * 16 + (lane & 15);
-            dKg[(int64_t)key * a.ld_qkv + c] = f2bf(dk[ds][r] * a.scale);
-            dVg[(int64_t)key * a.ld_qkv + c] = f2bf(dv[ds][r]);
+        for (int db = 0; db < DB; ++db) {
+            const int c = 32 * db + (lane & 31);
+            dKg[(int64_t)key * a.ld_qkv + c] = f2bf(dk[db][r] * a.scale);
+            dVg[(int64_t)key * a.ld_qkv + c] = f2bf(dv[db][r]);
         }
     }
 }
 
+// dQ for 128 queries (32 per wave); key blocks of 64 stream through LDS.
 template <int D>
-__global__ void __launch_bounds__(NT) attn_bwd_dq_kernel(const AttnArgs a) {
-    constexpr int KS = D / 32, DS = D / 16, LDK = D + 8;
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[BKV * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Vs[BKV * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Kt[D * LDT];
+__global__ void __launch_bounds__(NT, D <= 96 ? 2 : 1) attn_bwd_dq_kernel(const AttnArgs a) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // 2 slots x (K, V)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
     const int nqb = (s + BQ - 1) / BQ;
     const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ;
-    const int qw = q0 + wave * 16 + (lane & 15);  // this lane's query
+    const int q0 = qb * BQ, qw0 = q0 + 32 * wave;
+    const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
     const bf16_t* Vg = Qg + 2 * a.w;
     const bf16_t* dOg = a.dO + (int64_t)b * s * a.ld_o + g * D;
 
-    u32x4 qf[KS], of[KS];
+    u32x4 qf[KC], of[KC];  // Q^T, dO^T operands: column = query, k = d
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int c = 0; c < KC; ++c) {
         const bool ok = qw < s;
-        qf[ks] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + ks * 32 + grp * 8) : u32x4{0u, 0u, 0u, 0u};
-        of[ks] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + ks * 32 + grp * 8) : u32x4{0u, 0u, 0u, 0u};
+        qf[c] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+        of[c] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
     }
     const int64_t hrow = ((int64_t)b * a.heads + g) * s;
     const float lse2 = qw < s ? a.lse[hrow + qw] * LOG2E : 0.f;
     const float Dv = qw < s ? a.Dq[hrow + qw] : 0.f;
 
-    f32x4 dq[DS];
+    f32x16 dq[DB];
 #pragma unroll
-    for (int i = 0; i < DS; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DB; ++i) dq[i] = zero16();
 
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
+    BlockLoader<D> lk, lv;
+    lk.load(Kg, a.ld_qkv, 0, s, tid);
+    lv.load(Vg, a.ld_qkv, 0, s, tid);
+    lk.store(smem, tid);
+    lv.store(smem + TILE, tid);
+    __syncthreads();
+
     for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = kb * BKV;
-        stage_rows<D, true, true>(Kg, a.ld_qkv, k0, s, Ks, Kt, tid);
-        stage_rows<D, true, false>(Vg, a.ld_qkv, k0, s, Vs, nullptr, tid);
-        __syncthreads();
-
-        // S^T = K Q^T and dP^T = V dO^T: rows = keys (4 subtiles), column = this lane's query.
-        f32x4 sacc[4], pacc[4];
+        const bool more = kb + 1 < nkb;
+        if (more) {
+            lk.load(Kg, a.ld_qkv, k0 + BKV, s, tid);
+            lv.load(Vg, a.ld_qkv, k0 + BKV, s, tid);
+        }
+        const char* Kt = smem + (kb & 1) * 2 * TILE;
+        const char* Vt = Kt + TILE;
+        if (!(a.causal && k0 > qw0 + 31)) {
+            f32x16 sacc[2], pacc[2];  // S^T and dP^T: rows = keys, column = this lane's query
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sacc[kt] = pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < 2; ++h) {
+                sacc[h] = pacc[h] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int off = (kt * 16 + (lane & 15)) * LDK + ks * 32 + grp * 8;
-                sacc[kt] = mfma16x16x32(ld16(Ks + off), qf[ks], sacc[kt]);
-                pacc[kt] = mfma16x16x32(ld16(Vs + off), of[ks], pacc[kt]);
+                for (int c = 0; c < KC; ++c) {
+                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, 32 * h, c, lane), qf[c], sacc[h]);
+                    pacc[h] = mfma32x32x16(frag_rows<D>(Vt, 32 * h, c, lane), of[c], pacc[h]);
+                }
+            }
+            const bool edge = (a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s || qw0 + 32 > s;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * h + res_row(r, lane);
+                    float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -lse2));
+                    if (edge && !(qw < s && key < s && (!a.causal || key <= qw))) pv = 0.f;
+                    pacc[h][r] = pv * (pacc[h][r] - Dv);
+                }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const u32x4 sf = pack_chunk(pacc[kc >> 1], kc & 1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(frag_tr<D>(Kt, db, kc, lane), sf, dq[db]);
             }
         }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kt * 16 + grp * 4 + r;
-                const bool ok = qw < s && key < s && (!a.causal || key <= qw);
-                const float pv = ok ? exp2f(sacc[kt][r] * a.scale_log2 - lse2) : 0.f;
-                pacc[kt][r] = pv * (pacc[kt][r] - Dv);
-            }
-        const u32x4 sf0 = pack_pair(pacc[0], pacc[1]), sf1 = pack_pair(pacc[2], pacc[3]);
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            dq[ds] = mfma16x16x32(sf0, frag_t(Kt, ds, 0, lane), dq[ds]);
-            dq[ds] = mfma16x16x32(sf1, frag_t(Kt, ds, 1, lane), dq[ds]);
+        if (more) {
+            char* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+            lk.store(nxt, tid);
+            lv.store(nxt + TILE, tid);
         }
         __syncthreads();
     }
 
-    bf16_t* dQg = a.dqkv + (int64_t)b * s * a.ld_qkv + g * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int q = q0 + wave * 16 + grp * 4 + r;
-        if (q >= s) continue;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            dQg[(int64_t)q * a.ld_qkv + ds * 16 + (lane & 15)] = f2bf(dq[ds][r] * a.scale);
-    }
+    if (qw < s) store_rowT<D>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
 }
 
 AttnArgs make_args(const AttnDesc& d) {

@@ -14,19 +14,18 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_hw;
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 in the default
+// rounding mode); NaN stays a NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Two fp32 -> packed pair of bf16 (lo = a, hi = b).
+// Two fp32 -> packed pair of bf16 (lo = a, hi = b), one instruction.
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+    const bf16x2_hw v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // GeLU(u) = u * Phi(u) with Phi(u) = (1 + erf(u / sqrt 2)) / 2 (exact form).
