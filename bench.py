@@ -32,6 +32,9 @@ if ROOT not in sys.path:
 METRIC = "shard-layer fwd+bwd TFLOP/s and % of bf16 MFMA peak, 8.3B-shape t=8 shard"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per step launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (copy-calibrated),
+# valid while the kernel sources hash to the value recorded in the file
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_per_step_gpt8b_t8.txt")
 
 
 def log(*a):
@@ -62,11 +65,6 @@ def step_costs(cfg):
         "ATTN_DBIAS": (0, 3 * T * w * e + 3 * w * 4),
         "ATTN_DX": (g(T, h, 3 * w), (3 * T * w + 3 * w * h + T * h) * e),
     }
-
-
-# Steps that are a single kernel launch (usable for the roofline of "the dominant kernel").
-SINGLE_KERNEL = {"MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DX",
-                 "ATTN_DO", "ATTN_DX"}
 
 
 class HipEvents:
@@ -136,6 +134,9 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,6 +155,16 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
     cfg = CONFIGS[args.config]
     if not cfg.backward:
         cfg = cfg.with_(backward=True)
@@ -198,6 +209,7 @@ def main():
         torch.cuda.synchronize()
         ms_hooked = e0.elapsed_time(e1) / K
         counts = [tp.tp_profile_count(s) for s in range(nst)]
+        nkern = [tp.tp_profile_kernels(s) for s in range(nst)]
         tp.tp_profile_enable(None, 0)
         costs = step_costs(cfg)
         for s, name in enumerate(tp.STEPS):
@@ -208,6 +220,7 @@ def main():
             avg = sum(durs) / n
             fl, by = costs[name]
             kernels.append({"step": name, "avg_us": round(avg * 1e3, 2), "launches": n,
+                            "kernels_per_launch": round(nkern[s] / counts[s], 3),
                             "tflops": round(fl / (avg * 1e-3) / 1e12, 1) if fl else None,
                             "gbs": round(by / (avg * 1e-3) / 1e9, 1)})
         ev.close()
@@ -218,12 +231,25 @@ def main():
         for k in kernels:
             log(f"  {k['step']:<14} {k['avg_us']:9.2f} us  {k['share'] * 100:5.1f}%  "
                 f"{(str(k['tflops']) + ' TF/s') if k['tflops'] else '':>14}  {k['gbs']:8.1f} GB/s")
-        dom = max((k for k in kernels if k["step"] in SINGLE_KERNEL), key=lambda k: k["avg_us"])
+        # the dominant kernel: the longest step that is exactly one kernel launch
+        dom = max((k for k in kernels if k["kernels_per_launch"] == 1), key=lambda k: k["avg_us"])
         fl, by = costs[dom["step"]]
         ach = fl / (dom["avg_us"] * 1e-6) / 1e12
+        traffic, tnote = None, "no counter table for this workload"
+        if cfg.name == "gpt8b" and args.shard == 0:
+            from tensor_transformer_layer_02_amd.profiling import read_traffic, source_hash
+            tab, h = read_traffic(TRAFFIC_FILE)
+            if h is None:
+                tnote = "counter table missing"
+            elif h != source_hash():
+                tnote = "kernel sources changed since the counters were taken"
+            elif dom["step"] in tab:
+                traffic = int(round(sum(tab[dom["step"]])))
+                tnote = (f"FETCH_SIZE+WRITE_SIZE bytes per launch (copy-calibrated), "
+                         f"{os.path.relpath(TRAFFIC_FILE, ROOT)}; algorithmic minimum {by} bytes")
         roof = {"bound": "mfma", "kernel": dom["step"], "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "flops_per_launch": fl, "avg_us": dom["avg_us"]}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_note": tnote, "flops_per_launch": fl, "avg_us": dom["avg_us"]}
 
     cpu = None
     if not args.no_cpu_baseline:

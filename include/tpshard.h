@@ -204,11 +204,15 @@ enum {
  * step's launches modulo npairs.  `events` is a host array of
  * 2*TP_NUM_STEPS*npairs hipEvent_t handles created by the caller and must stay
  * valid until the hook is disabled (events == NULL or npairs == 0).
- * tp_profile_count(s) returns how many launches of step s were recorded.
+ * tp_profile_count(s) returns how many launches of step s were recorded, and
+ * tp_profile_kernels(s) how many GPU kernels those launches issued in total
+ * (a step is one kernel when the two are equal).  Both reset when the hook is
+ * enabled or disabled; -1 for a step out of range.
  * For measurement only: the hook is process-wide and not thread-safe.
  */
 int tp_profile_enable(void* const* events, int npairs);
 int tp_profile_count(int step);
+int tp_profile_kernels(int step);
 
 /*
  * Verification-only local sum that stands in for the all-reduce on one GPU

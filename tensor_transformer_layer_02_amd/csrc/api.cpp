@@ -120,13 +120,16 @@ struct Prof {
     void* const* events = nullptr;
     int npairs = 0;
     int count[TP_NUM_STEPS] = {};
+    int kernels[TP_NUM_STEPS] = {};
 };
 Prof g_prof;
+long long g_launches = 0;  // every kernel launch of the library (tp::count_launch)
 
 struct StepTimer {
     int step;
     hipStream_t st;
     hipEvent_t stop = nullptr;
+    long long launches0 = 0;
     StepTimer(int s, hipStream_t stream) : step(s), st(stream) {
         if (!g_prof.events || g_prof.npairs <= 0) return;
         const int k = g_prof.count[s] % g_prof.npairs;
@@ -134,9 +137,12 @@ struct StepTimer {
         hipEventRecord(static_cast<hipEvent_t>(g_prof.events[base]), st);
         stop = static_cast<hipEvent_t>(g_prof.events[base + 1]);
         g_prof.count[s]++;
+        launches0 = g_launches;
     }
     ~StepTimer() {
-        if (stop) hipEventRecord(stop, st);
+        if (!stop) return;
+        hipEventRecord(stop, st);
+        g_prof.kernels[step] += (int)(g_launches - launches0);
     }
 };
 
@@ -155,6 +161,10 @@ inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, i
 }
 
 }  // namespace
+
+namespace tp {
+void count_launch() { ++g_launches; }
+}  // namespace tp
 
 extern "C" {
 
@@ -187,11 +197,13 @@ int tp_profile_enable(void* const* events, int npairs) {
         g_prof.events = nullptr;
         g_prof.npairs = 0;
     }
-    for (int i = 0; i < TP_NUM_STEPS; ++i) g_prof.count[i] = 0;
+    for (int i = 0; i < TP_NUM_STEPS; ++i) g_prof.count[i] = g_prof.kernels[i] = 0;
     return TP_OK;
 }
 
 int tp_profile_count(int step) { return (step >= 0 && step < TP_NUM_STEPS) ? g_prof.count[step] : -1; }
+
+int tp_profile_kernels(int step) { return (step >= 0 && step < TP_NUM_STEPS) ? g_prof.kernels[step] : -1; }
 
 size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree) {
     Shape s;

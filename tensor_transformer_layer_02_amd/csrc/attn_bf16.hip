@@ -563,6 +563,7 @@ template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
     hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(NT), 0, s, a);
+    count_launch();
     return hipGetLastError();
 }
 
@@ -570,9 +571,12 @@ template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
     const int64_t T = (int64_t)a.batch * a.seq;
     hipLaunchKernelGGL(attn_rowdot_kernel<D>, dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
+    count_launch();
     dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(NT), 0, s, a);
+    count_launch();
     hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT), 0, s, a);
+    count_launch();
     return hipGetLastError();
 }
 

@@ -328,6 +328,7 @@ template <int DMAX>
 hipError_t fwd_f32(const AttnArgsF& a, hipStream_t s) {
     dim3 grid((a.seq + RB - 1) / RB, a.batch * a.heads);
     hipLaunchKernelGGL(attn_fwd_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    count_launch();
     return hipGetLastError();
 }
 
@@ -335,9 +336,12 @@ template <int DMAX>
 hipError_t bwd_f32(const AttnArgsF& a, hipStream_t s) {
     const int64_t n = (int64_t)a.batch * a.seq * a.heads;
     hipLaunchKernelGGL(attn_rowdot_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    count_launch();
     dim3 grid((a.seq + RB - 1) / RB, a.batch * a.heads);
     hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    count_launch();
     hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    count_launch();
     return hipGetLastError();
 }
 
@@ -367,6 +371,7 @@ hipError_t gemm_f32(const GemmDesc& d, hipStream_t s) {
         case EPI_GELU_BWD: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU_BWD>, grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
+    count_launch();
     return hipGetLastError();
 }
 

@@ -11,21 +11,22 @@
 //  * 32x32x16 MFMAs: with one wave per SIMD they sustain ~86% of the bf16 peak,
 //    the 16x16x32 form only ~55% (measured on MI355X), and a 256 x 256 tile
 //    needs one wave per SIMD for its 256 accumulator registers.
-//  * A 256-thread workgroup (4 wave64s, 2x2) computes a BM x BN tile; K advances
-//    in steps of 32 through a ring of four LDS stages, three of them in flight
-//    while one is consumed (one barrier per step).  The loads in flight per CU
-//    must cover the global-memory latency at the MFMA rate: 96 KB for a
-//    256 x 256 tile.
+//  * A 256-thread workgroup (4 wave64s, 2x2) computes a BM x BN tile.  K
+//    advances in steps of 64 (full 128-byte lines of a K-contiguous row) through
+//    two LDS slots, one barrier per step; the pipeline is described at
+//    GemmCore.  Operands travel global -> registers -> LDS: buffer loads are
+//    issued one or two steps before their data is stored, and every LDS read,
+//    LDS write and global load is paired with an MFMA by scheduling hints, in
+//    a branch-free steady state.
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
 //    over the 8 XCDs) owns a compact block of tiles that share A rows and B
 //    columns in its L2.
-//  * Operands go global -> LDS with buffer_load_dwordx4 ... lds: no VGPR
-//    staging, and the buffer range check returns zeros for rows/columns past
-//    the matrix edge and for the K tail (a lane whose source is out of range is
-//    given an out-of-range offset).
-//  * An operand that is contiguous along K is stored [rows][32] (64 B rows);
+//  * The buffer range check returns zeros for rows/columns past the matrix
+//    edge and for the K tail (a lane whose source is out of range is given an
+//    out-of-range offset), so edge tiles need no special path.
+//  * An operand that is contiguous along K is stored [rows][64] (128 B rows);
 //    one that is contiguous along M or N (the transposed operands of the
-//    weight gradients, and the weights of x*W) is stored [32][cols] as it
+//    weight gradients, and the weights of x*W) is stored [64][cols] as it
 //    lies in memory.  Both layouts XOR-swizzle their 16-byte chunks by row so
 //    that the MFMA fragment reads hit distinct LDS banks; the swizzle is
 //    applied by choosing which global chunk each lane fetches.
@@ -36,6 +37,10 @@
 //  * The epilogue stages each half of the fp32 tile through LDS so that every
 //    thread owns 8 consecutive columns of a row: bias, GeLU, GeLU' (reading U)
 //    and the stores all move 16 bytes per lane.
+//  * Two independent problems of one layout (the two weight gradients of a
+//    sublayer) share a launch; fp32 outputs may split K in two, both halves
+//    adding into a zeroed block (0 + a + b == 0 + b + a exactly, so the result
+//    is deterministic).
 #include "tp_common.h"
 #include "tp_kernels.h"
 
@@ -611,6 +616,7 @@ hipError_t launch(GemmBatch b, hipStream_t s) {
     if (b.n > 1) b.tiles += ((b.g[1].N + BN - 1) / BN) * ((b.g[1].M + BM - 1) / BM);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, BKSEG, EPI, OUTF32>), dim3(b.tiles * b.ksplit), dim3(NT),
                        0, s, b);
+    count_launch();
     return hipGetLastError();
 }
 

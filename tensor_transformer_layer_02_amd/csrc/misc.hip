@@ -115,10 +115,12 @@ hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t 
     else
         hipLaunchKernelGGL(colsum_partial_kernel<float>, g1, dim3(256), 0, s, static_cast<const float*>(X), rows,
                            cols, ld, work);
+    count_launch();
     Out3 o;
     for (int i = 0; i < 3; ++i) o.p[i] = out[i] ? out[i] : out[0];
     hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(work), cols, o, seg);
+    count_launch();
     return hipGetLastError();
 }
 
@@ -126,6 +128,7 @@ hipError_t zero_f32_2d(float* p, int64_t rows, int64_t cols, int64_t ld, hipStre
     const int64_t n = rows * ((cols + 3) / 4);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(zero_f32_2d_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, cols, ld);
+    count_launch();
     return hipGetLastError();
 }
 
@@ -144,6 +147,7 @@ hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const
         else
             hipLaunchKernelGGL(sum_partials_kernel<float>, grid, dim3(256), 0, s, rows, cols, P, cnt,
                                static_cast<const float*>(bias), k0 > 0 ? 1 : 0, out);
+        count_launch();
         if (nparts == 0) break;
     }
     return hipGetLastError();

@@ -7,6 +7,10 @@
 
 namespace tp {
 
+// Counts every kernel launch the library makes (read by the measurement hook
+// to tell single-launch steps apart).
+void count_launch();
+
 enum Epi : int {
     EPI_STORE = 0,      // C = acc (act dtype, or fp32 when out_f32)
     EPI_BIAS = 1,       // C = acc + bias[n]

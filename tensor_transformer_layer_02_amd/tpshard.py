@@ -22,7 +22,7 @@ STATUS = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_EDIVIDE", 3: "TP_ESHARD", 4: "TP_EA
 EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_bytes", "tp_attn_saved_bytes",
            "tp_mlp_work_bytes", "tp_attn_work_bytes", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
            "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_sum_partials", "tp_profile_enable",
-           "tp_profile_count"]
+           "tp_profile_count", "tp_profile_kernels"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.tp_sum_partials.argtypes = [i32, i64, i64, ctypes.POINTER(vp), i32, vp, fp, vp]
         L.tp_profile_enable.argtypes = [ctypes.POINTER(vp), i32]
         L.tp_profile_count.argtypes = [i32]
+        L.tp_profile_kernels.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -197,3 +198,7 @@ def tp_profile_enable(events, npairs) -> int:
 
 def tp_profile_count(step: int) -> int:
     return lib().tp_profile_count(int(step))
+
+
+def tp_profile_kernels(step: int) -> int:
+    return lib().tp_profile_kernels(int(step))
