@@ -486,8 +486,14 @@ struct GemmCore {
     }
 };
 
+// Workgroups per CU a tile shape is built for (registers: 512 / occupancy per lane).
+template <int BM, int BN>
+constexpr int tile_occupancy() {
+    return BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
+}
+
 template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
-__global__ void __launch_bounds__(NT, 1) gemm_bf16_kernel(const GemmBatch batch) {
+__global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kernel(const GemmBatch batch) {
     using Core = GemmCore<BM, BN, AK, BKC, BKSEG>;
     constexpr int RING = STAGES * Core::STAGE;
     constexpr int EROWS = BM / 2, ELD = BN + 8;          // epilogue staging: half a tile of fp32
@@ -677,12 +683,13 @@ GemmArgs make_args(const GemmDesc& d) {
 
 struct Cand {
     int bm, bn, occ;  // occ: workgroups resident per CU
-    double eff;       // relative efficiency of the shape
+    double eff;       // throughput of the shape relative to 256 x 256 (measured on MI355X)
     bool f32_tn_only;
 };
-const Cand kCands[] = {{256, 256, 1, 1.0, false}, {256, 192, 1, 0.97, false}, {192, 192, 1, 0.93, true},
-                       {256, 128, 1, 0.9, false},  {128, 128, 2, 0.8, false},  {64, 192, 2, 0.6, false},
-                       {64, 64, 4, 0.4, false}};
+const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
+                       {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
+                       {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}};
+constexpr double K_OVERHEAD = 384.0;  // prologue + epilogue of a tile, in units of K
 
 hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_t s) {
     switch (c) {
@@ -692,16 +699,18 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
         case 3: return dispatch<256, 128>(d, b, s);
         case 4: return dispatch<128, 128>(d, b, s);
         case 5: return dispatch<64, 192>(d, b, s);
-        default: return dispatch<64, 64>(d, b, s);
+        case 6: return dispatch<64, 64>(d, b, s);
+        default: return dispatch<128, 192>(d, b, s);
     }
 }
 
 }  // namespace
 
-// Tile shape (and K split) with the least estimated time on 256 CUs:
-// waves of workgroups x work per CU per wave / efficiency of the shape.  Every
-// N-segment must hold whole tiles; the 192 x 192 tile and the K split serve
-// only the fp32 weight-gradient GEMMs (split outputs must be zeroed first).
+// Tile shape (and K split) with the least estimated time on 256 CUs.  A CU
+// gets ceil(items / 256) tiles and runs o = min(occupancy, that) of them at
+// once; each costs BM * BN * (K per split + K_OVERHEAD / o) / efficiency.
+// Every N-segment must hold whole tiles; the 192 x 192 tile and the K split
+// serve only the fp32 weight-gradient GEMMs (split outputs are zeroed first).
 hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s) {
     if (n < 1 || n > 2) return hipErrorInvalidValue;
     GemmBatch b;
@@ -713,6 +722,8 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     const bool tn32 = !d[0].a_kcontig && !d[0].b_kcontig && !d[0].b_kseg && d[0].out_f32;
     int best = -1, best_split = 1;
     double best_cost = 1e300;
+    int kmax = 0;
+    for (int i = 0; i < n; ++i) kmax = d[i].K > kmax ? d[i].K : kmax;
     for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
@@ -726,28 +737,35 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
         }
         if (!ok) continue;
         for (int split = 1; split <= ((allow_split && tn32) ? 2 : 1); ++split) {
-            const int64_t items = t * split;
-            const int64_t slots = 256 * k.occ;
-            const double waves = (double)((items + slots - 1) / slots);
-            // per-wave time scales with the K range each workgroup covers
-            const double cost = waves * k.bm * k.bn * k.occ / k.eff / split * (split > 1 ? 1.04 : 1.0);
+            const int64_t tpc = (t * split + 255) / 256;  // tiles per CU
+            const int64_t o = tpc < k.occ ? tpc : k.occ;
+            const double kper = (double)((kmax + split - 1) / split);
+            const double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + K_OVERHEAD / o) / k.eff *
+                                (split > 1 ? 1.04 : 1.0);
             if (cost < best_cost) { best_cost = cost; best = c; best_split = split; }
         }
     }
     if (best < 0) return hipErrorInvalidValue;
     b.ksplit = best_split;
     if (ksplit_out) *ksplit_out = best_split;
-    if (best_split > 1) {  // the K halves add into zeroed output blocks
+    if (best_split > 1) {  // the K halves add into zeroed output blocks (one launch for all of them)
+        const float* zp[ZMAX];
+        int64_t zr[ZMAX], zc[ZMAX], zl[ZMAX];
+        int nz = 0;
         for (int i = 0; i < n; ++i) {
             const GemmDesc& g = d[i];
             if (g.M <= 0 || g.N <= 0 || g.K <= 0) continue;
             const int seg = g.cseg < (1 << 30) ? g.cseg : g.N;
             for (int z = 0; z * seg < g.N && z < 3; ++z) {
-                const int cols = g.N - z * seg < seg ? g.N - z * seg : seg;
-                hipError_t e = zero_f32_2d(static_cast<float*>(g.C[z] ? g.C[z] : g.C[0]), g.M, cols, g.ldc, s);
-                if (e != hipSuccess) return e;
+                zp[nz] = static_cast<const float*>(g.C[z] ? g.C[z] : g.C[0]);
+                zr[nz] = g.M;
+                zc[nz] = g.N - z * seg < seg ? g.N - z * seg : seg;
+                zl[nz] = g.ldc;
+                ++nz;
             }
         }
+        hipError_t e = zero_f32_2d(zp, zr, zc, zl, nz, s);
+        if (e != hipSuccess) return e;
     }
     return dispatch_idx(best, d[0], b, s);
 }

@@ -71,17 +71,21 @@ __global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restri
     out.p[sg][c - (int64_t)sg * seg] = acc;
 }
 
-__global__ void __launch_bounds__(256) zero_f32_2d_kernel(float* __restrict__ p, int64_t rows, int64_t cols,
-                                                          int64_t ld) {
-    const int64_t c4 = (cols + 3) / 4;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= rows * c4) return;
-    const int64_t r = i / c4, c = (i % c4) * 4;
-    float* q = p + r * ld + c;
-    if (c + 4 <= cols && ((reinterpret_cast<uintptr_t>(q) & 15) == 0)) {
-        *reinterpret_cast<f32x4*>(q) = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-        for (int64_t k = c; k < cols && k < c + 4; ++k) p[r * ld + k] = 0.f;
+// Zero up to ZMAX row-major fp32 blocks in one launch; thread item i covers 4
+// floats of one row (f32x4 store when aligned).
+__global__ void __launch_bounds__(256) zero_f32_2d_kernel(const ZeroRegions z) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < z.total; i += (int64_t)gridDim.x * 256) {
+        int k = 0;
+        while (k + 1 < z.n && i >= z.start[k + 1]) ++k;
+        const int64_t j = i - z.start[k];
+        const int64_t c4 = (z.cols[k] + 3) / 4;
+        const int64_t r = j / c4, c = (j % c4) * 4;
+        float* q = z.p[k] + r * z.ld[k] + c;
+        if (c + 4 <= z.cols[k] && ((reinterpret_cast<uintptr_t>(q) & 15) == 0)) {
+            *reinterpret_cast<f32x4*>(q) = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            for (int64_t e = c; e < z.cols[k] && e < c + 4; ++e) z.p[k][r * z.ld[k] + e] = 0.f;
+        }
     }
 }
 
@@ -124,10 +128,24 @@ hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t 
     return hipGetLastError();
 }
 
-hipError_t zero_f32_2d(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
-    const int64_t n = rows * ((cols + 3) / 4);
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_f32_2d_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, cols, ld);
+hipError_t zero_f32_2d(const float* const* p, const int64_t* rows, const int64_t* cols, const int64_t* ld, int n,
+                       hipStream_t s) {
+    if (n < 0 || n > ZMAX) return hipErrorInvalidValue;
+    ZeroRegions z;
+    z.n = 0;
+    z.total = 0;
+    for (int k = 0; k < n; ++k) {
+        if (rows[k] <= 0 || cols[k] <= 0) continue;
+        z.p[z.n] = const_cast<float*>(p[k]);
+        z.cols[z.n] = cols[k];
+        z.ld[z.n] = ld[k];
+        z.start[z.n] = z.total;
+        z.total += rows[k] * ((cols[k] + 3) / 4);
+        ++z.n;
+    }
+    if (z.total == 0) return hipSuccess;
+    const int64_t blocks = (z.total + 255) / 256;
+    hipLaunchKernelGGL(zero_f32_2d_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, z);
     count_launch();
     return hipGetLastError();
 }

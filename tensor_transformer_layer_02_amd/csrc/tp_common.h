@@ -28,16 +28,34 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// GeLU(u) = u * Phi(u) with Phi(u) = (1 + erf(u / sqrt 2)) / 2 (exact form).
-__device__ __forceinline__ float gelu_f(float u) {
-    return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+// Standard normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2 and density
+// phi(u) = exp(-u^2/2) / sqrt(2 pi), sharing one exponential: erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26,
+// erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0,
+// absolute error <= 1.5e-7 (so |Phi error| <= 7.5e-8), on the hardware
+// exp2 and reciprocal units.
+__device__ __forceinline__ float normal_cdf_pdf(float u, float& pdf) {
+    const float z = fabsf(u) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * u * u);  // exp(-u^2/2) = 2^(-u^2 log2(e)/2)
+    const float poly =
+        t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
+    const float tail = 0.5f * poly * e;  // Phi(-|u|)
+    pdf = 0.39894228040143268f * e;
+    return u >= 0.f ? 1.0f - tail : tail;
 }
 
-// d/du GeLU(u) = Phi(u) + u * phi(u), phi(u) = exp(-u^2/2) / sqrt(2 pi).
+// GeLU(u) = u * Phi(u) (the erf form, not the tanh approximation).
+__device__ __forceinline__ float gelu_f(float u) {
+    float pdf;
+    return u * normal_cdf_pdf(u, pdf);
+}
+
+// d/du GeLU(u) = Phi(u) + u * phi(u).
 __device__ __forceinline__ float gelu_prime_f(float u) {
-    const float Phi = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-    const float phi = 0.39894228040143268f * __expf(-0.5f * u * u);
-    return Phi + u * phi;
+    float pdf;
+    const float Phi = normal_cdf_pdf(u, pdf);
+    return fmaf(u, pdf, Phi);
 }
 
 // Bit-level reinterpretations between 16-byte vector types.

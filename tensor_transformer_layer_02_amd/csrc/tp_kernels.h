@@ -55,7 +55,17 @@ hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s);
 hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s);
 
 // Zero a [rows, cols] fp32 block with row stride ld (a kernel, so it can be captured).
-hipError_t zero_f32_2d(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+// Zero n (<= ZMAX) row-major fp32 blocks (p[k]: rows[k] x cols[k], row stride
+// ld[k]) in one launch.
+constexpr int ZMAX = 6;
+struct ZeroRegions {
+    float* p[ZMAX];
+    int64_t cols[ZMAX], ld[ZMAX], start[ZMAX];
+    int64_t total;
+    int n;
+};
+hipError_t zero_f32_2d(const float* const* p, const int64_t* rows, const int64_t* cols, const int64_t* ld, int n,
+                       hipStream_t s);
 // fp32 operands and outputs, fp32 FMA arithmetic.
 hipError_t gemm_f32(const GemmDesc& d, hipStream_t s);
 
