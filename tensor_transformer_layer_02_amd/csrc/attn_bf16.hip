@@ -45,7 +45,8 @@ namespace tp {
 
 namespace {
 
-constexpr int NT = 256;   // 4 waves
+constexpr int NT = 256;   // 4 waves (dK/dV pass, row sums)
+constexpr int NT8 = 512;  // 8 waves (forward, dQ pass): 4 row groups x 2 halves of the streamed blocks
 constexpr int BQ = 128;   // queries per workgroup (forward, dQ) / keys per workgroup (dK, dV)
 constexpr int BKV = 64;   // rows per streamed LDS block
 constexpr float LOG2E = 1.4426950408889634f;
@@ -93,29 +94,34 @@ __device__ __forceinline__ int toff(int r, int col) {
     return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + (col & 7) * 2;
 }
 
-// A 64-row block of a row-major bf16 matrix on its way global -> registers
-// -> LDS (rows >= nvalid are zeros).  Thread t moves chunks t + 256 i.
-template <int D>
-struct BlockLoader {
-    static constexpr int CH = D / 8;            // chunks per row
-    static constexpr int NI = BKV * CH / NT;    // chunks per thread
-    static_assert((BKV * CH) % NT == 0, "block must split evenly");
+// ROWS rows of a row-major bf16 matrix on their way global -> registers ->
+// LDS (rows >= nvalid are zeros), moved by THREADS threads: thread t moves
+// chunks t + THREADS i.
+template <int D, int ROWS, int THREADS>
+struct RowLoader {
+    static constexpr int CH = D / 8;                 // chunks per row
+    static constexpr int NI = ROWS * CH / THREADS;   // chunks per thread
+    static_assert((ROWS * CH) % THREADS == 0, "rows must split evenly");
     u32x4 v[NI];
     __device__ __forceinline__ void load(const bf16_t* __restrict__ src, int64_t ld, int row0, int nvalid, int tid) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int u = tid + NT * i, r = u / CH, c = u % CH;
+            const int u = tid + THREADS * i, r = u / CH, c = u % CH;
             v[i] = (row0 + r < nvalid) ? ld16(src + (int64_t)(row0 + r) * ld + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
     }
     __device__ __forceinline__ void store(char* tile, int tid) const {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int u = tid + NT * i, r = u / CH, c = u % CH;
+            const int u = tid + THREADS * i, r = u / CH, c = u % CH;
             *reinterpret_cast<u32x4*>(tile + toff<D>(r, c * 8)) = v[i];
         }
     }
 };
+template <int D>
+using BlockLoader = RowLoader<D, BKV, NT>;  // one 64-row block, 4 waves
+template <int D>
+using PairLoader = RowLoader<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
 
 // Operand fragment of rows rb .. rb+31 of a tile, k = d chunk c (16 wide):
 // lane l gets row rb + l%32, d = 16c + 8*(l/32) .. +7.
@@ -124,19 +130,19 @@ __device__ __forceinline__ u32x4 frag_rows(const char* tile, int rb, int c, int 
     return *reinterpret_cast<const u32x4*>(tile + toff<D>(rb + (lane & 31), 16 * c + 8 * (lane >> 5)));
 }
 
-// Operand fragment with rows = d (32db .. +31) and k = tile rows 16kc .. +15
-// in the relabelled order: slot s of lane l is tile row
-// 16kc + 8*(s/4) + 4*(l/32) + s%4.  Two transposed reads; in each 16-lane
-// group lane j addresses tile row base + j/4, d 4*(j%4) .. +3 of the group's
-// 16 columns, and lane i receives column i, 4 consecutive rows.
+// Operand fragment with rows = d (32db .. +31) and k = tile rows
+// rb + 16kc .. +15 in the relabelled order: slot s of lane l is tile row
+// rb + 16kc + 8*(s/4) + 4*(l/32) + s%4.  Two transposed reads; in each
+// 16-lane group lane j addresses tile row base + j/4, d 4*(j%4) .. +3 of the
+// group's 16 columns, and lane i receives column i, 4 consecutive rows.
 template <int D>
-__device__ __forceinline__ u32x4 frag_tr(const char* tile, int db, int kc, int lane) {
+__device__ __forceinline__ u32x4 frag_tr(const char* tile, int rb, int db, int kc, int lane) {
     const int G = lane >> 4, j = lane & 15;
     const int col = 32 * db + 16 * (G & 1) + 4 * (j & 3);
     u32x4 out;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int r = 16 * kc + 8 * h + 4 * (G >> 1) + (j >> 2);
+        const int r = rb + 16 * kc + 8 * h + 4 * (G >> 1) + (j >> 2);
         const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16*)(tile + toff<D>(r, col)));
         const u32x2 w = __builtin_bit_cast(u32x2, t);
@@ -179,17 +185,24 @@ __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x1
         }
 }
 
+// Forward.  Waves w and w+4 own the same 32 queries (row group w % 4) and
+// take alternate 64-key blocks of each streamed pair; their online-softmax
+// states (m, l, O^T) merge through LDS at the end.
 template <int D>
-__global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // 2 slots x (K, V)
+__global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
+    constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;  // one [128][D] pair tile
+    constexpr int SLOT = 2 * PT;                                   // K pair, V pair
+    constexpr int NMERGE = DB * 16 + 2;                            // m, l, O^T per lane
+    constexpr int SMEM = 2 * SLOT > NMERGE * 4 * 64 * 4 ? 2 * SLOT : NMERGE * 4 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qg = wave & 3, kp = wave >> 2;
     const int s = a.seq;
     const int nqb = (s + BQ - 1) / BQ;
     const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest rows first
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ, qw0 = q0 + 32 * wave;
+    const int q0 = qb * BQ, qw0 = q0 + 32 * qg;
     const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -208,29 +221,31 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(const AttnArgs a) {
 
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
-    BlockLoader<D> lk, lv;
+    const int npair = (nkb + 1) / 2;
+    PairLoader<D> lk, lv;
     lk.load(Kg, a.ld_qkv, 0, s, tid);
     lv.load(Vg, a.ld_qkv, 0, s, tid);
     lk.store(smem, tid);
-    lv.store(smem + TILE, tid);
+    lv.store(smem + PT, tid);
     __syncthreads();
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int k0 = kb * BKV;
-        const bool more = kb + 1 < nkb;
+    for (int it = 0; it < npair; ++it) {
+        const bool more = it + 1 < npair;
         if (more) {
-            lk.load(Kg, a.ld_qkv, k0 + BKV, s, tid);
-            lv.load(Vg, a.ld_qkv, k0 + BKV, s, tid);
+            lk.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
+            lv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
         }
-        const char* Kt = smem + (kb & 1) * 2 * TILE;
-        const char* Vt = Kt + TILE;
-        if (!(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
+        const char* Kt = smem + (it & 1) * SLOT;
+        const char* Vt = Kt + PT;
+        const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
+        if (kb < nkb && !(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
             f32x16 sacc[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 sacc[h] = zero16();
 #pragma unroll
-                for (int c = 0; c < KC; ++c) sacc[h] = mfma32x32x16(frag_rows<D>(Kt, 32 * h, c, lane), qf[c], sacc[h]);
+                for (int c = 0; c < KC; ++c)
+                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, rb + 32 * h, c, lane), qf[c], sacc[h]);
             }
             // Masks only where the block reaches past the diagonal or the
             // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
@@ -274,21 +289,45 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(const AttnArgs a) {
             for (int kc = 0; kc < 4; ++kc) {
                 const u32x4 pf = pack_chunk(sacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(frag_tr<D>(Vt, db, kc, lane), pf, oacc[db]);
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = mfma32x32x16(frag_tr<D>(Vt, rb, db, kc, lane), pf, oacc[db]);
             }
         }
-        if (more) {  // slot (kb+1)&1 was last read in iteration kb-1, before its closing barrier
-            char* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+        if (more) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
+            char* nxt = smem + ((it + 1) & 1) * SLOT;
             lk.store(nxt, tid);
-            lv.store(nxt + TILE, tid);
+            lv.store(nxt + PT, tid);
         }
         __syncthreads();
     }
 
+    // merge the two halves: element e of row group qg, lane l at [(e*4 + qg)*64 + l]
     lsum += __shfl_xor(lsum, 32);
-    if (qw < s) {
-        store_rowT<D>(a.O + ((int64_t)b * s + qw) * a.ld_o + g * D, oacc, 1.f / lsum, lane);
-        if (lane < 32) a.lse[((int64_t)b * a.heads + g) * s + qw] = (mrow + log2f(lsum)) * LN2;
+    float* mg = reinterpret_cast<float*>(smem);
+    if (kp == 1) {
+        mg[(0 * 4 + qg) * 64 + lane] = mrow;
+        mg[(1 * 4 + qg) * 64 + lane] = lsum;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mg[((2 + 16 * db + r) * 4 + qg) * 64 + lane] = oacc[db][r];
+    }
+    __syncthreads();
+    if (kp == 0) {
+        const float m1 = mg[(0 * 4 + qg) * 64 + lane], l1 = mg[(1 * 4 + qg) * 64 + lane];
+        const float mm = fmaxf(mrow, m1);
+        const float msub = (mm == -INFINITY) ? 0.f : mm;
+        const float a0 = ex2(mrow - msub), a1 = ex2(m1 - msub);
+        const float l = lsum * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                oacc[db][r] = oacc[db][r] * a0 + mg[((2 + 16 * db + r) * 4 + qg) * 64 + lane] * a1;
+        if (qw < s) {
+            store_rowT<D>(a.O + ((int64_t)b * s + qw) * a.ld_o + g * D, oacc, 1.f / l, lane);
+            if (lane < 32) a.lse[((int64_t)b * a.heads + g) * s + qw] = (mm + log2f(l)) * LN2;
+        }
     }
 }
 
@@ -428,8 +467,8 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
                 const int kc = 2 * h + half;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dv[db] = mfma32x32x16(pf, frag_tr<D>(dOt, db, kc, lane), dv[db]);
-                    dk[db] = mfma32x32x16(sf, frag_tr<D>(Qt, db, kc, lane), dk[db]);
+                    dv[db] = mfma32x32x16(pf, frag_tr<D>(dOt, 0, db, kc, lane), dv[db]);
+                    dk[db] = mfma32x32x16(sf, frag_tr<D>(Qt, 0, db, kc, lane), dk[db]);
                 }
             }
         }
@@ -453,18 +492,23 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
     }
 }
 
-// dQ for 128 queries (32 per wave); key blocks of 64 stream through LDS.
+// dQ for 128 queries.  Waves w and w+4 own the same 32 queries and take
+// alternate 64-key blocks of each streamed pair; their dQ^T sums add through
+// LDS at the end (in a fixed order: deterministic).
 template <int D>
-__global__ void __launch_bounds__(NT, D <= 96 ? 2 : 1) attn_bwd_dq_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // 2 slots x (K, V)
+__global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
+    constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
+    constexpr int SLOT = 2 * PT;  // K pair, V pair
+    constexpr int SMEM = 2 * SLOT > DB * 16 * 4 * 64 * 4 ? 2 * SLOT : DB * 16 * 4 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qg = wave & 3, kp = wave >> 2;
     const int s = a.seq;
     const int nqb = (s + BQ - 1) / BQ;
     const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ, qw0 = q0 + 32 * wave;
+    const int q0 = qb * BQ, qw0 = q0 + 32 * qg;
     const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -489,31 +533,32 @@ __global__ void __launch_bounds__(NT, D <= 96 ? 2 : 1) attn_bwd_dq_kernel(const 
 
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
-    BlockLoader<D> lk, lv;
+    const int npair = (nkb + 1) / 2;
+    PairLoader<D> lk, lv;
     lk.load(Kg, a.ld_qkv, 0, s, tid);
     lv.load(Vg, a.ld_qkv, 0, s, tid);
     lk.store(smem, tid);
-    lv.store(smem + TILE, tid);
+    lv.store(smem + PT, tid);
     __syncthreads();
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int k0 = kb * BKV;
-        const bool more = kb + 1 < nkb;
+    for (int it = 0; it < npair; ++it) {
+        const bool more = it + 1 < npair;
         if (more) {
-            lk.load(Kg, a.ld_qkv, k0 + BKV, s, tid);
-            lv.load(Vg, a.ld_qkv, k0 + BKV, s, tid);
+            lk.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
+            lv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
         }
-        const char* Kt = smem + (kb & 1) * 2 * TILE;
-        const char* Vt = Kt + TILE;
-        if (!(a.causal && k0 > qw0 + 31)) {
+        const char* Kt = smem + (it & 1) * SLOT;
+        const char* Vt = Kt + PT;
+        const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
+        if (kb < nkb && !(a.causal && k0 > qw0 + 31)) {
             f32x16 sacc[2], pacc[2];  // S^T and dP^T: rows = keys, column = this lane's query
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 sacc[h] = pacc[h] = zero16();
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, 32 * h, c, lane), qf[c], sacc[h]);
-                    pacc[h] = mfma32x32x16(frag_rows<D>(Vt, 32 * h, c, lane), of[c], pacc[h]);
+                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, rb + 32 * h, c, lane), qf[c], sacc[h]);
+                    pacc[h] = mfma32x32x16(frag_rows<D>(Vt, rb + 32 * h, c, lane), of[c], pacc[h]);
                 }
             }
             const bool edge = (a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s || qw0 + 32 > s;
@@ -530,18 +575,32 @@ __global__ void __launch_bounds__(NT, D <= 96 ? 2 : 1) attn_bwd_dq_kernel(const 
             for (int kc = 0; kc < 4; ++kc) {
                 const u32x4 sf = pack_chunk(pacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(frag_tr<D>(Kt, db, kc, lane), sf, dq[db]);
+                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(frag_tr<D>(Kt, rb, db, kc, lane), sf, dq[db]);
             }
         }
         if (more) {
-            char* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+            char* nxt = smem + ((it + 1) & 1) * SLOT;
             lk.store(nxt, tid);
-            lv.store(nxt + TILE, tid);
+            lv.store(nxt + PT, tid);
         }
         __syncthreads();
     }
 
-    if (qw < s) store_rowT<D>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
+    float* mg = reinterpret_cast<float*>(smem);
+    if (kp == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mg[((16 * db + r) * 4 + qg) * 64 + lane] = dq[db][r];
+    }
+    __syncthreads();
+    if (kp == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[db][r] += mg[((16 * db + r) * 4 + qg) * 64 + lane];
+        if (qw < s) store_rowT<D>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
+    }
 }
 
 AttnArgs make_args(const AttnDesc& d) {
@@ -562,7 +621,7 @@ AttnArgs make_args(const AttnDesc& d) {
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(NT8), 0, s, a);
     count_launch();
     return hipGetLastError();
 }
@@ -575,7 +634,7 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(NT), 0, s, a);
     count_launch();
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT8), 0, s, a);
     count_launch();
     return hipGetLastError();
 }

@@ -689,7 +689,8 @@ struct Cand {
 const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
                        {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
                        {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}};
-constexpr double K_OVERHEAD = 384.0;  // prologue + epilogue of a tile, in units of K
+constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
+constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
 
 hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_t s) {
     switch (c) {
@@ -708,7 +709,9 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
 
 // Tile shape (and K split) with the least estimated time on 256 CUs.  A CU
 // gets ceil(items / 256) tiles and runs o = min(occupancy, that) of them at
-// once; each costs BM * BN * (K per split + K_OVERHEAD / o) / efficiency.
+// once; each costs BM * BN * (K per split + overhead / o) / efficiency, the
+// overhead (prologue and epilogue, larger with GeLU math) being hidden by the
+// other resident tiles.
 // Every N-segment must hold whole tiles; the 192 x 192 tile and the K split
 // serve only the fp32 weight-gradient GEMMs (split outputs are zeroed first).
 hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s) {
@@ -724,6 +727,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     double best_cost = 1e300;
     int kmax = 0;
     for (int i = 0; i < n; ++i) kmax = d[i].K > kmax ? d[i].K : kmax;
+    const double kov = (d[0].epi == EPI_BIAS_GELU || d[0].epi == EPI_GELU_BWD) ? K_OVERHEAD_GELU : K_OVERHEAD;
     for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
@@ -740,7 +744,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
             const int64_t tpc = (t * split + 255) / 256;  // tiles per CU
             const int64_t o = tpc < k.occ ? tpc : k.occ;
             const double kper = (double)((kmax + split - 1) / split);
-            const double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + K_OVERHEAD / o) / k.eff *
+            const double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + kov / o) / k.eff *
                                 (split > 1 ? 1.04 : 1.0);
             if (cost < best_cost) { best_cost = cost; best = c; best_split = split; }
         }
