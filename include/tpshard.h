@@ -43,11 +43,18 @@
  *   - Ownership: the caller allocates every buffer (device memory),
  *     including `saved` (written by fwd, read by bwd; size from
  *     tp_*_saved_bytes) and `work` (scratch of the backward; size from
- *     tp_*_work_bytes).  The library allocates no device memory; its only
- *     mutable global state is the measurement hook (tp_profile_enable).
+ *     tp_*_work_bytes).  The library allocates no device memory; its
+ *     mutable global state is the measurement hook (tp_profile_enable) and,
+ *     per device, one auxiliary stream with two events (below).
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
  *     legacy default stream) and the call returns without synchronising.
- *     Execution faults surface at the caller's next synchronisation.
+ *     Execution faults surface at the caller's next synchronisation.  The
+ *     backward entry points run independent launches (a weight gradient, a
+ *     bias column sum) on the device's auxiliary stream (created on first
+ *     use, default priority), forked from and joined back to `stream` with
+ *     events, so everything a call enqueues precedes later work on `stream`;
+ *     host threads that call them concurrently are serialised while they
+ *     enqueue.
  *   - Errors: every argument is validated on the host BEFORE any HIP call
  *     or enqueue; on failure nothing is written and a tp_status is
  *     returned.  A failed launch returns TP_EHIP.  No C++ exception
@@ -191,10 +198,11 @@ enum {
     TP_STEP_MLP_DX = 8,      /* dX_part = dU A_i^T                                          */
     TP_STEP_ATTN_DO = 9,     /* dO = dZ Wo_i^T                                              */
     TP_STEP_ATTN_CORE_BWD = 10, /* softmax attention backward -> dQ, dK, dV                 */
-    TP_STEP_ATTN_DW = 11,    /* dW{q,k,v}_i = X^T d{Q,K,V} and dWo_i = O^T dZ (one launch)  */
+    TP_STEP_ATTN_DW = 11,    /* dW{q,k,v}_i = X^T d{Q,K,V}                                  */
     TP_STEP_ATTN_DBIAS = 12, /* db{q,k,v}_i = column sums                                   */
     TP_STEP_ATTN_DX = 13,    /* dX_part = d{Q,K,V} W{q,k,v}_i^T                             */
-    TP_NUM_STEPS = 14
+    TP_STEP_ATTN_DWO = 14,   /* dWo_i = O^T dZ                                              */
+    TP_NUM_STEPS = 15
 };
 
 /*

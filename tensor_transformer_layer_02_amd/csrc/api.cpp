@@ -8,9 +8,11 @@
 //                      [X^T dU -> dA_i]  [colsum dU -> db1_i]  [dU*A_i^T -> dX_part]
 //   tp_attn_shard_fwd: [X*[Wq|Wk|Wv]_i + b -> QKV]  [fused attention -> O, LSE]
 //                      [O*Wo_i -> Z_part]
-//   tp_attn_shard_bwd: [dZ*Wo_i^T -> dO]  [O^T dZ -> dWo_i]  [fused attention bwd -> dQKV]
-//                      [X^T dQKV -> dW{q,k,v}_i]  [colsum -> db{q,k,v}_i]
-//                      [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]
+//   tp_attn_shard_bwd: [dZ*Wo_i^T -> dO]  [fused attention bwd -> dQKV]
+//                      [X^T dQKV -> dW{q,k,v}_i]  [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]
+//                      and, on the auxiliary stream: [O^T dZ -> dWo_i] (from the
+//                      start), [colsum -> db{q,k,v}_i] (after the attention bwd)
+// The MLP backward's column sum also runs on the auxiliary stream.
 // The shard slices follow page "Megatron-LM: what the tensor parallelism paper
 // actually says": FFN columns/rows C_i ("How transformer layers actually
 // decompose"), head columns/rows G_i ("The attention heads split").
@@ -20,6 +22,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "tp_kernels.h"
@@ -151,6 +154,69 @@ inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, in
     return s.bf16 ? tp::gemm_bf16(g, st) : tp::gemm_f32(g, st);
 }
 
+// A weight-gradient GEMM (fp32 output; the bf16 path may split K in two).
+inline hipError_t gemm_w(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
+    StepTimer t(step, st);
+    return s.bf16 ? tp::gemm_bf16_batch(&g, 1, true, nullptr, st) : tp::gemm_f32(g, st);
+}
+
+// Per-device auxiliary stream for launches that are independent of the main
+// chain of a backward call: to_aux(k) makes it wait for everything enqueued on
+// the caller's stream so far, to_main(k) makes the caller's stream wait for
+// everything enqueued on it (k: one of the call's events, each used once per
+// call).  The lock is held from the first to the last of these in one call,
+// so the shared events are never re-recorded by another host thread in
+// between.
+constexpr int AUX_EVENTS = 6;
+struct Aux {
+    hipStream_t st = nullptr;
+    hipEvent_t ev[AUX_EVENTS] = {};
+    std::mutex mu;
+};
+constexpr int AUX_DEVICES = 64;
+Aux g_aux[AUX_DEVICES];
+std::mutex g_aux_init;
+
+struct AuxScope {
+    Aux* a = nullptr;
+    std::unique_lock<std::mutex> lock;
+    hipError_t err = hipSuccess;
+    AuxScope() {
+        int dev = 0;
+        if ((err = hipGetDevice(&dev)) != hipSuccess) return;
+        if (dev < 0 || dev >= AUX_DEVICES) { err = hipErrorInvalidDevice; return; }
+        Aux& x = g_aux[dev];
+        {
+            std::lock_guard<std::mutex> g(g_aux_init);
+            if (!x.st) {
+                hipStream_t st = nullptr;
+                hipEvent_t ev[AUX_EVENTS] = {};
+                if ((err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return;
+                for (int k = 0; k < AUX_EVENTS && err == hipSuccess; ++k)
+                    err = hipEventCreateWithFlags(&ev[k], hipEventDisableTiming);
+                if (err != hipSuccess) {
+                    for (int k = 0; k < AUX_EVENTS; ++k)
+                        if (ev[k]) hipEventDestroy(ev[k]);
+                    hipStreamDestroy(st);
+                    return;
+                }
+                for (int k = 0; k < AUX_EVENTS; ++k) x.ev[k] = ev[k];
+                x.st = st;
+            }
+        }
+        lock = std::unique_lock<std::mutex>(x.mu);
+        a = &x;
+    }
+    hipError_t to_aux(hipStream_t main, int k) {
+        hipError_t e = hipEventRecord(a->ev[k], main);
+        return e != hipSuccess ? e : hipStreamWaitEvent(a->st, a->ev[k], 0);
+    }
+    hipError_t to_main(hipStream_t main, int k) {
+        hipError_t e = hipEventRecord(a->ev[k], a->st);
+        return e != hipSuccess ? e : hipStreamWaitEvent(main, a->ev[k], 0);
+    }
+};
+
 // Two independent weight-gradient GEMMs of the same layout in one launch
 // (bf16 path; may split K in two with zeroed outputs), or one after the other.
 inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, int step) {
@@ -279,6 +345,9 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     float* cs = static_cast<float*>(at(work, W.cs, 1));
     const int64_t c0 = s.i * s.Fs;
 
+    AuxScope aux;
+    if (aux.err != hipSuccess) return TP_EHIP;
+
     tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * GeLU'(U)
     g.M = (int)s.T; g.N = (int)s.Fs; g.K = (int)s.h;
     g.A = dZ; g.lda = s.h; g.a_kcontig = true;
@@ -286,6 +355,13 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
     g.epi = tp::EPI_GELU_BWD;
     if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
+
+    if (db1) {  // db1[C_i] = column sums of dU, on the auxiliary stream beside the GEMMs below
+        float* outs[3] = {db1 + c0, nullptr, nullptr};
+        if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
+        StepTimer t(TP_STEP_MLP_DB1, aux.a->st);
+        if (tp::colsum(s.bf16, dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, aux.a->st) != hipSuccess) return TP_EHIP;
+    }
 
     tp::GemmDesc gw[2];  // one launch: dB[C_i, :] = Y^T dZ and dA[:, C_i] = X^T dU
     tp::GemmDesc& gb = gw[0];
@@ -300,18 +376,14 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
     if (gemm2(s, gw, st, TP_STEP_MLP_DW) != hipSuccess) return TP_EHIP;
 
-    if (db1) {  // db1[C_i] = column sums of dU
-        float* outs[3] = {db1 + c0, nullptr, nullptr};
-        StepTimer t(TP_STEP_MLP_DB1, st);
-        if (tp::colsum(s.bf16, dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, st) != hipSuccess) return TP_EHIP;
-    }
-
     tp::GemmDesc gx;  // dX_part = dU A[:, C_i]^T
     gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)s.Fs;
     gx.A = dU; gx.lda = s.Fs; gx.a_kcontig = true;
     gx.B[0] = at(A, c0, s.e); gx.ldb = s.F; gx.b_kcontig = true;
     gx.C[0] = dX_part; gx.ldc = s.h;
-    return hip_status(gemm(s, gx, st, TP_STEP_MLP_DX));
+    if (gemm(s, gx, st, TP_STEP_MLP_DX) != hipSuccess) return TP_EHIP;
+    if (db1 && aux.to_main(st, 1) != hipSuccess) return TP_EHIP;
+    return TP_OK;
 }
 
 int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq, const void* Wk,
@@ -391,6 +463,17 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     float* cs = static_cast<float*>(at(work, W.cs, 1));
     const int64_t col0 = s.i * s.w;
 
+    AuxScope aux;
+    if (aux.err != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc go;  // dWo[rows of G_i, :] = O^T dZ: needs only forward outputs, so it runs on
+    go.M = (int)s.w; go.N = (int)s.h; go.K = (int)s.T;  // the auxiliary stream beside dO and the core
+    go.A = O; go.lda = s.w; go.a_kcontig = false;
+    go.B[0] = dZ; go.ldb = s.h; go.b_kcontig = false;
+    go.C[0] = dWo + col0 * s.h; go.ldc = s.h; go.out_f32 = true;
+    if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
+    if (gemm_w(s, go, aux.a->st, TP_STEP_ATTN_DWO) != hipSuccess) return TP_EHIP;
+
     tp::GemmDesc g;  // dO = dZ Wo[rows of G_i, :]^T
     g.M = (int)s.T; g.N = (int)s.w; g.K = (int)s.h;
     g.A = dZ; g.lda = s.h; g.a_kcontig = true;
@@ -403,31 +486,33 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
     ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = const_cast<void*>(O); ad.ld_o = s.w;
     ad.lse = const_cast<float*>(lse); ad.dO = dO; ad.Dq = Dq; ad.dqkv = dQKV;
-    {
+    auto core = [&](int part, hipStream_t q) {
+        return s.bf16 ? tp::attn_bwd_bf16(ad, part, q) : tp::attn_bwd_f32(ad, part, q);
+    };
+    {   // D = rowsum(dO * O), the dK/dV pass, the dQ pass (running the last two
+        // concurrently measured slower: their workgroups compete for the same CUs)
         StepTimer t(TP_STEP_ATTN_CORE_BWD, st);
-        if ((s.bf16 ? tp::attn_bwd_bf16(ad, st) : tp::attn_bwd_f32(ad, st)) != hipSuccess) return TP_EHIP;
+        if (core(tp::ATTN_BWD_ROWDOT, st) != hipSuccess || core(tp::ATTN_BWD_DKDV, st) != hipSuccess ||
+            core(tp::ATTN_BWD_DQ, st) != hipSuccess)
+            return TP_EHIP;
     }
 
-    tp::GemmDesc gw[2];  // one launch: dW{q,k,v}[:, cols of G_i] = X^T dQKV and dWo[rows of G_i, :] = O^T dZ
-    tp::GemmDesc& gq = gw[0];
+    if (bias_grads) {  // db{q,k,v}[cols of G_i] = column sums of dQKV, on the auxiliary stream
+        float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
+        if (aux.to_aux(st, 1) != hipSuccess) return TP_EHIP;
+        StepTimer t(TP_STEP_ATTN_DBIAS, aux.a->st);
+        if (tp::colsum(s.bf16, dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, aux.a->st) != hipSuccess)
+            return TP_EHIP;
+    }
+
+    tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV
     gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
     gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
     gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
     float* dW3[3] = {dWq, dWk, dWv};
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
-    tp::GemmDesc& go = gw[1];
-    go.M = (int)s.w; go.N = (int)s.h; go.K = (int)s.T;
-    go.A = O; go.lda = s.w; go.a_kcontig = false;
-    go.B[0] = dZ; go.ldb = s.h; go.b_kcontig = false;
-    go.C[0] = dWo + col0 * s.h; go.ldc = s.h; go.out_f32 = true;
-    if (gemm2(s, gw, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
-
-    if (bias_grads) {  // db{q,k,v}[cols of G_i] = column sums of dQKV
-        float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
-        StepTimer t(TP_STEP_ATTN_DBIAS, st);
-        if (tp::colsum(s.bf16, dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, st) != hipSuccess) return TP_EHIP;
-    }
+    if (gemm_w(s, gq, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
 
     tp::GemmDesc gx;  // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T
     gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)(3 * s.w);
@@ -436,7 +521,8 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
     gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
     gx.C[0] = dX_part; gx.ldc = s.h;
-    return hip_status(gemm(s, gx, st, TP_STEP_ATTN_DX));
+    if (gemm(s, gx, st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
+    return aux.to_main(st, 2) != hipSuccess ? TP_EHIP : TP_OK;
 }
 
 int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts, const void* bias,

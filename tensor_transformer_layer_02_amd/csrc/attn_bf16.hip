@@ -94,63 +94,100 @@ __device__ __forceinline__ int toff(int r, int col) {
     return r * (D * 2) + ((((col >> 3) ^ swz<D>(r))) << 4) + (col & 7) * 2;
 }
 
-// ROWS rows of a row-major bf16 matrix on their way global -> registers ->
-// LDS (rows >= nvalid are zeros), moved by THREADS threads: thread t moves
-// chunks t + THREADS i.
+constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any range: the load returns zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Thread geometry of moving ROWS rows x D columns (16-byte chunks t + THREADS i
+// for thread t) from a row-major bf16 matrix with row stride ld into a
+// swizzled LDS tile; computed once per kernel, shared by every matrix of the
+// same shape.
 template <int D, int ROWS, int THREADS>
-struct RowLoader {
+struct RowGeom {
     static constexpr int CH = D / 8;                 // chunks per row
     static constexpr int NI = ROWS * CH / THREADS;   // chunks per thread
     static_assert((ROWS * CH) % THREADS == 0, "rows must split evenly");
-    u32x4 v[NI];
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ src, int64_t ld, int row0, int nvalid, int tid) {
+    uint32_t off[NI];  // byte offset of the chunk from the block's first row
+    int row[NI];       // its row within the block
+    int dst[NI];       // its byte offset in the LDS tile
+    __device__ __forceinline__ void init(int64_t ld, int tid) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int u = tid + THREADS * i, r = u / CH, c = u % CH;
-            v[i] = (row0 + r < nvalid) ? ld16(src + (int64_t)(row0 + r) * ld + c * 8) : u32x4{0u, 0u, 0u, 0u};
+            row[i] = r;
+            off[i] = (uint32_t)(r * ld * 2 + c * 16);
+            dst[i] = toff<D>(r, c * 8);
         }
     }
-    __device__ __forceinline__ void store(char* tile, int tid) const {
+    // Buffer loads of rows row0 .. row0+ROWS-1 (rows >= nvalid read as zeros):
+    // the buffer base moves to row0, so no lane branches.
+    __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int nvalid,
+                                         u32x4 (&v)[NI]) const {
+        const int rem = nvalid - row0;
+        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * ld * 2 + D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)(rem > 0 ? row0 : 0) * ld, bytes);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int u = tid + THREADS * i, r = u / CH, c = u % CH;
-            *reinterpret_cast<u32x4*>(tile + toff<D>(r, c * 8)) = v[i];
+            const uint32_t o = row[i] < rem ? off[i] : OOB;
+            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
         }
+    }
+    __device__ __forceinline__ void store(char* tile, const u32x4 (&v)[NI]) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(tile + dst[i]) = v[i];
     }
 };
 template <int D>
-using BlockLoader = RowLoader<D, BKV, NT>;  // one 64-row block, 4 waves
+using BlockGeom = RowGeom<D, BKV, NT>;  // one 64-row block, 4 waves
 template <int D>
-using PairLoader = RowLoader<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
+using PairGeom = RowGeom<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
 
-// Operand fragment of rows rb .. rb+31 of a tile, k = d chunk c (16 wide):
-// lane l gets row rb + l%32, d = 16c + 8*(l/32) .. +7.
+// Per-lane LDS byte offsets of the fragment reads of a [rows][D] tile.  The
+// chunk swizzle depends only on the row modulo 16, so a row base that is a
+// multiple of 16 (and the tile base) is a uniform addend.
+//   rows[c]:  row l%32, d = 16c + 8*(l/32) .. +7 (16-byte read);
+//   tr[h][db]: transposed read h of d block db: in each 16-lane group, lane j
+//              addresses row 8h + 4*(G/2) + j/4 and d 32db + 16*(G%2) + 4*(j%4)
+//              (G = l/16), and lane i receives column i, 4 consecutive rows.
 template <int D>
-__device__ __forceinline__ u32x4 frag_rows(const char* tile, int rb, int c, int lane) {
-    return *reinterpret_cast<const u32x4*>(tile + toff<D>(rb + (lane & 31), 16 * c + 8 * (lane >> 5)));
-}
-
-// Operand fragment with rows = d (32db .. +31) and k = tile rows
-// rb + 16kc .. +15 in the relabelled order: slot s of lane l is tile row
-// rb + 16kc + 8*(s/4) + 4*(l/32) + s%4.  Two transposed reads; in each
-// 16-lane group lane j addresses tile row base + j/4, d 4*(j%4) .. +3 of the
-// group's 16 columns, and lane i receives column i, 4 consecutive rows.
-template <int D>
-__device__ __forceinline__ u32x4 frag_tr(const char* tile, int rb, int db, int kc, int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int col = 32 * db + 16 * (G & 1) + 4 * (j & 3);
-    u32x4 out;
+struct FragAddr {
+    static constexpr int ROWB = D * 2, KC = D / 16, DB = D / 32;
+    int rows[KC];
+    int tr[2][DB];
+    __device__ __forceinline__ void init(int lane) {
+        const int lr = lane & 31, l5 = lane >> 5, G = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = rb + 16 * kc + 8 * h + 4 * (G >> 1) + (j >> 2);
-        const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(tile + toff<D>(r, col)));
-        const u32x2 w = __builtin_bit_cast(u32x2, t);
-        out[2 * h] = w[0];
-        out[2 * h + 1] = w[1];
+        for (int c = 0; c < KC; ++c) rows[c] = toff<D>(lr, 16 * c + 8 * l5);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                tr[h][db] = toff<D>(8 * h + 4 * (G >> 1) + (j >> 2), 32 * db + 16 * (G & 1) + 4 * (j & 3));
     }
-    return out;
-}
+    // Operand fragment of rows rb .. rb+31 (rb % 16 == 0), k = d chunk c:
+    // lane l gets row rb + l%32, d = 16c + 8*(l/32) .. +7.
+    __device__ __forceinline__ u32x4 frag_rows(const char* tile, int rb, int c) const {
+        return *reinterpret_cast<const u32x4*>(tile + rb * ROWB + rows[c]);
+    }
+    // Operand fragment with rows = d (32db .. +31) and k = tile rows
+    // rb + 16kc .. +15 (rb % 16 == 0) in the relabelled order: slot s of lane
+    // l is tile row rb + 16kc + 8*(s/4) + 4*(l/32) + s%4.
+    __device__ __forceinline__ u32x4 frag_tr(const char* tile, int rb, int db, int kc) const {
+        const char* base = tile + (rb + 16 * kc) * ROWB;
+        u32x4 out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(base + tr[h][db]));
+            const u32x2 w = __builtin_bit_cast(u32x2, t);
+            out[2 * h] = w[0];
+            out[2 * h + 1] = w[1];
+        }
+        return out;
+    }
+};
 
 // bf16 operand fragment (k16 chunk kc of a 64-row block) from the fp32
 // result registers of its 32-row half: slots s = values r = 8*(kc%2) + s.
@@ -187,13 +224,17 @@ __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x1
 
 // Forward.  Waves w and w+4 own the same 32 queries (row group w % 4) and
 // take alternate 64-key blocks of each streamed pair; their online-softmax
-// states (m, l, O^T) merge through LDS at the end.
+// states (m, l, O^T) merge through LDS at the end.  The running max is a
+// reference that moves only when some row's block max exceeds it by more
+// than 2^8 (in the exponent's base 2): the softmax is the same for any
+// reference, P stays <= 256, and O is rescaled rarely.
 template <int D>
 __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;  // one [128][D] pair tile
     constexpr int SLOT = 2 * PT;                                   // K pair, V pair
     constexpr int NMERGE = DB * 16 + 2;                            // m, l, O^T per lane
     constexpr int SMEM = 2 * SLOT > NMERGE * 4 * 64 * 4 ? 2 * SLOT : NMERGE * 4 * 64 * 4;
+    constexpr float LAZY = 8.f;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -214,26 +255,31 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     for (int c = 0; c < KC; ++c)
         qf[c] = (qw < s) ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
 
+    FragAddr<D> fa;
+    fa.init(lane);
+    PairGeom<D> geo;
+    geo.init(a.ld_qkv, tid);
+    u32x4 kv[PairGeom<D>::NI], vv[PairGeom<D>::NI];
+
     f32x16 oacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) oacc[i] = zero16();
-    float mrow = -INFINITY, lsum = 0.f;
+    float mref = -INFINITY, lsum = 0.f;
 
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
     const int npair = (nkb + 1) / 2;
-    PairLoader<D> lk, lv;
-    lk.load(Kg, a.ld_qkv, 0, s, tid);
-    lv.load(Vg, a.ld_qkv, 0, s, tid);
-    lk.store(smem, tid);
-    lv.store(smem + PT, tid);
+    geo.load(Kg, a.ld_qkv, 0, s, kv);
+    geo.load(Vg, a.ld_qkv, 0, s, vv);
+    geo.store(smem, kv);
+    geo.store(smem + PT, vv);
     __syncthreads();
 
     for (int it = 0; it < npair; ++it) {
         const bool more = it + 1 < npair;
         if (more) {
-            lk.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
-            lv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
+            geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
+            geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
         }
         const char* Kt = smem + (it & 1) * SLOT;
         const char* Vt = Kt + PT;
@@ -244,8 +290,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
             for (int h = 0; h < 2; ++h) {
                 sacc[h] = zero16();
 #pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, rb + 32 * h, c, lane), qf[c], sacc[h]);
+                for (int c = 0; c < KC; ++c) sacc[h] = mfma32x32x16(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
             }
             // Masks only where the block reaches past the diagonal or the
             // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
@@ -264,39 +309,37 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[h][r]);
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-            const float mnew = fmaxf(mrow, bmax * a.scale_log2);
-            const float msub = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = ex2(mrow - msub);
-            float psum = 0.f;
+            bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * a.scale_log2;
+            if (any_lane(bmax > mref + LAZY)) {  // move the reference (to the block max where it grew)
+                const float mnew = fmaxf(mref, bmax);
+                const float alpha = ex2(mref - ((mnew == -INFINITY) ? 0.f : mnew));
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+                mref = mnew;
+            }
+            const float msub = (mref == -INFINITY) ? 0.f : mref;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -msub));
                     sacc[h][r] = pv;
-                    psum += pv;
+                    lsum += pv;
                 }
-            lsum = lsum * alpha + psum;
-            mrow = mnew;
-            if (any_lane(alpha != 1.f)) {
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-            }
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
                 const u32x4 pf = pack_chunk(sacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    oacc[db] = mfma32x32x16(frag_tr<D>(Vt, rb, db, kc, lane), pf, oacc[db]);
+                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(fa.frag_tr(Vt, rb, db, kc), pf, oacc[db]);
             }
         }
         if (more) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
             char* nxt = smem + ((it + 1) & 1) * SLOT;
-            lk.store(nxt, tid);
-            lv.store(nxt + PT, tid);
+            geo.store(nxt, kv);
+            geo.store(nxt + PT, vv);
         }
         __syncthreads();
     }
@@ -305,7 +348,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     lsum += __shfl_xor(lsum, 32);
     float* mg = reinterpret_cast<float*>(smem);
     if (kp == 1) {
-        mg[(0 * 4 + qg) * 64 + lane] = mrow;
+        mg[(0 * 4 + qg) * 64 + lane] = mref;
         mg[(1 * 4 + qg) * 64 + lane] = lsum;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -315,9 +358,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     __syncthreads();
     if (kp == 0) {
         const float m1 = mg[(0 * 4 + qg) * 64 + lane], l1 = mg[(1 * 4 + qg) * 64 + lane];
-        const float mm = fmaxf(mrow, m1);
+        const float mm = fmaxf(mref, m1);
         const float msub = (mm == -INFINITY) ? 0.f : mm;
-        const float a0 = ex2(mrow - msub), a1 = ex2(m1 - msub);
+        const float a0 = ex2(mref - msub), a1 = ex2(m1 - msub);
         const float l = lsum * a0 + l1 * a1;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -355,47 +398,18 @@ __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
     a.Dq[((int64_t)b * a.heads + g) * a.seq + j] = acc;
 }
 
-// One 64-query block for the dK/dV pass: Q and dO rows plus, for threads
-// < 64, one query's log2-scaled log-sum-exp and D.  (A struct, not lambdas:
-// closure types in a kernel template defeat the host-side stub emission of
-// later instantiations with this compiler.)
-template <int D>
-struct QBlock {
-    static constexpr int TILE = BKV * D * 2;
-    static constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, log2-scaled LSE, D
-    BlockLoader<D> lq, lo;
-    float lsev = 0.f, dval = 0.f;
-    __device__ __forceinline__ void fetch(const AttnArgs& a, const bf16_t* Qg, const bf16_t* dOg, const float* lseg,
-                                          const float* Dg, int q0, int tid) {
-        lq.load(Qg, a.ld_qkv, q0, a.seq, tid);
-        lo.load(dOg, a.ld_o, q0, a.seq, tid);
-        if (tid < BKV) {
-            const int q = q0 + tid;
-            lsev = q < a.seq ? lseg[q] * LOG2E : 0.f;
-            dval = q < a.seq ? Dg[q] : 0.f;
-        }
-    }
-    __device__ __forceinline__ void put(char* slot, int tid) const {
-        lq.store(slot, tid);
-        lo.store(slot + TILE, tid);
-        if (tid < BKV) {
-            reinterpret_cast<float*>(slot + 2 * TILE)[tid] = lsev;
-            reinterpret_cast<float*>(slot + 2 * TILE + BKV * 4)[tid] = dval;
-        }
-    }
-};
-
-// dK, dV for 128 keys (32 per wave); query blocks of 64 stream through LDS.
+// dK, dV for 128 keys (32 per wave); query blocks of 64 (Q and dO rows plus
+// their log2-scaled LSE and D) stream through LDS.
 template <int D>
 __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, TILE = QBlock<D>::TILE, SLOT = QBlock<D>::SLOT;
+    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, LSE, D
     __shared__ __attribute__((aligned(16))) char smem[2 * SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const int kblk = (int)blockIdx.x;  // causal: low keys see the most queries and go first
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int k0 = kblk * BQ, kw0 = k0 + 32 * wave;
+    const int k0 = (int)blockIdx.x * BQ, kw0 = k0 + 32 * wave;  // causal: low keys see the most queries and go first
     const int kw = kw0 + (lane & 31);  // this lane's key
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -417,19 +431,45 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
 
+    FragAddr<D> fa;
+    fa.init(lane);
+    BlockGeom<D> gq, go;  // Q rows (stride ld_qkv) and dO rows (stride ld_o)
+    gq.init(a.ld_qkv, tid);
+    go.init(a.ld_o, tid);
+    u32x4 qv[BlockGeom<D>::NI], ov[BlockGeom<D>::NI];
+    float lsev = 0.f, dval = 0.f;  // threads < 64: one query's log2-scaled LSE and D
+
     const int nqb = (s + BKV - 1) / BKV;
     const int qb0 = a.causal ? (k0 / BKV) : 0;
-    QBlock<D> nb;
     if (qb0 < nqb) {
-        nb.fetch(a, Qg, dOg, lseg, Dg, qb0 * BKV, tid);
-        nb.put(smem, tid);
+        const int q0 = qb0 * BKV;
+        gq.load(Qg, a.ld_qkv, q0, s, qv);
+        go.load(dOg, a.ld_o, q0, s, ov);
+        if (tid < BKV) {
+            lsev = q0 + tid < s ? lseg[q0 + tid] * LOG2E : 0.f;
+            dval = q0 + tid < s ? Dg[q0 + tid] : 0.f;
+        }
+        gq.store(smem, qv);
+        go.store(smem + TILE, ov);
+        if (tid < BKV) {
+            reinterpret_cast<float*>(smem + 2 * TILE)[tid] = lsev;
+            reinterpret_cast<float*>(smem + 2 * TILE + BKV * 4)[tid] = dval;
+        }
     }
     __syncthreads();
 
     for (int qb = qb0; qb < nqb; ++qb) {
         const int q0 = qb * BKV;
         const bool more = qb + 1 < nqb;
-        if (more) nb.fetch(a, Qg, dOg, lseg, Dg, q0 + BKV, tid);
+        if (more) {
+            const int q1 = q0 + BKV;
+            gq.load(Qg, a.ld_qkv, q1, s, qv);
+            go.load(dOg, a.ld_o, q1, s, ov);
+            if (tid < BKV) {
+                lsev = q1 + tid < s ? lseg[q1 + tid] * LOG2E : 0.f;
+                dval = q1 + tid < s ? Dg[q1 + tid] : 0.f;
+            }
+        }
         const char* slot = smem + ((qb - qb0) & 1) * SLOT;
         const char* Qt = slot;
         const char* dOt = slot + TILE;
@@ -442,8 +482,8 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
             f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
-                sacc = mfma32x32x16(frag_rows<D>(Qt, 32 * h, c, lane), kf[c], sacc);
-                pacc = mfma32x32x16(frag_rows<D>(dOt, 32 * h, c, lane), vf[c], pacc);
+                sacc = mfma32x32x16(fa.frag_rows(Qt, 32 * h, c), kf[c], sacc);
+                pacc = mfma32x32x16(fa.frag_rows(dOt, 32 * h, c), vf[c], pacc);
             }
             // rows = queries qh0 + res_row(r), column = this lane's key
             const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
@@ -467,12 +507,20 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
                 const int kc = 2 * h + half;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dv[db] = mfma32x32x16(pf, frag_tr<D>(dOt, 0, db, kc, lane), dv[db]);
-                    dk[db] = mfma32x32x16(sf, frag_tr<D>(Qt, 0, db, kc, lane), dk[db]);
+                    dv[db] = mfma32x32x16(pf, fa.frag_tr(dOt, 0, db, kc), dv[db]);
+                    dk[db] = mfma32x32x16(sf, fa.frag_tr(Qt, 0, db, kc), dk[db]);
                 }
             }
         }
-        if (more) nb.put(smem + ((qb + 1 - qb0) & 1) * SLOT, tid);
+        if (more) {  // slot of block qb+1 was last read in iteration qb-1, before its closing barrier
+            char* nxt = smem + ((qb + 1 - qb0) & 1) * SLOT;
+            gq.store(nxt, qv);
+            go.store(nxt + TILE, ov);
+            if (tid < BKV) {
+                reinterpret_cast<float*>(nxt + 2 * TILE)[tid] = lsev;
+                reinterpret_cast<float*>(nxt + 2 * TILE + BKV * 4)[tid] = dval;
+            }
+        }
         __syncthreads();
     }
 
@@ -527,6 +575,12 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     const float lse2 = qw < s ? a.lse[hrow + qw] * LOG2E : 0.f;
     const float Dv = qw < s ? a.Dq[hrow + qw] : 0.f;
 
+    FragAddr<D> fa;
+    fa.init(lane);
+    PairGeom<D> geo;
+    geo.init(a.ld_qkv, tid);
+    u32x4 kv[PairGeom<D>::NI], vv[PairGeom<D>::NI];
+
     f32x16 dq[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) dq[i] = zero16();
@@ -534,18 +588,17 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     const int nkb_all = (s + BKV - 1) / BKV;
     const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
     const int npair = (nkb + 1) / 2;
-    PairLoader<D> lk, lv;
-    lk.load(Kg, a.ld_qkv, 0, s, tid);
-    lv.load(Vg, a.ld_qkv, 0, s, tid);
-    lk.store(smem, tid);
-    lv.store(smem + PT, tid);
+    geo.load(Kg, a.ld_qkv, 0, s, kv);
+    geo.load(Vg, a.ld_qkv, 0, s, vv);
+    geo.store(smem, kv);
+    geo.store(smem + PT, vv);
     __syncthreads();
 
     for (int it = 0; it < npair; ++it) {
         const bool more = it + 1 < npair;
         if (more) {
-            lk.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
-            lv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, tid);
+            geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
+            geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
         }
         const char* Kt = smem + (it & 1) * SLOT;
         const char* Vt = Kt + PT;
@@ -557,8 +610,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
                 sacc[h] = pacc[h] = zero16();
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    sacc[h] = mfma32x32x16(frag_rows<D>(Kt, rb + 32 * h, c, lane), qf[c], sacc[h]);
-                    pacc[h] = mfma32x32x16(frag_rows<D>(Vt, rb + 32 * h, c, lane), of[c], pacc[h]);
+                    sacc[h] = mfma32x32x16(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+                    pacc[h] = mfma32x32x16(fa.frag_rows(Vt, rb + 32 * h, c), of[c], pacc[h]);
                 }
             }
             const bool edge = (a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s || qw0 + 32 > s;
@@ -575,13 +628,13 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
             for (int kc = 0; kc < 4; ++kc) {
                 const u32x4 sf = pack_chunk(pacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(frag_tr<D>(Kt, rb, db, kc, lane), sf, dq[db]);
+                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(fa.frag_tr(Kt, rb, db, kc), sf, dq[db]);
             }
         }
         if (more) {
             char* nxt = smem + ((it + 1) & 1) * SLOT;
-            lk.store(nxt, tid);
-            lv.store(nxt + PT, tid);
+            geo.store(nxt, kv);
+            geo.store(nxt + PT, vv);
         }
         __syncthreads();
     }
@@ -627,14 +680,17 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
+hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
     const int64_t T = (int64_t)a.batch * a.seq;
-    hipLaunchKernelGGL(attn_rowdot_kernel<D>, dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
-    count_launch();
     dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(NT), 0, s, a);
-    count_launch();
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT8), 0, s, a);
+    if (part == ATTN_BWD_ROWDOT)
+        hipLaunchKernelGGL(attn_rowdot_kernel<D>, dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
+    else if (part == ATTN_BWD_DKDV)
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(NT), 0, s, a);
+    else if (part == ATTN_BWD_DQ)
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT8), 0, s, a);
+    else
+        return hipErrorInvalidValue;
     count_launch();
     return hipGetLastError();
 }
@@ -652,13 +708,13 @@ hipError_t attn_fwd_bf16(const AttnDesc& d, hipStream_t s) {
     }
 }
 
-hipError_t attn_bwd_bf16(const AttnDesc& d, hipStream_t s) {
+hipError_t attn_bwd_bf16(const AttnDesc& d, int part, hipStream_t s) {
     const AttnArgs a = make_args(d);
     switch (d.dh) {
-        case 32: return bwd_d<32>(a, s);
-        case 64: return bwd_d<64>(a, s);
-        case 96: return bwd_d<96>(a, s);
-        case 128: return bwd_d<128>(a, s);
+        case 32: return bwd_d<32>(a, part, s);
+        case 64: return bwd_d<64>(a, part, s);
+        case 96: return bwd_d<96>(a, part, s);
+        case 128: return bwd_d<128>(a, part, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -333,14 +333,17 @@ hipError_t fwd_f32(const AttnArgsF& a, hipStream_t s) {
 }
 
 template <int DMAX>
-hipError_t bwd_f32(const AttnArgsF& a, hipStream_t s) {
+hipError_t bwd_f32(const AttnArgsF& a, int part, hipStream_t s) {
     const int64_t n = (int64_t)a.batch * a.seq * a.heads;
-    hipLaunchKernelGGL(attn_rowdot_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-    count_launch();
     dim3 grid((a.seq + RB - 1) / RB, a.batch * a.heads);
-    hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
-    count_launch();
-    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    if (part == ATTN_BWD_ROWDOT)
+        hipLaunchKernelGGL(attn_rowdot_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    else if (part == ATTN_BWD_DKDV)
+        hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    else if (part == ATTN_BWD_DQ)
+        hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<DMAX>, grid, dim3(RB), 0, s, a);
+    else
+        return hipErrorInvalidValue;
     count_launch();
     return hipGetLastError();
 }
@@ -383,11 +386,11 @@ hipError_t attn_fwd_f32(const AttnDesc& d, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t attn_bwd_f32(const AttnDesc& d, hipStream_t s) {
+hipError_t attn_bwd_f32(const AttnDesc& d, int part, hipStream_t s) {
     const AttnArgsF a = make_args(d);
-    if (d.dh <= 32) return bwd_f32<32>(a, s);
-    if (d.dh <= 64) return bwd_f32<64>(a, s);
-    if (d.dh <= 128) return bwd_f32<128>(a, s);
+    if (d.dh <= 32) return bwd_f32<32>(a, part, s);
+    if (d.dh <= 64) return bwd_f32<64>(a, part, s);
+    if (d.dh <= 128) return bwd_f32<128>(a, part, s);
     return hipErrorInvalidValue;
 }
 

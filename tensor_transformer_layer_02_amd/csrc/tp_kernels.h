@@ -84,10 +84,13 @@ struct AttnDesc {
     void* dqkv = nullptr;               // [T, 3w]
 };
 
+// The backward is three launches: D = rowsum(dO * O) first, then the dK/dV
+// and dQ passes, which are independent of each other (both read D).
+enum AttnBwdPart { ATTN_BWD_ROWDOT = 0, ATTN_BWD_DKDV = 1, ATTN_BWD_DQ = 2 };
 hipError_t attn_fwd_bf16(const AttnDesc& a, hipStream_t s);
-hipError_t attn_bwd_bf16(const AttnDesc& a, hipStream_t s);
+hipError_t attn_bwd_bf16(const AttnDesc& a, int part, hipStream_t s);
 hipError_t attn_fwd_f32(const AttnDesc& a, hipStream_t s);
-hipError_t attn_bwd_f32(const AttnDesc& a, hipStream_t s);
+hipError_t attn_bwd_f32(const AttnDesc& a, int part, hipStream_t s);
 
 // out[c] = sum_r X[r*ld + c] over rows, fp32, into up to 3 column segments of length seg.
 // Deterministic two-pass reduction; `work` holds colsum_work_floats(cols) floats.

@@ -29,14 +29,15 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-# (step, kernel-name patterns in dispatch order); "zero*" is any number of
-# zero-fill launches (outputs of a K-split GEMM).
+# (step, kernel-name patterns in the order the steps are enqueued, either
+# stream); "zero*" is any number of zero-fill launches (outputs of a K-split
+# GEMM).
 STEP_ORDER = [
     ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gemm"]), ("ATTN_CORE", ["attn_fwd"]),
-    ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DW", ["zero*", "gemm"]),
-    ("MLP_DB1", ["colsum_partial", "colsum_final"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
-    ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]), ("ATTN_DW", ["zero*", "gemm"]),
-    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]),
+    ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
+    ("MLP_DW", ["zero*", "gemm"]), ("MLP_DX", ["gemm"]), ("ATTN_DWO", ["zero*", "gemm"]), ("ATTN_DO", ["gemm"]),
+    ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
+    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DW", ["zero*", "gemm"]), ("ATTN_DX", ["gemm"]),
 ]
 KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "zero": ("zero_f32_2d",),
         "colsum_partial": ("colsum_partial",), "colsum_final": ("colsum_final",), "attn_rowdot": ("attn_rowdot",),
@@ -105,7 +106,10 @@ def split_steps(dispatches):
                     break
             if not ok:
                 break
-            cur[step] = recs
+            if step.endswith("+"):
+                cur[step[:-1]] = cur.get(step[:-1], []) + recs
+            else:
+                cur[step] = recs
         if ok:
             steps.append(cur)
             i = j
@@ -171,6 +175,8 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
         "# step fetch_bytes write_bytes kernels",
     ]
     for step, _ in STEP_ORDER:
+        if step.endswith("+"):
+            continue
         fv = [sum(s[step]) for s in fs if step in s]
         wv = [sum(s[step]) for s in ws if step in s]
         nk = [len(s[step]) for s in fs if step in s]
@@ -203,6 +209,8 @@ def durations(trace_dir, out):
     ]
     tot = 0.0
     for step, _ in STEP_ORDER:
+        if step.endswith("+"):
+            continue
         per = [s[step] for s in steps if step in s]
         if not per:
             continue

@@ -26,7 +26,7 @@ EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_byte
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
-         "ATTN_DO", "ATTN_CORE_BWD", "ATTN_DW", "ATTN_DBIAS", "ATTN_DX"]
+         "ATTN_DO", "ATTN_CORE_BWD", "ATTN_DW", "ATTN_DBIAS", "ATTN_DX", "ATTN_DWO"]
 
 
 class TpError(RuntimeError):
