@@ -95,16 +95,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // consecutive rows at one logical chunk is conflict-free.
 __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
-// Swizzle of a [64][cols] M/N-contiguous tile, by k-row.  One transposed
-// fragment read touches rows 8g + r (+4), g, r in 0..3; the XOR spreads those
-// 16 rows over all banks (rows of a multiple of 256 B) or, with the row
-// parity, over both halves of the banks (rows of an odd multiple of 128 B).
+// Swizzle of a [64][cols] M/N-contiguous tile, by k-row.  A half-wave of a
+// transposed fragment read touches 4 consecutive k-rows x 4 consecutive
+// chunks (64 B per row); the XOR moves the 4 rows to 4 different 4-chunk
+// bank groups (rows of a multiple of 256 B: by k & 3; rows of an odd
+// multiple of 128 B, where consecutive rows already alternate halves: by
+// bit 1 of k), so every half-wave hits each bank once.
 template <int COLS>
 __device__ __forceinline__ int swz_mn(int k) {
     if constexpr ((COLS * 2) % 256 == 0)
-        return 2 * ((k & 3) | (((k >> 3) & 1) << 2));   // 0..14, within 16-chunk groups
+        return (k & 3) << 2;
     else
-        return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));  // 0..6, within 8-chunk groups
+        return ((k >> 1) & 1) << 2;
 }
 
 // One stage of a K-contiguous operand, [ROWS][64]: instruction q fills LDS
