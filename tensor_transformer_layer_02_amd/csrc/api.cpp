@@ -11,7 +11,8 @@
 //   tp_attn_shard_bwd: [dZ*Wo_i^T -> dO]  [fused attention bwd -> dQKV]
 //                      [X^T dQKV -> dW{q,k,v}_i]  [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]
 //                      and, on the auxiliary stream: [O^T dZ -> dWo_i] (from the
-//                      start), [colsum -> db{q,k,v}_i] (after the attention bwd)
+//                      start), [colsum -> db{q,k,v}_i] and the dX_part GEMM (after
+//                      the attention bwd, beside the dW{q,k,v} GEMM)
 // The MLP backward's column sum also runs on the auxiliary stream.
 // The shard slices follow page "Megatron-LM: what the tensor parallelism paper
 // actually says": FFN columns/rows C_i ("How transformer layers actually
@@ -497,13 +498,24 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
             return TP_EHIP;
     }
 
-    if (bias_grads) {  // db{q,k,v}[cols of G_i] = column sums of dQKV, on the auxiliary stream
+    // On the auxiliary stream: db{q,k,v}[cols of G_i] = column sums of dQKV, then
+    // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T, beside the weight-gradient GEMM
+    // (whose tiles leave CUs idle).
+    if (aux.to_aux(st, 1) != hipSuccess) return TP_EHIP;
+    if (bias_grads) {
         float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
-        if (aux.to_aux(st, 1) != hipSuccess) return TP_EHIP;
         StepTimer t(TP_STEP_ATTN_DBIAS, aux.a->st);
         if (tp::colsum(s.bf16, dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, aux.a->st) != hipSuccess)
             return TP_EHIP;
     }
+    tp::GemmDesc gx;
+    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)(3 * s.w);
+    gx.A = dQKV; gx.lda = 3 * s.w; gx.a_kcontig = true;
+    const void* W3[3] = {Wq, Wk, Wv};
+    for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
+    gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
+    gx.C[0] = dX_part; gx.ldc = s.h;
+    if (gemm(s, gx, aux.a->st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
 
     tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV
     gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
@@ -513,15 +525,6 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
     if (gemm_w(s, gq, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
-
-    tp::GemmDesc gx;  // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T
-    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)(3 * s.w);
-    gx.A = dQKV; gx.lda = 3 * s.w; gx.a_kcontig = true;
-    const void* W3[3] = {Wq, Wk, Wv};
-    for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
-    gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
-    gx.C[0] = dX_part; gx.ldc = s.h;
-    if (gemm(s, gx, st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
     return aux.to_main(st, 2) != hipSuccess ? TP_EHIP : TP_OK;
 }
 

@@ -37,7 +37,7 @@ STEP_ORDER = [
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
     ("MLP_DW", ["zero*", "gemm"]), ("MLP_DX", ["gemm"]), ("ATTN_DWO", ["zero*", "gemm"]), ("ATTN_DO", ["gemm"]),
     ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
-    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DW", ["zero*", "gemm"]), ("ATTN_DX", ["gemm"]),
+    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["zero*", "gemm"]),
 ]
 KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "zero": ("zero_f32_2d",),
         "colsum_partial": ("colsum_partial",), "colsum_final": ("colsum_final",), "attn_rowdot": ("attn_rowdot",),
