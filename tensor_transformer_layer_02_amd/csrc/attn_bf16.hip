@@ -10,8 +10,9 @@
 // 8*(l/32) .. +7; the 32x32 result gives lane l column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
 //
-// Forward: a workgroup owns 128 queries of one (sequence, head), a wave 32 of
-// them.  Scores are formed transposed, S^T = K Q^T, so that each lane holds
+// Forward: a workgroup owns two 64-query blocks of one (sequence, head), x
+// and nb-1-x, so that under the causal mask every workgroup has about the
+// same work; a wave takes 32 of the queries.  Scores are formed transposed, S^T = K Q^T, so that each lane holds
 // ONE query and 16 keys of a 32-key block: the online-softmax max and sum are
 // lane-local (plus one exchange between the lane pair l, l^32).  O^T = V^T P^T
 // takes P^T straight from those registers: the k-slots of a k16 chunk are
@@ -23,8 +24,8 @@
 //
 // Backward: P is recomputed from Q, K and the saved log-sum-exp.
 //   D_j = dO_j . O_j            (row sums, equal to sum_m P_jm dP_jm)
-//   dV = P^T dO, dK = dS^T Q / sqrt(d)     a workgroup per 128 keys
-//   dQ = dS K / sqrt(d)                    a workgroup per 128 queries
+//   dV = P^T dO, dK = dS^T Q / sqrt(d)     a workgroup per two 64-key blocks
+//   dQ = dS K / sqrt(d)                    a workgroup per two 64-query blocks
 // with dP = dO V^T and dS = P * (dP - D).  Splitting dQ into its own pass
 // keeps every output written by exactly one workgroup (no atomics; the result
 // is deterministic) at the price of recomputing S and dP once more.  The
@@ -45,9 +46,8 @@ namespace tp {
 
 namespace {
 
-constexpr int NT = 256;   // 4 waves (dK/dV pass, row sums)
-constexpr int NT8 = 512;  // 8 waves (forward, dQ pass): 4 row groups x 2 halves of the streamed blocks
-constexpr int BQ = 128;   // queries per workgroup (forward, dQ) / keys per workgroup (dK, dV)
+constexpr int NT = 256;   // row sums
+constexpr int NT8 = 512;  // 8 waves (forward, dK/dV, dQ): 4 row groups x 2 halves of the streamed rows
 constexpr int BKV = 64;   // rows per streamed LDS block
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
@@ -103,22 +103,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Thread geometry of moving ROWS rows x D columns (16-byte chunks t + THREADS i
 // for thread t) from a row-major bf16 matrix with row stride ld into a
 // swizzled LDS tile; computed once per kernel, shared by every matrix of the
-// same shape.
+// same shape.  When the chunks do not split evenly, the threads past the last
+// chunk of the final round load nothing and store nothing.
 template <int D, int ROWS, int THREADS>
 struct RowGeom {
-    static constexpr int CH = D / 8;                 // chunks per row
-    static constexpr int NI = ROWS * CH / THREADS;   // chunks per thread
-    static_assert((ROWS * CH) % THREADS == 0, "rows must split evenly");
+    static constexpr int CH = D / 8;                           // chunks per row
+    static constexpr int TOTAL = ROWS * CH;
+    static constexpr int NI = (TOTAL + THREADS - 1) / THREADS;  // chunks per thread
+    static constexpr bool EXACT = TOTAL % THREADS == 0;
     uint32_t off[NI];  // byte offset of the chunk from the block's first row
-    int row[NI];       // its row within the block
-    int dst[NI];       // its byte offset in the LDS tile
+    int row[NI];       // its row within the block (1 << 30: no chunk)
+    int dst[NI];       // its byte offset in the LDS tile (-1: no chunk)
     __device__ __forceinline__ void init(int64_t ld, int tid) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int u = tid + THREADS * i, r = u / CH, c = u % CH;
-            row[i] = r;
-            off[i] = (uint32_t)(r * ld * 2 + c * 16);
-            dst[i] = toff<D>(r, c * 8);
+            const bool has = EXACT || u < TOTAL;
+            row[i] = has ? r : (1 << 30);
+            off[i] = has ? (uint32_t)(r * ld * 2 + c * 16) : OOB;
+            dst[i] = has ? toff<D>(r, c * 8) : -1;
         }
     }
     // Buffer loads of rows row0 .. row0+ROWS-1 (rows >= nvalid read as zeros):
@@ -136,11 +139,10 @@ struct RowGeom {
     }
     __device__ __forceinline__ void store(char* tile, const u32x4 (&v)[NI]) const {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(tile + dst[i]) = v[i];
+        for (int i = 0; i < NI; ++i)
+            if (EXACT || i + 1 < NI || dst[i] >= 0) *reinterpret_cast<u32x4*>(tile + dst[i]) = v[i];
     }
 };
-template <int D>
-using BlockGeom = RowGeom<D, BKV, NT>;  // one 64-row block, 4 waves
 template <int D>
 using PairGeom = RowGeom<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
 
@@ -222,8 +224,29 @@ __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x1
         }
 }
 
-// Forward.  Waves w and w+4 own the same 32 queries (row group w % 4) and
-// take alternate 64-key blocks of each streamed pair; their online-softmax
+// Rows of a forward / dQ workgroup: the 64-row blocks x and nb-1-x of the
+// sequence (nb blocks of 64 rows), so that under the causal mask a short and a
+// long row range share every workgroup and all workgroups carry about the same
+// work.  Row groups 0, 1 are the 32-row halves of block x, 2, 3 those of block
+// nb-1-x (empty when the two coincide).  Wave w takes the key blocks of half
+// kp = w / 4 of each streamed pair and row group (w + 2 kp) mod 4, so the two
+// waves that share a SIMD (w and w + 4) hold rows of different blocks.
+struct PairRows {
+    int qg, kp;
+    int qw0;  // first row of the wave's group (the sequence length when the group is empty)
+    int nkb;  // 64-key blocks the workgroup streams
+    __device__ __forceinline__ PairRows(int x, int s, int wave, int causal) {
+        const int nb = (s + BKV - 1) / BKV, xl = nb - 1 - x;
+        kp = wave >> 2;
+        qg = (wave + 2 * kp) & 3;
+        const int blk = qg < 2 ? x : xl;
+        qw0 = (qg < 2 || xl != x) ? min(s, blk * BKV + 32 * (qg & 1)) : s;
+        nkb = causal ? xl + 1 : nb;
+    }
+};
+
+// Forward.  The two waves of a row group (32 queries) take alternate 64-key
+// blocks of each streamed pair; their online-softmax
 // states (m, l, O^T) merge through LDS at the end.  The running max is a
 // reference that moves only when some row's block max exceeds it by more
 // than 2^8 (in the exponent's base 2): the softmax is the same for any
@@ -238,12 +261,10 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qg = wave & 3, kp = wave >> 2;
     const int s = a.seq;
-    const int nqb = (s + BQ - 1) / BQ;
-    const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest rows first
+    const PairRows pr((int)blockIdx.x, s, wave, a.causal);
+    const int qg = pr.qg, kp = pr.kp, qw0 = pr.qw0;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ, qw0 = q0 + 32 * qg;
     const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -266,8 +287,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     for (int i = 0; i < DB; ++i) oacc[i] = zero16();
     float mref = -INFINITY, lsum = 0.f;
 
-    const int nkb_all = (s + BKV - 1) / BKV;
-    const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
+    const int nkb = pr.nkb;
     const int npair = (nkb + 1) / 2;
     geo.load(Kg, a.ld_qkv, 0, s, kv);
     geo.load(Vg, a.ld_qkv, 0, s, vv);
@@ -284,7 +304,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
         const char* Kt = smem + (it & 1) * SLOT;
         const char* Vt = Kt + PT;
         const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
-        if (kb < nkb && !(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
+        if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
             f32x16 sacc[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -398,18 +418,47 @@ __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
     a.Dq[((int64_t)b * a.heads + g) * a.seq + j] = acc;
 }
 
-// dK, dV for 128 keys (32 per wave); query blocks of 64 (Q and dO rows plus
-// their log2-scaled LSE and D) stream through LDS.
+// Sum of the two query halves' partial dK (or dV) of a key group: the half-1
+// wave writes value r of d block db for lane l at [((db*16 + r)*4 + kg)*64 + l]
+// and the half-0 wave adds it.  Every wave of the workgroup calls it.
+template <int DB>
+__device__ __forceinline__ void merge_halves(f32x16 (&acc)[DB], float* mg, int qh, int kg, int lane) {
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mg[((16 * db + r) * 4 + kg) * 64 + lane] = acc[db][r];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][r] += mg[((16 * db + r) * 4 + kg) * 64 + lane];
+    }
+    __syncthreads();
+}
+
+// dK, dV for the 64-key blocks x and nb-1-x (key groups of 32 as the row
+// groups of PairRows, so the two waves sharing a SIMD hold keys of different
+// blocks and every workgroup carries about the same work under the causal
+// mask).  Query blocks of 64 (Q and dO rows plus their log2-scaled LSE and D)
+// stream through LDS; the two waves of a key group take the two 32-query
+// halves of each block, and their dK, dV partial sums add through LDS at the
+// end (in a fixed order: deterministic).
 template <int D>
-__global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
     constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, LSE, D
-    __shared__ __attribute__((aligned(16))) char smem[2 * SLOT];
+    constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for the 4 key groups
+    constexpr int SMEM = 2 * SLOT > MERGE ? 2 * SLOT : MERGE;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
+    const PairRows pr((int)blockIdx.x, s, wave, a.causal);  // rows = keys here
+    const int kg = pr.qg, qh = pr.kp, kw0 = pr.qw0;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int k0 = (int)blockIdx.x * BQ, kw0 = k0 + 32 * wave;  // causal: low keys see the most queries and go first
     const int kw = kw0 + (lane & 31);  // this lane's key
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -433,14 +482,14 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
 
     FragAddr<D> fa;
     fa.init(lane);
-    BlockGeom<D> gq, go;  // Q rows (stride ld_qkv) and dO rows (stride ld_o)
+    RowGeom<D, BKV, NT8> gq, go;  // Q rows (stride ld_qkv) and dO rows (stride ld_o)
     gq.init(a.ld_qkv, tid);
     go.init(a.ld_o, tid);
-    u32x4 qv[BlockGeom<D>::NI], ov[BlockGeom<D>::NI];
+    u32x4 qv[RowGeom<D, BKV, NT8>::NI], ov[RowGeom<D, BKV, NT8>::NI];
     float lsev = 0.f, dval = 0.f;  // threads < 64: one query's log2-scaled LSE and D
 
     const int nqb = (s + BKV - 1) / BKV;
-    const int qb0 = a.causal ? (k0 / BKV) : 0;
+    const int qb0 = a.causal ? (int)blockIdx.x : 0;  // the first query that sees the lowest key
     if (qb0 < nqb) {
         const int q0 = qb0 * BKV;
         gq.load(Qg, a.ld_qkv, q0, s, qv);
@@ -475,21 +524,20 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
         const char* dOt = slot + TILE;
         const float* lse2 = reinterpret_cast<const float*>(slot + 2 * TILE);
         const float* Dl = lse2 + BKV;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {  // 32-query half of the block
-            const int qh0 = q0 + 32 * h;
-            if (a.causal && qh0 + 31 < kw0) continue;  // every query precedes every key of this wave
+        const int qh0 = q0 + 32 * qh;  // this wave's 32 queries
+        // skip when the key group is empty or every query precedes every key
+        if (kw0 < s && !(a.causal && qh0 + 31 < kw0)) {
             f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
-                sacc = mfma32x32x16(fa.frag_rows(Qt, 32 * h, c), kf[c], sacc);
-                pacc = mfma32x32x16(fa.frag_rows(dOt, 32 * h, c), vf[c], pacc);
+                sacc = mfma32x32x16(fa.frag_rows(Qt, 32 * qh, c), kf[c], sacc);
+                pacc = mfma32x32x16(fa.frag_rows(dOt, 32 * qh, c), vf[c], pacc);
             }
             // rows = queries qh0 + res_row(r), column = this lane's key
             const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int ql = 32 * h + 8 * r4 + 4 * (lane >> 5);
+                const int ql = 32 * qh + 8 * r4 + 4 * (lane >> 5);
                 const f32x4 L = *reinterpret_cast<const f32x4*>(lse2 + ql);
                 const f32x4 Dd = *reinterpret_cast<const f32x4*>(Dl + ql);
 #pragma unroll
@@ -504,7 +552,7 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const u32x4 pf = pack_chunk(sacc, half), sf = pack_chunk(pacc, half);
-                const int kc = 2 * h + half;
+                const int kc = 2 * qh + half;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dv[db] = mfma32x32x16(pf, fa.frag_tr(dOt, 0, db, kc), dv[db]);
@@ -524,25 +572,30 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(const AttnArgs a) 
         __syncthreads();
     }
 
+    merge_halves<DB>(dk, reinterpret_cast<float*>(smem), qh, kg, lane);
+    merge_halves<DB>(dv, reinterpret_cast<float*>(smem), qh, kg, lane);
+
     // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
-    bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
-    bf16_t* dVg = dKg + a.w;
+    if (qh == 0 && kw0 < s) {
+        bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
+        bf16_t* dVg = dKg + a.w;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = kw0 + res_row(r, lane);
-        if (key >= s) continue;
+        for (int r = 0; r < 16; ++r) {
+            const int key = kw0 + res_row(r, lane);
+            if (key >= s) continue;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int c = 32 * db + (lane & 31);
-            dKg[(int64_t)key * a.ld_qkv + c] = f2bf(dk[db][r] * a.scale);
-            dVg[(int64_t)key * a.ld_qkv + c] = f2bf(dv[db][r]);
+            for (int db = 0; db < DB; ++db) {
+                const int c = 32 * db + (lane & 31);
+                dKg[(int64_t)key * a.ld_qkv + c] = f2bf(dk[db][r] * a.scale);
+                dVg[(int64_t)key * a.ld_qkv + c] = f2bf(dv[db][r]);
+            }
         }
     }
 }
 
-// dQ for 128 queries.  Waves w and w+4 own the same 32 queries and take
-// alternate 64-key blocks of each streamed pair; their dQ^T sums add through
-// LDS at the end (in a fixed order: deterministic).
+// dQ for two 64-query blocks (rows as in the forward).  The two waves of a
+// row group take alternate 64-key blocks of each streamed pair; their dQ^T
+// sums add through LDS at the end (in a fixed order: deterministic).
 template <int D>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
@@ -551,12 +604,10 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qg = wave & 3, kp = wave >> 2;
     const int s = a.seq;
-    const int nqb = (s + BQ - 1) / BQ;
-    const int qb = a.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    const PairRows pr((int)blockIdx.x, s, wave, a.causal);
+    const int qg = pr.qg, kp = pr.kp, qw0 = pr.qw0;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int q0 = qb * BQ, qw0 = q0 + 32 * qg;
     const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -585,8 +636,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) dq[i] = zero16();
 
-    const int nkb_all = (s + BKV - 1) / BKV;
-    const int nkb = a.causal ? min(nkb_all, (q0 + BQ - 1) / BKV + 1) : nkb_all;
+    const int nkb = pr.nkb;
     const int npair = (nkb + 1) / 2;
     geo.load(Kg, a.ld_qkv, 0, s, kv);
     geo.load(Vg, a.ld_qkv, 0, s, vv);
@@ -603,7 +653,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
         const char* Kt = smem + (it & 1) * SLOT;
         const char* Vt = Kt + PT;
         const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
-        if (kb < nkb && !(a.causal && k0 > qw0 + 31)) {
+        if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {
             f32x16 sacc[2], pacc[2];  // S^T and dP^T: rows = keys, column = this lane's query
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -673,7 +723,7 @@ AttnArgs make_args(const AttnDesc& d) {
 
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-    dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
+    dim3 grid(((a.seq + BKV - 1) / BKV + 1) / 2, a.batch * a.heads);
     hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(NT8), 0, s, a);
     count_launch();
     return hipGetLastError();
@@ -682,13 +732,13 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 template <int D>
 hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
     const int64_t T = (int64_t)a.batch * a.seq;
-    dim3 grid((a.seq + BQ - 1) / BQ, a.batch * a.heads);
+    dim3 grid_pair(((a.seq + BKV - 1) / BKV + 1) / 2, a.batch * a.heads);
     if (part == ATTN_BWD_ROWDOT)
         hipLaunchKernelGGL(attn_rowdot_kernel<D>, dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
     else if (part == ATTN_BWD_DKDV)
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid, dim3(NT), 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid_pair, dim3(NT8), 0, s, a);
     else if (part == ATTN_BWD_DQ)
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid, dim3(NT8), 0, s, a);
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid_pair, dim3(NT8), 0, s, a);
     else
         return hipErrorInvalidValue;
     count_launch();
