@@ -34,9 +34,11 @@
 //    with two ds_read_b64_tr_b16, which transpose 4x16 blocks across each
 //    16-lane group so that every lane receives 4 consecutive K values of its
 //    row.  No register transposes are needed.
-//  * The epilogue stages each half of the fp32 tile through LDS so that every
-//    thread owns 8 consecutive columns of a row: bias, GeLU, GeLU' (reading U)
-//    and the stores all move 16 bytes per lane.
+//  * The MFMAs accumulate C^T blocks, so a lane holds 4 consecutive columns
+//    of one row.  bf16 outputs get their bias and GeLU in registers and go
+//    through LDS once as a bf16 image (8-byte writes, no bank conflicts), from
+//    which every thread stores 16 bytes of a row; fp32 outputs and the GeLU'
+//    epilogue (which reads U) stage half a tile at a time as fp32.
 //  * Two independent problems of one layout (the two weight gradients of a
 //    sublayer) share a launch; fp32 outputs may split K in two, both halves
 //    adding into a zeroed block (0 + a + b == 0 + b + a exactly, so the result
@@ -254,13 +256,16 @@ struct Half {
     u32x4 b[FN];
 };
 
-// MFMAs number FROM..TO-1 of a sub-step (index = i*FN + j).
+// MFMAs number FROM..TO-1 of a sub-step (index = i*FN + j).  The B fragment
+// goes in as the first operand, so block (i, j) accumulates C^T: lane l holds
+// row l%32 of the block and the 4 consecutive columns 8q + 4*(l/32) .. +3 in
+// values 4q .. 4q+3 (q = 0..3), which the epilogue writes 8 or 16 bytes at a time.
 template <int FROM, int TO, int FM, int FN>
 __device__ __forceinline__ void run_mfmas(f32x16 (&acc)[FM][FN], const Half<FM, FN>& F) {
 #pragma unroll
     for (int idx = FROM; idx < TO; ++idx) {
         const int i = idx / FN, j = idx % FN;
-        acc[i][j] = mfma32x32x16(F.a[i], F.b[j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(F.b[j], F.a[i], acc[i][j]);
     }
 }
 
@@ -494,12 +499,68 @@ constexpr int tile_occupancy() {
     return BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
 }
 
+// bf16 epilogue, first half: the tile's values (plus bias, through GeLU when
+// GELU) as bf16 into a [BM][SP bytes] LDS image.  Each lane writes 8 bytes (4
+// columns of one row) per store; a row pitch of SP = 2*BN + 8 bytes (an odd
+// number of 8-byte pairs) puts the 32 rows of a half-wave on distinct banks.
+template <int FM, int FN, int WTM, int WTN, int SP, bool GELU>
+__device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN], const bf16_t* bias, int ncols,
+                                           int wm, int wn, int lane) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);  // first of the 4 columns
+            float b4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias && nl < ncols) {
+                const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + nl);
+                b4[0] = __uint_as_float(bw[0] << 16);
+                b4[1] = __uint_as_float(bw[0] & 0xffff0000u);
+                b4[2] = __uint_as_float(bw[1] << 16);
+                b4[3] = __uint_as_float(bw[1] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[i][j][4 * q + e] + b4[e];
+                    if constexpr (GELU) v[e] = gelu_f(v[e]);
+                }
+                const u32x2 o = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(st + (wm * WTM + i * 32 + (lane & 31)) * SP + nl * 2) = o;
+            }
+        }
+}
+
+// bf16 epilogue, second half: the LDS image to C rows m0.. (8 columns, 16
+// bytes, per thread and item; rows past M and columns past ncols skipped).
+template <int BM, int BN, int SP>
+__device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ldc, int rows, int ncols, int tid) {
+    constexpr int GPR = BN / 8;  // 8-column groups per row
+    constexpr int ITEMS = BM * GPR / NT;
+    static_assert((BM * GPR) % NT == 0, "epilogue split");
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int e = tid + it * NT;
+        const int lr = e / GPR, cg = e % GPR;
+        if (lr >= rows || cg * 8 >= ncols) continue;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16 + 8);
+        *reinterpret_cast<u32x4*>(C + (int64_t)lr * ldc + cg * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+}
+
 template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
 __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kernel(const GemmBatch batch) {
     using Core = GemmCore<BM, BN, AK, BKC, BKSEG>;
     constexpr int RING = STAGES * Core::STAGE;
-    constexpr int EROWS = BM / 2, ELD = BN + 8;          // epilogue staging: half a tile of fp32
-    constexpr int EBYTES = EROWS * ELD * 4;
+    // fp32 epilogues (weight gradients, GeLU') stage half a tile at a time as
+    // fp32; the bf16 ones stage the whole tile as bf16.
+    constexpr bool F32STAGE = OUTF32 || EPI == EPI_GELU_BWD;
+    constexpr int EROWS = BM / 2, ELD = BN + 4;  // fp32 staging: row pitch BN + 4 floats
+    constexpr int SP = BN * 2 + 8;               // bf16 staging: row pitch in bytes
+    constexpr int EBYTES = F32STAGE ? EROWS * ELD * 4 : BM * SP;
     constexpr int SMEM = RING > EBYTES ? RING : EBYTES;
     constexpr int WTM = Core::WTM, WTN = Core::WTN, FM = Core::FM, FN = Core::FN;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -525,92 +586,92 @@ __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kern
     core.run();
     auto& acc = core.acc;
 
-    // Epilogue: each half of the tile (rows owned by wave-row wm) goes through
-    // LDS as fp32 so that every thread then handles 8 consecutive columns of a
-    // row: 16-byte loads of bias / U and 16-byte stores of the outputs.
     const int csg = n0 / p.cseg;
     const int cofs = csg * p.cseg;
-    float* stage = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    const int rows = p.M - m0, ncols = p.N - n0;  // valid extent of the tile
+    if constexpr (!F32STAGE) {
+        // Bias (and GeLU) on the accumulators; the output image goes through
+        // LDS once (twice with GeLU: U, then Y).
+        const bf16_t* bias = nullptr;
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias = p.bias[csg] ? p.bias[csg] + (n0 - cofs) : nullptr;
+        bf16_t* C = reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m0 * p.ldc + (n0 - cofs);
+        __syncthreads();  // every wave is done with the operand ring
+        stage_bf16<FM, FN, WTM, WTN, SP, false>(smem, acc, bias, ncols, wm, wn, lane);
         __syncthreads();
-        if (wm == half) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        stage[(i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ELD + wn * WTN + j * 32 +
-                              (lane & 31)] = acc[i][j][r];
+        store_bf16<BM, BN, SP>(smem, C, p.ldc, rows, ncols, tid);
+        if constexpr (EPI == EPI_BIAS_GELU) {
+            __syncthreads();
+            stage_bf16<FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane);
+            __syncthreads();
+            store_bf16<BM, BN, SP>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
         }
-        __syncthreads();
-        constexpr int GPR = BN / 8;                 // 8-column groups per row
-        constexpr int ITEMS = EROWS * GPR / NT;
-        static_assert(ITEMS >= 1 && (EROWS * GPR) % NT == 0, "epilogue split");
+    } else {
+        // fp32 staging, half a tile (the rows of wave-row wm == half) at a time,
+        // 16 bytes per lane and store; every thread then handles 8 consecutive
+        // columns of a row (16-byte loads of U and stores of the outputs).
+        float* stage = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int e = tid + it * NT;
-            const int lr = e / GPR, cg = e % GPR;
-            const int m = m0 + half * EROWS + lr, n = n0 + cg * 8;
-            if (m >= p.M || n >= p.N) continue;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8 + 4);
-            float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const int nl = n - cofs;
-            if constexpr (OUTF32) {
-                float* c = reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + nl;
-                if (batch.ksplit > 1) {
-                    continue;  // added below, lane-contiguous
-                } else {
-                    *reinterpret_cast<f32x4*>(c) = lo;
-                    *reinterpret_cast<f32x4*>(c + 4) = hi;
-                }
-            } else {
-                if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-                    const bf16_t* bias = p.bias[csg];
-                    if (bias) {
-                        const u32x4 bw = *reinterpret_cast<const u32x4*>(bias + nl);
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads();
+            if (wm == half) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            v[2 * q] += __uint_as_float(bw[q] << 16);
-                            v[2 * q + 1] += __uint_as_float(bw[q] & 0xffff0000u);
-                        }
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<f32x4*>(stage + (i * 32 + (lane & 31)) * ELD + wn * WTN + j * 32 + 8 * q +
+                                                      4 * (lane >> 5)) =
+                                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
+            __syncthreads();
+            constexpr int GPR = BN / 8;                 // 8-column groups per row
+            constexpr int ITEMS = EROWS * GPR / NT;
+            static_assert(ITEMS >= 1 && (EROWS * GPR) % NT == 0, "epilogue split");
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it) {
+                const int e = tid + it * NT;
+                const int lr = e / GPR, cg = e % GPR;
+                const int m = m0 + half * EROWS + lr, n = n0 + cg * 8;
+                if (m >= p.M || n >= p.N) continue;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8 + 4);
+                const int nl = n - cofs;
+                if constexpr (OUTF32) {
+                    if (batch.ksplit == 1) {
+                        float* c = reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + nl;
+                        *reinterpret_cast<f32x4*>(c) = lo;
+                        *reinterpret_cast<f32x4*>(c + 4) = hi;
                     }
-                }
-                if constexpr (EPI == EPI_GELU_BWD) {
+                } else {  // EPI_GELU_BWD: dU = dY * GeLU'(U)
+                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     const u32x4 uw = *reinterpret_cast<const u32x4*>(p.aux + (int64_t)m * p.ldaux + nl);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         v[2 * q] *= gelu_prime_f(__uint_as_float(uw[q] << 16));
                         v[2 * q + 1] *= gelu_prime_f(__uint_as_float(uw[q] & 0xffff0000u));
                     }
-                }
-                u32x4 o;
+                    u32x4 o;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
-                *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
-                if constexpr (EPI == EPI_BIAS_GELU) {
-                    u32x4 y;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) y[q] = pack_bf2(gelu_f(v[2 * q]), gelu_f(v[2 * q + 1]));
-                    *reinterpret_cast<u32x4*>(p.C2 + (int64_t)m * p.ldc2 + nl) = y;
+                    for (int q = 0; q < 4; ++q) o[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
                 }
             }
-        }
-        if constexpr (OUTF32) {
-            if (batch.ksplit > 1) {
-                // The two K halves add into a zeroed block (0 + a + b == 0 + b + a
-                // exactly, so the result does not depend on their order); consecutive
-                // lanes take consecutive columns so each atomic covers whole lines.
-                constexpr int AITEMS = EROWS * BN / NT;
+            if constexpr (OUTF32) {
+                if (batch.ksplit > 1) {
+                    // The two K halves add into a zeroed block (0 + a + b == 0 + b + a
+                    // exactly, so the result does not depend on their order); consecutive
+                    // lanes take consecutive columns so each atomic covers whole lines.
+                    constexpr int AITEMS = EROWS * BN / NT;
 #pragma unroll 4
-                for (int it = 0; it < AITEMS; ++it) {
-                    const int e = tid + it * NT;
-                    const int lr = e / BN, c = e % BN;
-                    const int m = m0 + half * EROWS + lr, n = n0 + c;
-                    if (m < p.M && n < p.N)
-                        atomicAdd(reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + (n - cofs), stage[lr * ELD + c]);
+                    for (int it = 0; it < AITEMS; ++it) {
+                        const int e = tid + it * NT;
+                        const int lr = e / BN, c = e % BN;
+                        const int m = m0 + half * EROWS + lr, n = n0 + c;
+                        if (m < p.M && n < p.N)
+                            atomicAdd(reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + (n - cofs),
+                                      stage[lr * ELD + c]);
+                    }
                 }
             }
         }
