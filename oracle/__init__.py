@@ -197,25 +197,81 @@ def attn_full_bwd(d, X, Wq, Wk, Wv, bq, bk, bv, Wo, G):
     return o
 
 
-def layernorm(x, eps=1e-5):
-    x = _f64(x)
+def layernorm(x, eps=1e-5, gamma=None, beta=None, stats=False):
+    """Row-wise LayerNorm y = gamma * (x - mean) / sqrt(var + eps) + beta (biased variance;
+    gamma, beta None for 1 and 0).  With stats, also the row means and 1/sqrt(var + eps)."""
+    x, gamma, beta = map(_f64, (x, gamma, beta))
     y = np.empty_like(x)
-    lib().tpo_layernorm(ctypes.c_long(x.shape[0]), ctypes.c_long(x.shape[1]), ctypes.c_double(eps),
-                        _p(x), _p(y))
-    return y
+    mean = np.empty(x.shape[0]); rstd = np.empty(x.shape[0])
+    lib().tpo_layernorm_affine(ctypes.c_long(x.shape[0]), ctypes.c_long(x.shape[1]), ctypes.c_double(eps),
+                               _p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd))
+    return (y, mean, rstd) if stats else y
 
 
-def prelayer_fwd(d, degree, X, p, eps=1e-5):
+def layernorm_bwd(x, dy, eps=1e-5, gamma=None):
+    """Backward of layernorm: dx, dgamma, dbeta for the upstream gradient dy."""
+    x, dy, gamma = map(_f64, (x, dy, gamma))
+    dx = np.empty_like(x); dg = np.empty(x.shape[1]); db = np.empty(x.shape[1])
+    lib().tpo_layernorm_bwd(ctypes.c_long(x.shape[0]), ctypes.c_long(x.shape[1]), ctypes.c_double(eps),
+                            _p(x), _p(gamma), _p(dy), _p(dx), _p(dg), _p(db))
+    return dx, dg, db
+
+
+def _ln_params(p, k):
+    return p.get(f"ln{k}_g"), p.get(f"ln{k}_b")
+
+
+def prelayer_fwd(d, degree, X, p, eps=1e-5, full=False):
     """Pre-LN layer from the shard partials (page "what the tensor parallelism paper actually
-    says", section "The layernorm placement the paper flags as critical"):
-        h1  = x + sum_i Attn_i(LN(x)) + bo
-        out = h1 + sum_i MLP_i(LN(h1)) + b2
-    LayerNorm has no affine part here (gamma = 1, beta = 0)."""
+    says", section "The layernorm placement the paper flags as critical": LayerNorm on the
+    residual stream before each sublayer):
+        h1  = x + sum_i Attn_i(LN1(x)) + bo
+        out = h1 + sum_i MLP_i(LN2(h1)) + b2
+    LN k has the affine part p["lnk_g"], p["lnk_b"] when present (else gamma = 1, beta = 0).
+    With full, a dict of out and the intermediates h1, ln1, ln2."""
     X = _f64(X)
-    ln1 = layernorm(X, eps)
+    g1, be1 = _ln_params(p, 1)
+    g2, be2 = _ln_params(p, 2)
+    ln1 = layernorm(X, eps, g1, be1)
     att = sum(attn_shard_fwd(d, i, degree, ln1, p["Wq"], p["Wk"], p["Wv"], p["bq"], p["bk"],
                              p["bv"], p["Wo"])["Z"] for i in range(degree))
     h1 = X + att + _f64(p["bo"])[None, :]
-    ln2 = layernorm(h1, eps)
+    ln2 = layernorm(h1, eps, g2, be2)
     mlp = sum(mlp_shard_fwd(d, i, degree, ln2, p["A"], p["b1"], p["B"])["Z"] for i in range(degree))
-    return h1 + mlp + _f64(p["b2"])[None, :]
+    out = h1 + mlp + _f64(p["b2"])[None, :]
+    return {"out": out, "h1": h1, "ln1": ln1, "ln2": ln2} if full else out
+
+
+def prelayer_bwd(d, degree, X, p, G, eps=1e-5):
+    """Chain rule back through prelayer_fwd for the upstream gradient G = dL/d out:
+        dh1 = G + LN2_bwd(sum_i dX_i^mlp(G))           (dZ of every MLP shard is G)
+        dx  = dh1 + LN1_bwd(sum_i dX_i^att(dh1))       (dZ of every attention shard is dh1)
+    Returns dx and every parameter gradient (shard blocks filled into full-size arrays;
+    b2 and bo, added once after the sum, get the column sums of G and dh1)."""
+    X, G = _f64(X), _f64(G)
+    g1, _ = _ln_params(p, 1)
+    g2, _ = _ln_params(p, 2)
+    f = prelayer_fwd(d, degree, X, p, eps, full=True)
+    o = {}
+    dx2 = np.zeros_like(X)
+    for i in range(degree):
+        r = mlp_shard_bwd(d, i, degree, f["ln2"], p["A"], p["b1"], p["B"], G,
+                          o.get("dA"), o.get("db1"), o.get("dB"))
+        o["dA"], o["db1"], o["dB"] = r["dA"], r["db1"], r["dB"]
+        dx2 += r["dX"]
+    o["db2"] = G.sum(axis=0)
+    dln2, o["ln2_dg"], o["ln2_db"] = layernorm_bwd(f["h1"], dx2, eps, g2)
+    dh1 = G + dln2
+    dx1 = np.zeros_like(X)
+    att = {}
+    for i in range(degree):
+        att = attn_shard_bwd(d, i, degree, f["ln1"], p["Wq"], p["Wk"], p["Wv"], p["bq"], p["bk"],
+                             p["bv"], p["Wo"], dh1, out=att)
+        dx1 += att["dX"]
+    for k in ("dWq", "dWk", "dWv", "dWo", "dbq", "dbk", "dbv"):
+        o[k] = att[k]
+    o["dbo"] = dh1.sum(axis=0)
+    dln1, o["ln1_dg"], o["ln1_db"] = layernorm_bwd(X, dx1, eps, g1)
+    o["dX"] = dh1 + dln1
+    o["dh1"] = dh1
+    return o

@@ -691,16 +691,76 @@ int tpo_attn_full_bwd(const tpo_dims* d, const double* X,
 
 void tpo_layernorm(long rows, long cols, double eps, const double* x, double* y)
 {
+    tpo_layernorm_affine(rows, cols, eps, x, NULL, NULL, y, NULL, NULL);
+}
+
+/* Row r: mean = (1/n) sum_c x[r,c], var = (1/n) sum_c (x[r,c] - mean)^2 (biased),
+ * rstd = 1/sqrt(var + eps), y[r,c] = gamma[c] * (x[r,c] - mean) * rstd + beta[c]. */
+void tpo_layernorm_affine(long rows, long cols, double eps, const double* x, const double* gamma,
+                          const double* beta, double* y, double* mean_out, double* rstd_out)
+{
+#pragma omp parallel for schedule(static)
     for (long r = 0; r < rows; ++r) {
+        const double* xr = x + r * cols;
         double mean = 0.0, var = 0.0;
-        for (long c = 0; c < cols; ++c) mean += x[r * cols + c];
+        for (long c = 0; c < cols; ++c) mean += xr[c];
         mean /= (double)cols;
-        for (long c = 0; c < cols; ++c) {
-            const double t = x[r * cols + c] - mean;
-            var += t * t;
-        }
+        for (long c = 0; c < cols; ++c) var += (xr[c] - mean) * (xr[c] - mean);
         var /= (double)cols;
-        const double inv = 1.0 / sqrt(var + eps);
-        for (long c = 0; c < cols; ++c) y[r * cols + c] = (x[r * cols + c] - mean) * inv;
+        const double rstd = 1.0 / sqrt(var + eps);
+        for (long c = 0; c < cols; ++c) {
+            const double xhat = (xr[c] - mean) * rstd;
+            y[r * cols + c] = (gamma ? gamma[c] : 1.0) * xhat + (beta ? beta[c] : 0.0);
+        }
+        if (mean_out) mean_out[r] = mean;
+        if (rstd_out) rstd_out[r] = rstd;
     }
+}
+
+/* Chain rule through the row's normalisation, with g = dy * gamma:
+ *   dx[c] = rstd * (g[c] - (1/n) sum_k g[k] - xhat[c] * (1/n) sum_k g[k] xhat[k]),
+ * the terms coming from xhat's direct dependence on x[c], from the mean and
+ * from the variance.  dgamma[c] = sum_r dy[r,c] xhat[r,c], dbeta[c] = sum_r dy[r,c]. */
+void tpo_layernorm_bwd(long rows, long cols, double eps, const double* x, const double* gamma,
+                       const double* dy, double* dx, double* dgamma, double* dbeta)
+{
+    double* xh = (double*)malloc(sizeof(double) * (size_t)(rows * cols));
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const double* xr = x + r * cols;
+        const double* gr = dy + r * cols;
+        double mean = 0.0, var = 0.0;
+        for (long c = 0; c < cols; ++c) mean += xr[c];
+        mean /= (double)cols;
+        for (long c = 0; c < cols; ++c) var += (xr[c] - mean) * (xr[c] - mean);
+        var /= (double)cols;
+        const double rstd = 1.0 / sqrt(var + eps);
+        double sg = 0.0, sgx = 0.0;
+        for (long c = 0; c < cols; ++c) {
+            const double xhat = (xr[c] - mean) * rstd;
+            const double g = gr[c] * (gamma ? gamma[c] : 1.0);
+            xh[r * cols + c] = xhat;
+            sg += g;
+            sgx += g * xhat;
+        }
+        sg /= (double)cols;
+        sgx /= (double)cols;
+        for (long c = 0; c < cols; ++c) {
+            const double g = gr[c] * (gamma ? gamma[c] : 1.0);
+            dx[r * cols + c] = rstd * (g - sg - xh[r * cols + c] * sgx);
+        }
+    }
+    if (dgamma || dbeta) {
+#pragma omp parallel for schedule(static)
+        for (long c = 0; c < cols; ++c) {
+            double sgam = 0.0, sbet = 0.0;
+            for (long r = 0; r < rows; ++r) {
+                sgam += dy[r * cols + c] * xh[r * cols + c];
+                sbet += dy[r * cols + c];
+            }
+            if (dgamma) dgamma[c] = sgam;
+            if (dbeta) dbeta[c] = sbet;
+        }
+    }
+    free(xh);
 }

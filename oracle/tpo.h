@@ -98,6 +98,14 @@ int tpo_attn_full_bwd(const tpo_dims* d, const double* X,
 /* ---- pre-LN layer composition (LayerNorm before each sublayer, residual after) */
 /* LN(x) = (x - mean) / sqrt(var + eps), biased variance, no affine. */
 void tpo_layernorm(long rows, long cols, double eps, const double* x, double* y);
+/* The same with the affine part, y = gamma * LN(x) + beta (gamma, beta [cols] or
+ * NULL for 1 and 0); the row means and 1/sqrt(var + eps) into mean, rstd [rows]
+ * (may be NULL). */
+void tpo_layernorm_affine(long rows, long cols, double eps, const double* x, const double* gamma,
+                          const double* beta, double* y, double* mean, double* rstd);
+/* Its backward: dx [rows,cols] from dy; dgamma, dbeta [cols] (may be NULL). */
+void tpo_layernorm_bwd(long rows, long cols, double eps, const double* x, const double* gamma,
+                       const double* dy, double* dx, double* dgamma, double* dbeta);
 
 /* Number of OpenMP threads the oracle will use. */
 int tpo_num_threads(void);

@@ -366,6 +366,116 @@ def test_layernorm_and_prelayer_composition(oracle_lib):
     assert relerr(out, ref) < 1e-12
 
 
+def _ln_params(rng, h):
+    return {"ln1_g": 1.0 + 0.3 * rng.standard_normal(h), "ln1_b": 0.1 * rng.standard_normal(h),
+            "ln2_g": 1.0 + 0.3 * rng.standard_normal(h), "ln2_b": 0.1 * rng.standard_normal(h)}
+
+
+def test_layernorm_affine_matches_torch_and_normalises(oracle_lib):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((7, 24)) * 3.0 + 1.5
+    g, b = 1.0 + rng.standard_normal(24), rng.standard_normal(24)
+    y, mean, rstd = oracle.layernorm(x, 1e-5, g, b, stats=True)
+    ref = torch.nn.functional.layer_norm(torch.tensor(x), (24,), torch.tensor(g), torch.tensor(b), eps=1e-5)
+    assert relerr(y, ref) < 1e-14
+    np.testing.assert_allclose(mean, x.mean(axis=1), rtol=1e-14)
+    np.testing.assert_allclose(rstd, 1.0 / np.sqrt(x.var(axis=1) + 1e-5), rtol=1e-14)
+    # without the affine part every row has mean 0 and variance var / (var + eps)
+    z = oracle.layernorm(x, 1e-5)
+    np.testing.assert_allclose(z.mean(axis=1), 0.0, atol=1e-14)
+    np.testing.assert_allclose(z.var(axis=1), x.var(axis=1) / (x.var(axis=1) + 1e-5), rtol=1e-13)
+
+
+def test_layernorm_backward_autograd_fd_and_row_sum(oracle_lib):
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((6, 20)) * 2.0
+    g, b = 1.0 + 0.5 * rng.standard_normal(20), rng.standard_normal(20)
+    dy = rng.standard_normal((6, 20))
+    dx, dg, db = oracle.layernorm_bwd(x, dy, 1e-5, g)
+    # torch float64 autograd (library)
+    xt, gt, bt = (torch.tensor(a, requires_grad=True) for a in (x, g, b))
+    yt = torch.nn.functional.layer_norm(xt, (20,), gt, bt, eps=1e-5)
+    ax, ag, ab = torch.autograd.grad((yt * torch.tensor(dy)).sum(), (xt, gt, bt))
+    assert relerr(dx, ax) < 1e-12 and relerr(dg, ag) < 1e-12 and relerr(db, ab) < 1e-13
+    # central finite differences of L = <dy, LN(x)> (calculus)
+    L = lambda xx, gg, bb: float((oracle.layernorm(xx, 1e-5, gg, bb) * dy).sum())
+    e = 1e-6
+    for (r, c) in [(0, 0), (2, 7), (5, 19)]:
+        xp, xm = x.copy(), x.copy()
+        xp[r, c] += e; xm[r, c] -= e
+        assert abs((L(xp, g, b) - L(xm, g, b)) / (2 * e) - dx[r, c]) < 1e-7 * max(1.0, abs(dx[r, c]))
+    for c in (0, 11):
+        gp, gm = g.copy(), g.copy()
+        gp[c] += e; gm[c] -= e
+        assert abs((L(x, gp, b) - L(x, gm, b)) / (2 * e) - dg[c]) < 1e-7 * max(1.0, abs(dg[c]))
+    # the normalisation removes the row mean, so every row of dx sums to zero
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-12)
+
+
+def _torch_prelayer(p, H, s, causal, eps=1e-5):
+    """Unsharded pre-LN layer in torch float64 (library routines), autograd-ready."""
+    names = ["X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo", "bo", "A", "b1", "B", "b2",
+             "ln1_g", "ln1_b", "ln2_g", "ln2_b"]
+    t = {n: torch.tensor(p[n], requires_grad=True) for n in names}
+    h = p["X"].shape[1]
+    ln1 = torch.nn.functional.layer_norm(t["X"], (h,), t["ln1_g"], t["ln1_b"], eps=eps)
+    T, d = ln1.shape[0], h // H
+    b = T // s
+    q = (ln1 @ t["Wq"] + t["bq"]).reshape(b, s, H, d).permute(0, 2, 1, 3)
+    k = (ln1 @ t["Wk"] + t["bk"]).reshape(b, s, H, d).permute(0, 2, 1, 3)
+    v = (ln1 @ t["Wv"] + t["bv"]).reshape(b, s, H, d).permute(0, 2, 1, 3)
+    S = (q @ k.transpose(-1, -2)) / math.sqrt(d)
+    if causal:
+        S = S.masked_fill(torch.ones(s, s, dtype=torch.bool).triu(1), float("-inf"))
+    O = (torch.softmax(S, dim=-1) @ v).permute(0, 2, 1, 3).reshape(T, h)
+    h1 = t["X"] + O @ t["Wo"] + t["bo"]
+    ln2 = torch.nn.functional.layer_norm(h1, (h,), t["ln2_g"], t["ln2_b"], eps=eps)
+    out = h1 + torch.nn.functional.gelu(ln2 @ t["A"] + t["b1"], approximate="none") @ t["B"] + t["b2"]
+    return out, h1, t
+
+
+@pytest.mark.parametrize("degree", [1, 2, 4])
+def test_prelayer_backward_matches_torch_autograd(oracle_lib, degree):
+    rng = np.random.default_rng(23 + degree)
+    b, s, h, H, F = 2, 6, 16, 4, 32
+    d = dims(b, s, h, H, F, True)
+    p = {**rand_params(rng, b * s, h, F), **_ln_params(rng, h)}
+    G = p["G"]
+    o = oracle.prelayer_bwd(d, degree, p["X"], p, G)
+    out, h1, t = _torch_prelayer(p, H, s, True)
+    assert relerr(oracle.prelayer_fwd(d, degree, p["X"], p), out.detach()) < 1e-12
+    names = ["X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo", "bo", "A", "b1", "B", "b2",
+             "ln1_g", "ln1_b", "ln2_g", "ln2_b"]
+    grads = dict(zip(names, torch.autograd.grad((out * torch.tensor(G)).sum(), [t[n] for n in names])))
+    key = {"X": "dX", "ln1_g": "ln1_dg", "ln1_b": "ln1_db", "ln2_g": "ln2_dg", "ln2_b": "ln2_db"}
+    for n in names:
+        k = key.get(n, "d" + n)
+        # dbk is zero in exact arithmetic (a key bias shifts a query's scores by one
+        # constant, which softmax ignores), hence the absolute floor of 1
+        err = np.max(np.abs(o[k] - grads[n].numpy())) / max(1.0, float(np.max(np.abs(grads[n].numpy()))))
+        assert err < 1e-11, (n, err)
+
+
+def test_prelayer_backward_finite_differences(oracle_lib):
+    rng = np.random.default_rng(31)
+    b, s, h, H, F, t = 1, 4, 8, 2, 16, 2
+    d = dims(b, s, h, H, F, True)
+    p = {**rand_params(rng, b * s, h, F), **_ln_params(rng, h)}
+    G = p["G"]
+    o = oracle.prelayer_bwd(d, t, p["X"], p, G)
+    L = lambda q: float((oracle.prelayer_fwd(d, t, q["X"], q) * G).sum())
+    e = 1e-6
+    for name, key, idx in [("X", "dX", (1, 3)), ("X", "dX", (3, 0)), ("ln1_g", "ln1_dg", (5,)),
+                           ("ln2_b", "ln2_db", (2,)), ("Wq", "dWq", (4, 6)), ("B", "dB", (9, 1)),
+                           ("bo", "dbo", (7,))]:
+        qp = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+        qm = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+        qp[name][idx] += e
+        qm[name][idx] -= e
+        fd = (L(qp) - L(qm)) / (2 * e)
+        assert abs(fd - o[key][idx]) < 1e-6 * max(1.0, abs(fd)), (name, idx, fd, o[key][idx])
+
+
 # ------------------------------------------------------------- shape pin
 
 def test_30b_ffn_shape_matches_page():
