@@ -233,6 +233,59 @@ int tp_sum_partials(int dtype, int64_t rows, int64_t cols,
                     const void* const* parts, int nparts, const void* bias,
                     float* out, void* stream);
 
+/*
+ * The pre-LN residual stream around the shards (page "Megatron-LM: what the
+ * tensor parallelism paper actually says", section "The layernorm placement
+ * the paper flags as critical": LayerNorm is applied to the residual stream
+ * before each sublayer, whose output is added back to the stream).  With
+ * h1 = x + sum_i Attn_i(LN1(x)) + bo and out = h1 + sum_i MLP_i(LN2(h1)) + b2,
+ * the layer on one GPU is: tp_residual_layernorm (LN1 of x) -> attention shards
+ * -> tp_residual_layernorm (h1 and LN2 of it) -> MLP shards ->
+ * tp_residual_layernorm (out); backward: MLP shards -> tp_layernorm_bwd (dh1,
+ * db2, dbo is its dx_sum) -> attention shards -> tp_layernorm_bwd (dx).
+ *
+ * tp_residual_layernorm, one workgroup per row:
+ *   h[r,c] = residual[r,c] + bias[c] + sum_k parts[k][r,c]   (fp32; into out if
+ *            out != NULL; residual, bias may be NULL for 0, nparts may be 0)
+ *   y[r,c] = gamma[c] * (h[r,c] - mean_r) * rstd_r + beta[c]  (if y != NULL)
+ *   mean_r = (1/cols) sum_c h[r,c], rstd_r = 1/sqrt((1/cols) sum_c (h[r,c] -
+ *   mean_r)^2 + eps) (biased variance), stored in mean[r], rstd[r] if non-NULL.
+ * parts: host array of `nparts` (<= 16) device pointers to [rows, cols] of
+ * `dtype`; bias [cols] of `dtype`; y [rows, cols] of `dtype`; residual, out
+ * [rows, cols], gamma, beta [cols] (NULL: 1, 0), mean, rstd [rows]: fp32.  All
+ * rows contiguous (row stride cols).  out may alias residual.  At least one of
+ * out, y.  cols a multiple of 8 (else TP_EALIGN) and <= 8192 (else
+ * TP_EUNSUPPORTED); eps > 0.
+ */
+int tp_residual_layernorm(int dtype, int64_t rows, int64_t cols,
+                          const void* const* parts, int nparts, const void* bias,
+                          const float* residual, float* out,
+                          const float* gamma, const float* beta, double eps,
+                          void* y, float* mean, float* rstd, void* stream);
+
+/*
+ * Backward of the LayerNorm y = gamma * (x - mean) * rstd + beta for the
+ * gradient g = sum_k dparts[k] of y (the input-gradient partials of the next
+ * sublayer's shards), plus a residual gradient:
+ *   xhat = (x - mean_r) * rstd_r,  gg = g * gamma
+ *   dx[r,c] = dres[r,c] + rstd_r * (gg - (1/cols) sum_c gg - xhat * (1/cols) sum_c gg*xhat)
+ * dx (fp32) and, if dx_act != NULL, a copy in `dtype` (the next backward's
+ * upstream gradient).  Column sums over rows into the non-NULL ones of:
+ * dgamma = sum_r g*xhat, dbeta = sum_r g, dres_sum = sum_r dres,
+ * dx_sum = sum_r dx ([cols] fp32).  x fp32 [rows, cols] (the LayerNorm input),
+ * mean, rstd as written by tp_residual_layernorm, dres NULL for 0.  work: at
+ * least tp_layernorm_bwd_work_bytes(rows, cols) bytes of device memory
+ * (else TP_ESIZE).  Same layout and size rules as tp_residual_layernorm;
+ * nparts >= 1.  Deterministic (fixed summation orders).
+ */
+size_t tp_layernorm_bwd_work_bytes(int64_t rows, int64_t cols);
+int tp_layernorm_bwd(int dtype, int64_t rows, int64_t cols,
+                     const float* x, const float* gamma, const float* mean, const float* rstd,
+                     const void* const* dparts, int nparts, const float* dres,
+                     float* dx, void* dx_act, float* dgamma, float* dbeta,
+                     float* dres_sum, float* dx_sum, void* work, size_t work_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -541,4 +541,65 @@ int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* pa
                                        static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+constexpr int64_t LN_MAX_COLS = 8192;
+bool ln_cols_ok(int64_t cols) { return cols % 8 == 0; }
+}  // namespace
+
+int tp_residual_layernorm(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts,
+                          const void* bias, const float* residual, float* out, const float* gamma,
+                          const float* beta, double eps, void* y, float* mean, float* rstd, void* stream) {
+    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (rows <= 0 || cols <= 0 || nparts < 0 || nparts > tp::LN_MAXP || (nparts > 0 && !parts) || (!out && !y) ||
+        !(eps > 0.0))
+        return TP_EINVAL;
+    if (!ln_cols_ok(cols)) return TP_EALIGN;
+    if (cols > LN_MAX_COLS || rows > 0x7fffffff) return TP_EUNSUPPORTED;
+    tp::LnFwdDesc d;
+    for (int k = 0; k < nparts; ++k) {
+        if (!parts[k]) return TP_EINVAL;
+        if (!aligned16(parts[k])) return TP_EALIGN;
+        d.parts[k] = parts[k];
+    }
+    const void* ptrs[] = {bias, residual, out, gamma, beta, y, mean, rstd};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return TP_EALIGN;
+    d.rows = rows; d.cols = (int)cols; d.bf16 = dtype == TP_BF16; d.nparts = nparts;
+    d.bias = bias; d.residual = residual; d.out = out; d.gamma = gamma; d.beta = beta; d.eps = (float)eps;
+    d.y = y; d.mean = mean; d.rstd = rstd;
+    return hip_status(tp::residual_layernorm(d, static_cast<hipStream_t>(stream)));
+}
+
+size_t tp_layernorm_bwd_work_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)4 * (size_t)tp::ln_bwd_bands(rows) * (size_t)cols * sizeof(float);
+}
+
+int tp_layernorm_bwd(int dtype, int64_t rows, int64_t cols, const float* x, const float* gamma, const float* mean,
+                     const float* rstd, const void* const* dparts, int nparts, const float* dres, float* dx,
+                     void* dx_act, float* dgamma, float* dbeta, float* dres_sum, float* dx_sum, void* work,
+                     size_t work_bytes, void* stream) {
+    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (rows <= 0 || cols <= 0 || nparts < 1 || nparts > tp::LN_MAXP || !dparts || !x || !mean || !rstd || !dx ||
+        !work)
+        return TP_EINVAL;
+    if (!ln_cols_ok(cols)) return TP_EALIGN;
+    if (cols > LN_MAX_COLS || rows > 0x7fffffff) return TP_EUNSUPPORTED;
+    tp::LnBwdDesc d;
+    for (int k = 0; k < nparts; ++k) {
+        if (!dparts[k]) return TP_EINVAL;
+        if (!aligned16(dparts[k])) return TP_EALIGN;
+        d.dparts[k] = dparts[k];
+    }
+    const void* ptrs[] = {x, gamma, mean, rstd, dres, dx, dx_act, dgamma, dbeta, dres_sum, dx_sum, work};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return TP_EALIGN;
+    if (work_bytes < tp_layernorm_bwd_work_bytes(rows, cols)) return TP_ESIZE;
+    d.rows = rows; d.cols = (int)cols; d.bf16 = dtype == TP_BF16; d.nparts = nparts;
+    d.x = x; d.gamma = gamma; d.mean = mean; d.rstd = rstd; d.dres = dres; d.dx = dx; d.dx_act = dx_act;
+    d.dgamma = dgamma; d.dbeta = dbeta; d.dres_sum = dres_sum; d.dx_sum = dx_sum;
+    d.work = static_cast<float*>(work);
+    return hip_status(tp::layernorm_bwd(d, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

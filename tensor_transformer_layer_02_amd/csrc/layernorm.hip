@@ -1,0 +1,268 @@
+// The pre-LN residual stream around the shards (page "Megatron-LM: what the
+// tensor parallelism paper actually says", section "The layernorm placement
+// the paper flags as critical": LayerNorm is applied to the residual stream
+// before each sublayer, and the sublayer output is added back to it).
+//
+// Forward, one kernel per residual step:
+//   h = residual + bias + sum_k part_k        (the sum that stands in for the
+//                                              all-reduce, the row-parallel bias
+//                                              added once, the residual add)
+//   y = gamma * (h - mean) * rstd + beta      (the next sublayer's LayerNorm;
+//                                              rstd = 1/sqrt(var + eps), biased var)
+// Backward, fed by the input-gradient partials of the sublayer's shards:
+//   g = sum_k dpart_k,  gg = g * gamma
+//   dx = dres + rstd * (gg - mean_c(gg) - xhat * mean_c(gg * xhat))
+//   dgamma = sum_r g * xhat, dbeta = sum_r g, and the column sums of dres and
+//   dx (the row-parallel bias gradients of the two sublayers).
+//
+// A 256-thread workgroup owns a row (forward) or a band of rows (backward);
+// thread t holds the 4-column chunks t, t + 256, ... of a row in registers
+// (NCH chunks, a template parameter, so cols <= 1024 * NCH).  Row sums use a
+// fixed butterfly inside each wave and the four wave sums in order, and the
+// column sums of the backward go through per-band partials added in band
+// order, so every result is deterministic.
+#include "tp_common.h"
+#include "tp_kernels.h"
+
+namespace tp {
+
+namespace {
+
+constexpr int LNT = 256;
+
+struct LnParts {
+    const void* p[LN_MAXP];
+};
+
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 ld4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const f32x4& v);
+template <>
+__device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const f32x4& v) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+}
+
+// Sum of v over the workgroup, the same value in every thread.  red: 4 floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    const float s = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return s;
+}
+
+template <typename T, int NCH>
+__global__ void __launch_bounds__(LNT) residual_ln_kernel(int64_t rows, int cols, const LnParts parts, int nparts,
+                                                          const T* __restrict__ bias,
+                                                          const float* __restrict__ residual, float* __restrict__ out,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta, float eps, T* __restrict__ y,
+                                                          float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t base = r * cols;
+    f32x4 v[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int c = 4 * (tid + LNT * k);
+        v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c >= cols) continue;
+        if (residual) v[k] = ld4<float>(residual + base + c);
+        if (bias) v[k] += ld4<T>(bias + c);
+        for (int q = 0; q < nparts; ++q) v[k] += ld4<T>(static_cast<const T*>(parts.p[q]) + base + c);
+        if (out) st4<float>(out + base + c, v[k]);
+    }
+    if (!y) return;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);  // zero past cols
+    const float mean = block_sum(s, red) / (float)cols;
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        if (4 * (tid + LNT * k) >= cols) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s2 += (v[k][e] - mean) * (v[k][e] - mean);
+    }
+    const float rstd = 1.0f / sqrtf(block_sum(s2, red) / (float)cols + eps);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int c = 4 * (tid + LNT * k);
+        if (c >= cols) continue;
+        const f32x4 g = gamma ? ld4<float>(gamma + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+        const f32x4 b = beta ? ld4<float>(beta + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(g[e], (v[k][e] - mean) * rstd, b[e]);
+        st4<T>(y + base + c, o);
+    }
+    if (tid == 0) {
+        if (mean_out) mean_out[r] = mean;
+        if (rstd_out) rstd_out[r] = rstd;
+    }
+}
+
+// Band b of rows: per-row dx, and per-thread column sums of g * xhat, g, dres
+// and dx over the band into work[q][b][cols] (q = 0..3).
+template <typename T, int NCH>
+__global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int64_t band,
+                                                     const float* __restrict__ x, const float* __restrict__ gamma,
+                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                     const LnParts dparts, int nparts, const float* __restrict__ dres,
+                                                     float* __restrict__ dx, T* __restrict__ dx_act,
+                                                     float* __restrict__ work) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * band, r1 = min(rows, r0 + band);
+    f32x4 sg[NCH], sb[NCH], sr[NCH], sx[NCH], gm[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        sg[k] = sb[k] = sr[k] = sx[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int c = 4 * (tid + LNT * k);
+        gm[k] = (gamma && c < cols) ? ld4<float>(gamma + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t base = r * cols;
+        const float mu = mean[r], rs = rstd[r];
+        f32x4 g[NCH], xh[NCH];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = 4 * (tid + LNT * k);
+            g[k] = xh[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (c >= cols) continue;
+            for (int q = 0; q < nparts; ++q) g[k] += ld4<T>(static_cast<const T*>(dparts.p[q]) + base + c);
+            const f32x4 xv = ld4<float>(x + base + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xh[k][e] = (xv[e] - mu) * rs;
+                const float gg = g[k][e] * gm[k][e];
+                s1 += gg;
+                s2 += gg * xh[k][e];
+            }
+        }
+        const float m1 = block_sum(s1, red) / (float)cols, m2 = block_sum(s2, red) / (float)cols;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = 4 * (tid + LNT * k);
+            if (c >= cols) continue;
+            const f32x4 dr = dres ? ld4<float>(dres + base + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[e] = dr[e] + rs * (g[k][e] * gm[k][e] - m1 - xh[k][e] * m2);
+                sg[k][e] += g[k][e] * xh[k][e];
+                sb[k][e] += g[k][e];
+                sr[k][e] += dr[e];
+                sx[k][e] += o[e];
+            }
+            st4<float>(dx + base + c, o);
+            if (dx_act) st4<T>(dx_act + base + c, o);
+        }
+    }
+    const int64_t nb = gridDim.x;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int c = 4 * (tid + LNT * k);
+        if (c >= cols) continue;
+        st4<float>(work + (0 * nb + blockIdx.x) * cols + c, sg[k]);
+        st4<float>(work + (1 * nb + blockIdx.x) * cols + c, sb[k]);
+        st4<float>(work + (2 * nb + blockIdx.x) * cols + c, sr[k]);
+        st4<float>(work + (3 * nb + blockIdx.x) * cols + c, sx[k]);
+    }
+}
+
+struct Out4 {
+    float* p[4];
+};
+
+// out[q][c] = sum over bands b (in order) of work[q][b][c], for the requested q.
+__global__ void __launch_bounds__(LNT) ln_bwd_colsum_kernel(int cols, int nb, const float* __restrict__ work, Out4 o) {
+    const int c = blockIdx.x * LNT + threadIdx.x;
+    const int q = blockIdx.y;
+    if (c >= cols || !o.p[q]) return;
+    float s = 0.f;
+    for (int b = 0; b < nb; ++b) s += work[((int64_t)q * nb + b) * cols + c];
+    o.p[q][c] = s;
+}
+
+template <typename T, int NCH>
+hipError_t launch_fwd(const LnFwdDesc& d, hipStream_t s) {
+    LnParts P;
+    for (int i = 0; i < LN_MAXP; ++i) P.p[i] = i < d.nparts ? d.parts[i] : nullptr;
+    hipLaunchKernelGGL((residual_ln_kernel<T, NCH>), dim3((unsigned)d.rows), dim3(LNT), 0, s, d.rows, d.cols, P,
+                       d.nparts, static_cast<const T*>(d.bias), d.residual, d.out, d.gamma, d.beta, d.eps,
+                       static_cast<T*>(d.y), d.mean, d.rstd);
+    count_launch();
+    return hipGetLastError();
+}
+
+template <typename T, int NCH>
+hipError_t launch_bwd(const LnBwdDesc& d, hipStream_t s) {
+    LnParts P;
+    for (int i = 0; i < LN_MAXP; ++i) P.p[i] = i < d.nparts ? d.dparts[i] : nullptr;
+    const int nb = ln_bwd_bands(d.rows);
+    const int64_t band = (d.rows + nb - 1) / nb;
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NCH>), dim3((unsigned)nb), dim3(LNT), 0, s, d.rows, d.cols, band, d.x,
+                       d.gamma, d.mean, d.rstd, P, d.nparts, d.dres, d.dx, static_cast<T*>(d.dx_act), d.work);
+    count_launch();
+    Out4 o{{d.dgamma, d.dbeta, d.dres_sum, d.dx_sum}};
+    if (o.p[0] || o.p[1] || o.p[2] || o.p[3]) {
+        hipLaunchKernelGGL(ln_bwd_colsum_kernel, dim3((unsigned)((d.cols + LNT - 1) / LNT), 4), dim3(LNT), 0, s,
+                           d.cols, nb, d.work, o);
+        count_launch();
+    }
+    return hipGetLastError();
+}
+
+// Chunks per thread for a row of `cols` columns (4 columns per chunk).
+int nch_for(int cols) {
+    const int per = (cols / 4 + LNT - 1) / LNT;
+    return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+}
+
+}  // namespace
+
+int ln_bwd_bands(int64_t rows) { return (int)(rows < 256 ? rows : 256); }
+
+hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s) {
+    if (d.rows <= 0) return hipSuccess;
+    switch (nch_for(d.cols)) {
+        case 1: return d.bf16 ? launch_fwd<bf16_t, 1>(d, s) : launch_fwd<float, 1>(d, s);
+        case 2: return d.bf16 ? launch_fwd<bf16_t, 2>(d, s) : launch_fwd<float, 2>(d, s);
+        case 4: return d.bf16 ? launch_fwd<bf16_t, 4>(d, s) : launch_fwd<float, 4>(d, s);
+        default: return d.bf16 ? launch_fwd<bf16_t, 8>(d, s) : launch_fwd<float, 8>(d, s);
+    }
+}
+
+hipError_t layernorm_bwd(const LnBwdDesc& d, hipStream_t s) {
+    if (d.rows <= 0) return hipSuccess;
+    switch (nch_for(d.cols)) {
+        case 1: return d.bf16 ? launch_bwd<bf16_t, 1>(d, s) : launch_bwd<float, 1>(d, s);
+        case 2: return d.bf16 ? launch_bwd<bf16_t, 2>(d, s) : launch_bwd<float, 2>(d, s);
+        case 4: return d.bf16 ? launch_bwd<bf16_t, 4>(d, s) : launch_bwd<float, 4>(d, s);
+        default: return d.bf16 ? launch_bwd<bf16_t, 8>(d, s) : launch_bwd<float, 8>(d, s);
+    }
+}
+
+}  // namespace tp

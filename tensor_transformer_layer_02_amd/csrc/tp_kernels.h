@@ -102,4 +102,55 @@ hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t 
 hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const* parts,
                         int nparts, const void* bias, float* out, hipStream_t s);
 
+// ---- pre-LN residual stream (layernorm.hip) ----
+constexpr int LN_MAXP = 16;  // partials per call
+// h = residual + bias + sum_k parts[k] -> out (fp32, if non-null); then, if y is
+// non-null, y = gamma * (h - mean) / sqrt(var + eps) + beta (biased var; gamma,
+// beta null for 1, 0) in the activation dtype, row means / rstd into mean, rstd.
+// Rows are contiguous ([rows, cols], cols <= 8192, a multiple of 4).
+struct LnFwdDesc {
+    int64_t rows = 0;
+    int cols = 0;
+    bool bf16 = false;               // dtype of parts, bias and y
+    const void* parts[LN_MAXP] = {};
+    int nparts = 0;
+    const void* bias = nullptr;
+    const float* residual = nullptr;
+    float* out = nullptr;
+    const float* gamma = nullptr;
+    const float* beta = nullptr;
+    float eps = 1e-5f;
+    void* y = nullptr;
+    float* mean = nullptr;
+    float* rstd = nullptr;
+};
+hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s);
+
+// LayerNorm backward for g = sum_k dparts[k] (the gradient of y):
+// dx = dres + rstd * (g*gamma - mean_c(g*gamma) - xhat * mean_c(g*gamma*xhat)) (fp32,
+// and in the activation dtype into dx_act if non-null); the column sums
+// dgamma = sum_r g*xhat, dbeta = sum_r g, dres_sum = sum_r dres, dx_sum = sum_r dx
+// into the non-null ones.  work: 4 * ln_bwd_bands(rows) * cols floats.
+struct LnBwdDesc {
+    int64_t rows = 0;
+    int cols = 0;
+    bool bf16 = false;               // dtype of dparts and dx_act
+    const float* x = nullptr;
+    const float* gamma = nullptr;
+    const float* mean = nullptr;
+    const float* rstd = nullptr;
+    const void* dparts[LN_MAXP] = {};
+    int nparts = 0;
+    const float* dres = nullptr;
+    float* dx = nullptr;
+    void* dx_act = nullptr;
+    float* dgamma = nullptr;
+    float* dbeta = nullptr;
+    float* dres_sum = nullptr;
+    float* dx_sum = nullptr;
+    float* work = nullptr;
+};
+int ln_bwd_bands(int64_t rows);
+hipError_t layernorm_bwd(const LnBwdDesc& d, hipStream_t s);
+
 }  // namespace tp

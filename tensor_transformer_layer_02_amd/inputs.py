@@ -67,3 +67,28 @@ def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a stored tensor to a contiguous float64 numpy array."""
     return np.ascontiguousarray(t.to(torch.float64).numpy())
+
+
+LAYER_EXTRA = ["X32", "ln1_g", "ln1_b", "ln2_g", "ln2_b"]
+
+
+def make_layer_inputs(cfg: LayerConfig, bias_std: float = 0.0, ln_std: float = 0.0) -> dict:
+    """Inputs of the whole pre-LN layer: the shard tensors of make_inputs, plus the fp32
+    residual-stream input X32 ~ N(0, 1), LayerNorm gains 1 + N(0, ln_std) and shifts
+    N(0, ln_std) (fp32), and the upstream gradient twice: dZ in the storage dtype (what
+    the shards take) and G32, the same values widened to fp32 (what the residual path
+    adds).  Seeds continue after TENSOR_ORDER (k = 14, 15, ...)."""
+    out = make_inputs(cfg, bias_std)
+    base = 1000 * cfg.cid
+    T, h = cfg.tokens, cfg.hidden
+    for j, name in enumerate(LAYER_EXTRA):
+        g = torch.Generator().manual_seed(base + len(TENSOR_ORDER) + j)
+        if name == "X32":
+            out[name] = torch.randn((T, h), generator=g, dtype=torch.float32)
+        elif ln_std == 0.0:
+            out[name] = (torch.ones if name.endswith("_g") else torch.zeros)(h, dtype=torch.float32)
+        else:
+            t = torch.randn(h, generator=g, dtype=torch.float32) * ln_std
+            out[name] = t + 1.0 if name.endswith("_g") else t
+    out["G32"] = out["dZ"].to(torch.float32)
+    return out

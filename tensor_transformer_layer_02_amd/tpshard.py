@@ -22,7 +22,8 @@ STATUS = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_EDIVIDE", 3: "TP_ESHARD", 4: "TP_EA
 EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_bytes", "tp_attn_saved_bytes",
            "tp_mlp_work_bytes", "tp_attn_work_bytes", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
            "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_sum_partials", "tp_profile_enable",
-           "tp_profile_count", "tp_profile_kernels"]
+           "tp_profile_count", "tp_profile_kernels", "tp_residual_layernorm", "tp_layernorm_bwd_work_bytes",
+           "tp_layernorm_bwd"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
@@ -71,6 +72,13 @@ def lib() -> ctypes.CDLL:
         L.tp_profile_enable.argtypes = [ctypes.POINTER(vp), i32]
         L.tp_profile_count.argtypes = [i32]
         L.tp_profile_kernels.argtypes = [i32]
+        PP = ctypes.POINTER(vp)
+        L.tp_residual_layernorm.argtypes = [i32, i64, i64, PP, i32, vp, fp, fp, fp, fp, ctypes.c_double, vp, fp, fp,
+                                            vp]
+        L.tp_layernorm_bwd_work_bytes.restype = sz
+        L.tp_layernorm_bwd_work_bytes.argtypes = [i64, i64]
+        L.tp_layernorm_bwd.argtypes = [i32, i64, i64, fp, fp, fp, fp, PP, i32, fp, fp, vp, fp, fp, fp, fp, vp, sz,
+                                       vp]
         _lib = L
     return _lib
 
@@ -202,3 +210,27 @@ def tp_profile_count(step: int) -> int:
 
 def tp_profile_kernels(step: int) -> int:
     return lib().tp_profile_kernels(int(step))
+
+
+def _parr(ts):
+    arr = (ctypes.c_void_p * max(1, len(ts)))(*[_ptr(t) for t in ts])
+    return arr
+
+
+def tp_residual_layernorm(dtype, rows, cols, parts, bias, residual, out, gamma, beta, eps, y, mean, rstd,
+                          stream=None):
+    return _call("tp_residual_layernorm", int(dtype), int(rows), int(cols), _parr(parts), len(parts), _ptr(bias),
+                 _ptr(residual), _ptr(out), _ptr(gamma), _ptr(beta), float(eps), _ptr(y), _ptr(mean), _ptr(rstd),
+                 _stream(stream))
+
+
+def tp_layernorm_bwd_work_bytes(rows, cols) -> int:
+    return lib().tp_layernorm_bwd_work_bytes(int(rows), int(cols))
+
+
+def tp_layernorm_bwd(dtype, rows, cols, x, gamma, mean, rstd, dparts, dres, dx, dx_act, dgamma, dbeta, dres_sum,
+                     dx_sum, work, stream=None):
+    return _call("tp_layernorm_bwd", int(dtype), int(rows), int(cols), _ptr(x), _ptr(gamma), _ptr(mean),
+                 _ptr(rstd), _parr(dparts), len(dparts), _ptr(dres), _ptr(dx), _ptr(dx_act), _ptr(dgamma),
+                 _ptr(dbeta), _ptr(dres_sum), _ptr(dx_sum), _ptr(work), work.numel() * work.element_size(),
+                 _stream(stream))
