@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole pre-LN layer instead (all t shards of both sublayers plus the "
+                         "residual / LayerNorm kernels, on one GPU) and print its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -170,6 +173,8 @@ def main():
     if not cfg.backward:
         cfg = cfg.with_(backward=True)
     K, W = args.steps, args.warmup
+    if args.layer:
+        return bench_layer(cfg, K, W)
     log(f"[bench] {cfg.note}: T={cfg.tokens} h={cfg.hidden} F/t={cfg.ffn_per_shard} H/t={cfg.heads_per_shard} "
         f"d={cfg.head_dim} shard={args.shard}")
     inp = make_inputs(cfg)
@@ -279,6 +284,72 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_layer(cfg, K, W):
+    """The whole pre-LN layer on one GPU: every shard of both sublayers, the fused residual-sum +
+    LayerNorm kernels and the LayerNorm backward.  value = algorithmic TFLOP/s of the t shards;
+    the roofline object is the LayerNorm / residual phase with the largest share (HBM-bound)."""
+    import torch
+
+    from tensor_transformer_layer_02_amd.configs import shard_flops
+    from tensor_transformer_layer_02_amd.inputs import make_layer_inputs
+    from tensor_transformer_layer_02_amd.layer import PreLNLayer
+
+    log(f"[bench] pre-LN layer {cfg.name}: T={cfg.tokens} h={cfg.hidden} F={cfg.ffn} H={cfg.heads} "
+        f"t={cfg.degree} shards on one GPU")
+    layer = PreLNLayer(cfg, make_layer_inputs(cfg))
+    flops = cfg.degree * shard_flops(cfg, backward=True)["total"]
+    phases = PreLNLayer.FORWARD + PreLNLayer.BACKWARD
+    for _ in range(W):
+        layer.forward()
+        layer.backward()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        layer.forward()
+        layer.backward()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/layer step  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    # per-phase timing (events on the current stream around each phase)
+    ev = {ph: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for ph in phases}
+    for k in range(K):
+        for ph in phases:
+            ev[ph][k][0].record()
+            getattr(layer, ph)()
+            ev[ph][k][1].record()
+    torch.cuda.synchronize()
+    nbytes = layer.ln_bytes()
+    rows = []
+    for ph in phases:
+        us = sum(a.elapsed_time(b) for a, b in ev[ph]) / K * 1e3
+        r = {"phase": ph, "avg_us": round(us, 2)}
+        if ph in nbytes:
+            r["bytes"] = nbytes[ph]
+            r["gbs"] = round(nbytes[ph] / (us * 1e-6) / 1e9, 1)
+        rows.append(r)
+        log(f"  {ph:<14} {us:9.2f} us" + (f"  {r['gbs']:8.1f} GB/s" if "gbs" in r else ""))
+    dom = max((r for r in rows if "gbs" in r), key=lambda r: r["avg_us"])
+    out = {
+        "metric": "pre-LN layer fwd+bwd TFLOP/s, all t shards on one GPU, 8.3B shape",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": f"{cfg.name} pre-LN layer: {cfg.degree} shards + residual/LayerNorm kernels",
+                   "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn,
+                   "degree": cfg.degree, "flops_per_step": flops},
+        "roofline": {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dom["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "traffic_note": "algorithmic bytes; no counter table for this workload"},
+        "cpu_baseline": None,
+        "phases": rows,
     }
     print(json.dumps(out), flush=True)
 

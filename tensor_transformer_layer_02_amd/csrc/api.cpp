@@ -572,7 +572,7 @@ int tp_residual_layernorm(int dtype, int64_t rows, int64_t cols, const void* con
 
 size_t tp_layernorm_bwd_work_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)4 * (size_t)tp::ln_bwd_bands(rows) * (size_t)cols * sizeof(float);
+    return (size_t)4 * ((size_t)tp::ln_bwd_bands(rows) + tp::LN_BWD_GROUPS) * (size_t)cols * sizeof(float);
 }
 
 int tp_layernorm_bwd(int dtype, int64_t rows, int64_t cols, const float* x, const float* gamma, const float* mean,

@@ -19,8 +19,8 @@
 // thread t holds the 4-column chunks t, t + 256, ... of a row in registers
 // (NCH chunks, a template parameter, so cols <= 1024 * NCH).  Row sums use a
 // fixed butterfly inside each wave and the four wave sums in order, and the
-// column sums of the backward go through per-band partials added in band
-// order, so every result is deterministic.
+// column sums of the backward go through per-band partials added in two
+// levels of fixed order, so every result is deterministic.
 #include "tp_common.h"
 #include "tp_kernels.h"
 
@@ -29,6 +29,7 @@ namespace tp {
 namespace {
 
 constexpr int LNT = 256;
+constexpr int LN_GROUPS = LN_BWD_GROUPS;  // first-level groups of bands in the column sums
 
 struct LnParts {
     const void* p[LN_MAXP];
@@ -68,6 +69,24 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     const float s = (red[0] + red[1]) + (red[2] + red[3]);
     __syncthreads();
     return s;
+}
+
+// The same for two values at once (one pair of barriers).  red: 8 floats of LDS.
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a += __shfl_xor(a, o);
+        b += __shfl_xor(b, o);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[wave] = a;
+        red[4 + wave] = b;
+    }
+    __syncthreads();
+    a = (red[0] + red[1]) + (red[2] + red[3]);
+    b = (red[4] + red[5]) + (red[6] + red[7]);
+    __syncthreads();
 }
 
 template <typename T, int NCH>
@@ -123,15 +142,15 @@ __global__ void __launch_bounds__(LNT) residual_ln_kernel(int64_t rows, int cols
 }
 
 // Band b of rows: per-row dx, and per-thread column sums of g * xhat, g, dres
-// and dx over the band into work[q][b][cols] (q = 0..3).
+// and dx over the band into work[q][b][cols] for the requested q (bit q of need).
 template <typename T, int NCH>
 __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int64_t band,
                                                      const float* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      const LnParts dparts, int nparts, const float* __restrict__ dres,
                                                      float* __restrict__ dx, T* __restrict__ dx_act,
-                                                     float* __restrict__ work) {
-    __shared__ float red[4];
+                                                     float* __restrict__ work, int need) {
+    __shared__ float red[8];
     const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * band, r1 = min(rows, r0 + band);
     f32x4 sg[NCH], sb[NCH], sr[NCH], sx[NCH], gm[NCH];
@@ -161,7 +180,8 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
                 s2 += gg * xh[k][e];
             }
         }
-        const float m1 = block_sum(s1, red) / (float)cols, m2 = block_sum(s2, red) / (float)cols;
+        block_sum2(s1, s2, red);
+        const float m1 = s1 / (float)cols, m2 = s2 / (float)cols;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int c = 4 * (tid + LNT * k);
@@ -185,10 +205,10 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
     for (int k = 0; k < NCH; ++k) {
         const int c = 4 * (tid + LNT * k);
         if (c >= cols) continue;
-        st4<float>(work + (0 * nb + blockIdx.x) * cols + c, sg[k]);
-        st4<float>(work + (1 * nb + blockIdx.x) * cols + c, sb[k]);
-        st4<float>(work + (2 * nb + blockIdx.x) * cols + c, sr[k]);
-        st4<float>(work + (3 * nb + blockIdx.x) * cols + c, sx[k]);
+        if (need & 1) st4<float>(work + (0 * nb + blockIdx.x) * cols + c, sg[k]);
+        if (need & 2) st4<float>(work + (1 * nb + blockIdx.x) * cols + c, sb[k]);
+        if (need & 4) st4<float>(work + (2 * nb + blockIdx.x) * cols + c, sr[k]);
+        if (need & 8) st4<float>(work + (3 * nb + blockIdx.x) * cols + c, sx[k]);
     }
 }
 
@@ -196,13 +216,27 @@ struct Out4 {
     float* p[4];
 };
 
-// out[q][c] = sum over bands b (in order) of work[q][b][c], for the requested q.
-__global__ void __launch_bounds__(LNT) ln_bwd_colsum_kernel(int cols, int nb, const float* __restrict__ work, Out4 o) {
+// Column sums of the band partials in two levels, each in a fixed order:
+// part2[q][s][c] = sum over the bands of group s (nb / LN_GROUPS consecutive bands) ...
+__global__ void __launch_bounds__(LNT) ln_bwd_colsum1_kernel(int cols, int nb, const float* __restrict__ work,
+                                                             float* __restrict__ part2, int need) {
+    const int c = blockIdx.x * LNT + threadIdx.x;
+    const int q = blockIdx.y, g = blockIdx.z;
+    if (c >= cols || !((need >> q) & 1)) return;
+    const int per = (nb + LN_GROUPS - 1) / LN_GROUPS;
+    const int b0 = g * per, b1 = min(nb, b0 + per);
+    float s = 0.f;
+    for (int b = b0; b < b1; ++b) s += work[((int64_t)q * nb + b) * cols + c];
+    part2[((int64_t)q * LN_GROUPS + g) * cols + c] = s;
+}
+
+// ... and out[q][c] = sum over the groups s (in order) of part2[q][s][c].
+__global__ void __launch_bounds__(LNT) ln_bwd_colsum2_kernel(int cols, const float* __restrict__ part2, Out4 o) {
     const int c = blockIdx.x * LNT + threadIdx.x;
     const int q = blockIdx.y;
     if (c >= cols || !o.p[q]) return;
     float s = 0.f;
-    for (int b = 0; b < nb; ++b) s += work[((int64_t)q * nb + b) * cols + c];
+    for (int g = 0; g < LN_GROUPS; ++g) s += part2[((int64_t)q * LN_GROUPS + g) * cols + c];
     o.p[q][c] = s;
 }
 
@@ -223,13 +257,18 @@ hipError_t launch_bwd(const LnBwdDesc& d, hipStream_t s) {
     for (int i = 0; i < LN_MAXP; ++i) P.p[i] = i < d.nparts ? d.dparts[i] : nullptr;
     const int nb = ln_bwd_bands(d.rows);
     const int64_t band = (d.rows + nb - 1) / nb;
-    hipLaunchKernelGGL((ln_bwd_kernel<T, NCH>), dim3((unsigned)nb), dim3(LNT), 0, s, d.rows, d.cols, band, d.x,
-                       d.gamma, d.mean, d.rstd, P, d.nparts, d.dres, d.dx, static_cast<T*>(d.dx_act), d.work);
-    count_launch();
     Out4 o{{d.dgamma, d.dbeta, d.dres_sum, d.dx_sum}};
-    if (o.p[0] || o.p[1] || o.p[2] || o.p[3]) {
-        hipLaunchKernelGGL(ln_bwd_colsum_kernel, dim3((unsigned)((d.cols + LNT - 1) / LNT), 4), dim3(LNT), 0, s,
-                           d.cols, nb, d.work, o);
+    const int need = (o.p[0] ? 1 : 0) | (o.p[1] ? 2 : 0) | (o.p[2] ? 4 : 0) | (o.p[3] ? 8 : 0);
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NCH>), dim3((unsigned)nb), dim3(LNT), 0, s, d.rows, d.cols, band, d.x,
+                       d.gamma, d.mean, d.rstd, P, d.nparts, d.dres, d.dx, static_cast<T*>(d.dx_act), d.work, need);
+    count_launch();
+    if (need) {
+        float* part2 = d.work + (int64_t)4 * nb * d.cols;
+        const unsigned cb = (unsigned)((d.cols + LNT - 1) / LNT);
+        hipLaunchKernelGGL(ln_bwd_colsum1_kernel, dim3(cb, 4, LN_GROUPS), dim3(LNT), 0, s, d.cols, nb, d.work, part2,
+                           need);
+        count_launch();
+        hipLaunchKernelGGL(ln_bwd_colsum2_kernel, dim3(cb, 4), dim3(LNT), 0, s, d.cols, part2, o);
         count_launch();
     }
     return hipGetLastError();
@@ -243,7 +282,9 @@ int nch_for(int cols) {
 
 }  // namespace
 
-int ln_bwd_bands(int64_t rows) { return (int)(rows < 256 ? rows : 256); }
+// 768 bands: one round of workgroups on 256 CUs at three per CU (the backward
+// kernel's registers allow three 4-wave workgroups).
+int ln_bwd_bands(int64_t rows) { return (int)(rows < 768 ? rows : 768); }
 
 hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s) {
     if (d.rows <= 0) return hipSuccess;

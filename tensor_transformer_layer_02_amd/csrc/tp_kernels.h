@@ -130,7 +130,7 @@ hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s);
 // dx = dres + rstd * (g*gamma - mean_c(g*gamma) - xhat * mean_c(g*gamma*xhat)) (fp32,
 // and in the activation dtype into dx_act if non-null); the column sums
 // dgamma = sum_r g*xhat, dbeta = sum_r g, dres_sum = sum_r dres, dx_sum = sum_r dx
-// into the non-null ones.  work: 4 * ln_bwd_bands(rows) * cols floats.
+// into the non-null ones.  work: 4 * (ln_bwd_bands(rows) + LN_BWD_GROUPS) * cols floats.
 struct LnBwdDesc {
     int64_t rows = 0;
     int cols = 0;
@@ -151,6 +151,7 @@ struct LnBwdDesc {
     float* work = nullptr;
 };
 int ln_bwd_bands(int64_t rows);
+constexpr int LN_BWD_GROUPS = 32;
 hipError_t layernorm_bwd(const LnBwdDesc& d, hipStream_t s);
 
 }  // namespace tp

@@ -58,42 +58,88 @@ class PreLNLayer:
                      "dX_attn": torch.empty((T, h), **act), "dX_mlp": torch.empty((T, h), **act)}
                     for i in range(t)]
 
-    def forward(self, stream=None):
+    # ------------------------------------------------------------ phases
+    def ln1(self, stream=None):
         x, a, T, h = self.x, self.a, self.cfg.tokens, self.cfg.hidden
-        # LN1(x)
         tp.tp_residual_layernorm(self.act, T, h, [], None, x["X32"], None, x["ln1_g"], x["ln1_b"], EPS,
                                  a["ln1"], a["mean1"], a["rstd1"], stream)
+
+    def attn_fwd(self, stream=None):
+        x, a = self.x, self.a
         for i, b in enumerate(self.buf):
             tp.tp_attn_shard_fwd(self.dims, i, self.t, a["ln1"], x["Wq"], x["Wk"], x["Wv"], x.get("bq"),
                                  x.get("bk"), x.get("bv"), x["Wo"], b["Z_attn"], b["attn_saved"], stream)
-        # h1 = x + sum_i Z_i + bo, and LN2(h1)
+
+    def residual_ln2(self, stream=None):
+        """h1 = x + sum_i Z_i + bo, and LN2(h1)."""
+        x, a, T, h = self.x, self.a, self.cfg.tokens, self.cfg.hidden
         tp.tp_residual_layernorm(self.act, T, h, [b["Z_attn"] for b in self.buf], x.get("bo"), x["X32"], a["h1"],
                                  x["ln2_g"], x["ln2_b"], EPS, a["ln2"], a["mean2"], a["rstd2"], stream)
+
+    def mlp_fwd(self, stream=None):
+        x, a = self.x, self.a
         for i, b in enumerate(self.buf):
             tp.tp_mlp_shard_fwd(self.dims, i, self.t, a["ln2"], x["A"], x.get("b1"), x["B"], b["Z_mlp"],
                                 b["mlp_saved"], stream)
-        # out = h1 + sum_i Z_i + b2
+
+    def residual_out(self, stream=None):
+        """out = h1 + sum_i Z_i + b2."""
+        x, a, T, h = self.x, self.a, self.cfg.tokens, self.cfg.hidden
         tp.tp_residual_layernorm(self.act, T, h, [b["Z_mlp"] for b in self.buf], x.get("b2"), a["h1"], a["out"],
                                  None, None, EPS, None, None, None, stream)
-        return a["out"]
 
-    def backward(self, stream=None):
-        """Upstream gradient: x["dZ"] (activation dtype, fed to the MLP shards) and x["G32"]
-        (the same values in fp32, on the residual path)."""
-        x, a, g, T, h = self.x, self.a, self.grads, self.cfg.tokens, self.cfg.hidden
+    def mlp_bwd(self, stream=None):
+        x, a, g = self.x, self.a, self.grads
         for i, b in enumerate(self.buf):
             tp.tp_mlp_shard_bwd(self.dims, i, self.t, a["ln2"], x["A"], x["B"], b["mlp_saved"], x["dZ"],
                                 b["dX_mlp"], g["dA"], g["db1"], g["dB"], b["mlp_work"], stream)
-        # dh1 = G + LN2_bwd(sum_i dX_i); db2 = column sums of G, dbo = those of dh1
+
+    def ln2_bwd(self, stream=None):
+        """dh1 = G + LN2_bwd(sum_i dX_i); db2 = column sums of G, dbo = those of dh1."""
+        x, a, g, T, h = self.x, self.a, self.grads, self.cfg.tokens, self.cfg.hidden
         tp.tp_layernorm_bwd(self.act, T, h, a["h1"], x["ln2_g"], a["mean2"], a["rstd2"],
                             [b["dX_mlp"] for b in self.buf], x["G32"], a["dh1"], a["dh1_act"], g["ln2_dg"],
                             g["ln2_db"], g["db2"], g["dbo"], a["ln_work"], stream)
+
+    def attn_bwd(self, stream=None):
+        x, a, g = self.x, self.a, self.grads
         for i, b in enumerate(self.buf):
             tp.tp_attn_shard_bwd(self.dims, i, self.t, a["ln1"], x["Wq"], x["Wk"], x["Wv"], x["Wo"],
                                  b["attn_saved"], a["dh1_act"], b["dX_attn"], g["dWq"], g["dWk"], g["dWv"],
                                  g["dbq"], g["dbk"], g["dbv"], g["dWo"], b["attn_work"], stream)
-        # dx = dh1 + LN1_bwd(sum_i dX_i)
+
+    def ln1_bwd(self, stream=None):
+        """dx = dh1 + LN1_bwd(sum_i dX_i)."""
+        x, a, g, T, h = self.x, self.a, self.grads, self.cfg.tokens, self.cfg.hidden
         tp.tp_layernorm_bwd(self.act, T, h, x["X32"], x["ln1_g"], a["mean1"], a["rstd1"],
                             [b["dX_attn"] for b in self.buf], a["dh1"], a["dX"], None, g["ln1_dg"], g["ln1_db"],
                             None, None, a["ln_work"], stream)
-        return a["dX"]
+
+    FORWARD = ("ln1", "attn_fwd", "residual_ln2", "mlp_fwd", "residual_out")
+    BACKWARD = ("mlp_bwd", "ln2_bwd", "attn_bwd", "ln1_bwd")
+
+    def forward(self, stream=None):
+        for ph in self.FORWARD:
+            getattr(self, ph)(stream)
+        return self.a["out"]
+
+    def backward(self, stream=None):
+        """Upstream gradient: x["dZ"] (activation dtype, fed to the MLP shards) and x["G32"]
+        (the same values in fp32, on the residual path)."""
+        for ph in self.BACKWARD:
+            getattr(self, ph)(stream)
+        return self.a["dX"]
+
+    def ln_bytes(self) -> dict:
+        """Algorithmic HBM bytes of each LayerNorm / residual phase (every tensor read or
+        written once; the backward's band partials counted)."""
+        T, h, t = self.cfg.tokens, self.cfg.hidden, self.t
+        e = 2 if self.dt == torch.bfloat16 else 4
+        nb = min(T, 768)
+        # band partials: written, read, and their 32 group sums written and read
+        part = lambda q: q * 2 * (nb + 32) * h * 4
+        return {"ln1": T * h * (4 + e) + 8 * T,
+                "residual_ln2": T * h * (4 + t * e + 4 + e) + h * e + 8 * T,
+                "residual_out": T * h * (4 + t * e + 4) + h * e,
+                "ln2_bwd": T * h * (4 + t * e + 4 + 4 + e) + 8 * T + part(4),
+                "ln1_bwd": T * h * (4 + t * e + 4 + 4) + 8 * T + part(2)}
