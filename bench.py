@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="backward with activation recompute (the forward's activations rebuilt from X; "
+                         "recompute FLOPs are not counted)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole pre-LN layer instead (all t shards of both sublayers plus the "
                          "residual / LayerNorm kernels, on one GPU) and print its own JSON line")
@@ -178,13 +181,14 @@ def main():
     log(f"[bench] {cfg.note}: T={cfg.tokens} h={cfg.hidden} F/t={cfg.ffn_per_shard} H/t={cfg.heads_per_shard} "
         f"d={cfg.head_dim} shard={args.shard}")
     inp = make_inputs(cfg)
-    run = ShardRun(cfg, inp, shards=[args.shard])
+    run = ShardRun(cfg, inp, shards=[args.shard], recompute=args.recompute)
+    step = lambda: run.step(args.shard, recompute=args.recompute)
     flops = shard_flops(cfg, backward=True)["total"]
     prop = torch.cuda.get_device_properties(0)
     log(f"[bench] device {prop.name} CUs={prop.multi_processor_count} peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
 
     for _ in range(W):
-        run.step(args.shard)
+        step()
     torch.cuda.synchronize()
 
     # ---- timed region: K whole steps on the current stream ----
@@ -193,7 +197,7 @@ def main():
     t_wall = time.perf_counter()
     e0.record()
     for _ in range(K):
-        run.step(args.shard)
+        step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -210,7 +214,7 @@ def main():
         tp.tp_profile_enable(ev.ev, K)
         e0.record()
         for _ in range(K):
-            run.step(args.shard)
+            step()
         e1.record()
         torch.cuda.synchronize()
         ms_hooked = e0.elapsed_time(e1) / K
@@ -280,7 +284,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": cfg.batch, "seq": cfg.seq,
                    "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn,
                    "degree": cfg.degree, "shard": args.shard, "causal": cfg.causal,
-                   "flops_per_step": flops, "parallelism": "one tp shard on one GPU (no collectives)"},
+                   "flops_per_step": flops, "parallelism": "one tp shard on one GPU (no collectives)",
+                   "activations": "recomputed in the backward" if args.recompute else "saved"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

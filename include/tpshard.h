@@ -206,6 +206,34 @@ enum {
 };
 
 /*
+ * Activation-recompute variants of the backward entry points (page
+ * "Megatron-LM: what the tensor parallelism paper actually says", section
+ * "What actually limits throughput in production": activation checkpointing
+ * recomputes the forward's activations in the backward instead of keeping
+ * them).  They take no `saved` buffer: the forward steps whose outputs the
+ * backward reads (MLP: U and Y, one GEMM; attention: QKV and the attention
+ * core, O and LSE) run again from X into the front of `work`, then the
+ * backward runs exactly as tp_*_shard_bwd, so the results are bitwise those of
+ * the saved-activation path.  The caller need not keep `saved` from the
+ * forward.  work: tp_*_recompute_work_bytes bytes (the saved layout followed
+ * by the backward's work), else TP_ESIZE.  The column-parallel biases are
+ * needed again (b1; bq, bk, bv), NULL meaning zero as in the forward.
+ */
+size_t tp_mlp_recompute_work_bytes(const tp_dims* dims, int shard, int degree);
+size_t tp_attn_recompute_work_bytes(const tp_dims* dims, int shard, int degree);
+int tp_mlp_shard_bwd_recompute(const tp_dims* dims, int shard, int degree,
+                               const void* X, const void* A, const void* b1, const void* B,
+                               const void* dZ, void* dX_part, float* dA, float* db1, float* dB,
+                               void* work, size_t work_bytes, void* stream);
+int tp_attn_shard_bwd_recompute(const tp_dims* dims, int shard, int degree,
+                                const void* X, const void* Wq, const void* Wk, const void* Wv,
+                                const void* bq, const void* bk, const void* bv, const void* Wo,
+                                const void* dZ, void* dX_part,
+                                float* dWq, float* dWk, float* dWv,
+                                float* dbq, float* dbk, float* dbv, float* dWo,
+                                void* work, size_t work_bytes, void* stream);
+
+/*
  * While enabled, every launch of step s is bracketed by
  * hipEventRecord(events[2*(s*npairs + k)], stream) and
  * hipEventRecord(events[2*(s*npairs + k) + 1], stream), where k counts that

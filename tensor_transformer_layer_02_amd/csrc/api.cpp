@@ -227,6 +227,51 @@ inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, i
     return e != hipSuccess ? e : tp::gemm_f32(g[1], st);
 }
 
+// The forward steps whose outputs the backward needs, into `saved`:
+// U = X A[:, C_i] + b1[C_i] and Y = GeLU(U) (one GEMM with a fused epilogue).
+hipError_t mlp_fwd_saved(const Shape& s, const void* X, const void* A, const void* b1, void* saved,
+                         hipStream_t st) {
+    const MlpSaved L = mlp_saved(s);
+    const int64_t c0 = s.i * s.Fs;
+    tp::GemmDesc g1;
+    g1.M = (int)s.T; g1.N = (int)s.Fs; g1.K = (int)s.h;
+    g1.A = X; g1.lda = s.h; g1.a_kcontig = true;
+    g1.B[0] = at(A, c0, s.e); g1.ldb = s.F; g1.b_kcontig = false;
+    g1.C[0] = at(saved, L.U, 1); g1.ldc = s.Fs; g1.C2 = at(saved, L.Y, 1); g1.ldc2 = s.Fs;
+    g1.bias[0] = b1 ? at(b1, c0, s.e) : nullptr;
+    g1.epi = tp::EPI_BIAS_GELU;
+    return gemm(s, g1, st, TP_STEP_MLP_UP);
+}
+
+// QKV = X [Wq|Wk|Wv][:, cols of G_i] + [bq|bk|bv], then per-head attention: O and LSE.
+hipError_t attn_fwd_saved(const Shape& s, const void* X, const void* Wq, const void* Wk, const void* Wv,
+                          const void* bq, const void* bk, const void* bv, void* saved, hipStream_t st) {
+    const AttnSaved L = attn_saved(s);
+    void* QKV = at(saved, L.QKV, 1);
+    const int64_t col0 = s.i * s.w;
+    tp::GemmDesc g;
+    g.M = (int)s.T; g.N = (int)(3 * s.w); g.K = (int)s.h;
+    g.A = X; g.lda = s.h; g.a_kcontig = true;
+    const void* W3[3] = {Wq, Wk, Wv};
+    const void* b3[3] = {bq, bk, bv};
+    for (int z = 0; z < 3; ++z) {
+        g.B[z] = at(W3[z], col0, s.e);
+        g.C[z] = at(QKV, z * s.w, s.e);
+        g.bias[z] = b3[z] ? at(b3[z], col0, s.e) : nullptr;
+    }
+    g.ldb = s.h; g.b_kcontig = false; g.bseg = (int)s.w;
+    g.ldc = 3 * s.w; g.cseg = (int)s.w;
+    g.epi = tp::EPI_BIAS;
+    hipError_t e = gemm(s, g, st, TP_STEP_QKV);
+    if (e != hipSuccess) return e;
+    tp::AttnDesc ad;
+    ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
+    ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = at(saved, L.O, 1); ad.ld_o = s.w;
+    ad.lse = static_cast<float*>(at(saved, L.LSE, 1));
+    StepTimer t(TP_STEP_ATTN_CORE, st);
+    return s.bf16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st);
+}
+
 }  // namespace
 
 namespace tp {
@@ -302,20 +347,9 @@ int tp_mlp_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, 
         (b1 && !aligned16(b1)))
         return TP_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const MlpSaved L = mlp_saved(s);
-    void* U = at(saved, L.U, 1);
-    void* Y = at(saved, L.Y, 1);
+    if (mlp_fwd_saved(s, X, A, b1, saved, st) != hipSuccess) return TP_EHIP;
+    const void* Y = at(saved, mlp_saved(s).Y, 1);
     const int64_t c0 = s.i * s.Fs;
-
-    tp::GemmDesc g1;  // U = X A[:, C_i] + b1[C_i];  Y = GeLU(U)
-    g1.M = (int)s.T; g1.N = (int)s.Fs; g1.K = (int)s.h;
-    g1.A = X; g1.lda = s.h; g1.a_kcontig = true;
-    g1.B[0] = at(A, c0, s.e); g1.ldb = s.F; g1.b_kcontig = false;
-    g1.C[0] = U; g1.ldc = s.Fs; g1.C2 = Y; g1.ldc2 = s.Fs;
-    g1.bias[0] = b1 ? at(b1, c0, s.e) : nullptr;
-    g1.epi = tp::EPI_BIAS_GELU;
-    hipError_t e = gemm(s, g1, st, TP_STEP_MLP_UP);
-    if (e != hipSuccess) return TP_EHIP;
 
     tp::GemmDesc g2;  // Z_part = Y B[C_i, :]
     g2.M = (int)s.T; g2.N = (int)s.h; g2.K = (int)s.Fs;
@@ -399,34 +433,9 @@ int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X,
         (bv && !aligned16(bv)))
         return TP_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const AttnSaved L = attn_saved(s);
-    void* QKV = at(saved, L.QKV, 1);
-    void* O = at(saved, L.O, 1);
-    float* lse = static_cast<float*>(at(saved, L.LSE, 1));
+    if (attn_fwd_saved(s, X, Wq, Wk, Wv, bq, bk, bv, saved, st) != hipSuccess) return TP_EHIP;
+    const void* O = at(saved, attn_saved(s).O, 1);
     const int64_t col0 = s.i * s.w;
-
-    tp::GemmDesc g;  // QKV = X [Wq|Wk|Wv][:, cols of G_i] + [bq|bk|bv]
-    g.M = (int)s.T; g.N = (int)(3 * s.w); g.K = (int)s.h;
-    g.A = X; g.lda = s.h; g.a_kcontig = true;
-    const void* W3[3] = {Wq, Wk, Wv};
-    const void* b3[3] = {bq, bk, bv};
-    for (int z = 0; z < 3; ++z) {
-        g.B[z] = at(W3[z], col0, s.e);
-        g.C[z] = at(QKV, z * s.w, s.e);
-        g.bias[z] = b3[z] ? at(b3[z], col0, s.e) : nullptr;
-    }
-    g.ldb = s.h; g.b_kcontig = false; g.bseg = (int)s.w;
-    g.ldc = 3 * s.w; g.cseg = (int)s.w;
-    g.epi = tp::EPI_BIAS;
-    if (gemm(s, g, st, TP_STEP_QKV) != hipSuccess) return TP_EHIP;
-
-    tp::AttnDesc ad;
-    ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
-    ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = O; ad.ld_o = s.w; ad.lse = lse;
-    {
-        StepTimer t(TP_STEP_ATTN_CORE, st);
-        if ((s.bf16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st)) != hipSuccess) return TP_EHIP;
-    }
 
     tp::GemmDesc go;  // Z_part = O Wo[rows of G_i, :]
     go.M = (int)s.T; go.N = (int)s.h; go.K = (int)s.w;
@@ -539,6 +548,55 @@ int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* pa
     if (!aligned16(out) || (bias && !aligned16(bias))) return TP_EALIGN;
     return hip_status(tp::sum_partials(dtype == TP_BF16, rows, cols, parts, nparts, bias, out,
                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t tp_mlp_recompute_work_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)(mlp_saved(s).total + mlp_work(s).total) : 0;
+}
+
+size_t tp_attn_recompute_work_bytes(const tp_dims* dims, int shard, int degree) {
+    Shape s;
+    return derive(dims, shard, degree, &s) == TP_OK ? (size_t)(attn_saved(s).total + attn_work(s).total) : 0;
+}
+
+int tp_mlp_shard_bwd_recompute(const tp_dims* dims, int shard, int degree, const void* X, const void* A,
+                               const void* b1, const void* B, const void* dZ, void* dX_part, float* dA, float* db1,
+                               float* dB, void* work, size_t work_bytes, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !A || !B || !dZ || !dX_part || !dA || !dB || !work) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dZ) || !aligned16(dX_part) ||
+        !aligned16(dA) || !aligned16(dB) || !aligned16(work) || (db1 && !aligned16(db1)) || (b1 && !aligned16(b1)))
+        return TP_EALIGN;
+    const int64_t sv = mlp_saved(s).total;
+    if (work_bytes < (size_t)(sv + mlp_work(s).total)) return TP_ESIZE;
+    if (mlp_fwd_saved(s, X, A, b1, work, static_cast<hipStream_t>(stream)) != hipSuccess) return TP_EHIP;
+    return tp_mlp_shard_bwd(dims, shard, degree, X, A, B, work, dZ, dX_part, dA, db1, dB, at(work, sv, 1),
+                            work_bytes - (size_t)sv, stream);
+}
+
+int tp_attn_shard_bwd_recompute(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq,
+                                const void* Wk, const void* Wv, const void* bq, const void* bk, const void* bv,
+                                const void* Wo, const void* dZ, void* dX_part, float* dWq, float* dWk, float* dWv,
+                                float* dbq, float* dbk, float* dbv, float* dWo, void* work, size_t work_bytes,
+                                void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if (!X || !Wq || !Wk || !Wv || !Wo || !dZ || !dX_part || !dWq || !dWk || !dWv || !dWo || !work) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) || !aligned16(Wo) || !aligned16(dZ) ||
+        !aligned16(dX_part) || !aligned16(dWq) || !aligned16(dWk) || !aligned16(dWv) || !aligned16(dWo) ||
+        !aligned16(work) || (bq && !aligned16(bq)) || (bk && !aligned16(bk)) || (bv && !aligned16(bv)) ||
+        (dbq && !aligned16(dbq)) || (dbk && !aligned16(dbk)) || (dbv && !aligned16(dbv)))
+        return TP_EALIGN;
+    const int64_t sv = attn_saved(s).total;
+    if (work_bytes < (size_t)(sv + attn_work(s).total)) return TP_ESIZE;
+    if (attn_fwd_saved(s, X, Wq, Wk, Wv, bq, bk, bv, work, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TP_EHIP;
+    return tp_attn_shard_bwd(dims, shard, degree, X, Wq, Wk, Wv, Wo, work, dZ, dX_part, dWq, dWk, dWv, dbq, dbk,
+                             dbv, dWo, at(work, sv, 1), work_bytes - (size_t)sv, stream);
 }
 
 namespace {

@@ -14,7 +14,8 @@ from .configs import LayerConfig
 
 
 class ShardRun:
-    def __init__(self, cfg: LayerConfig, inputs: dict, device="cuda", degree=None, shards=None):
+    def __init__(self, cfg: LayerConfig, inputs: dict, device="cuda", degree=None, shards=None,
+                 recompute=False):
         self.cfg = cfg
         self.degree = cfg.degree if degree is None else degree
         self.dims = tp.dims_of(cfg)
@@ -39,6 +40,9 @@ class ShardRun:
                 "attn_saved": torch.empty(tp.tp_attn_saved_bytes(d, i, t), **u8),
                 "mlp_work": torch.empty(tp.tp_mlp_work_bytes(d, i, t), **u8),
                 "attn_work": torch.empty(tp.tp_attn_work_bytes(d, i, t), **u8),
+                # the recompute backward's work: saved layout + backward work
+                "mlp_rwork": torch.empty(tp.tp_mlp_recompute_work_bytes(d, i, t) if recompute else 0, **u8),
+                "attn_rwork": torch.empty(tp.tp_attn_recompute_work_bytes(d, i, t) if recompute else 0, **u8),
                 "Z_mlp": torch.empty((T, h), dtype=self.dt, device=self.dev),
                 "Z_attn": torch.empty((T, h), dtype=self.dt, device=self.dev),
                 "dX_mlp": torch.empty((T, h), dtype=self.dt, device=self.dev),
@@ -67,11 +71,27 @@ class ShardRun:
                              b["attn_saved"], x["dZ"], b["dX_attn"], g["dWq"], g["dWk"], g["dWv"], g["dbq"],
                              g["dbk"], g["dbv"], g["dWo"], b["attn_work"], stream)
 
-    def step(self, i, backward=True, stream=None):
-        """One pass of the shard's hot path: forward of both sublayers, then backward."""
+    def mlp_bwd_recompute(self, i, stream=None):
+        x, b, g = self.x, self.buf[i], self.grads
+        tp.tp_mlp_shard_bwd_recompute(self.dims, i, self.degree, x["X"], x["A"], x.get("b1"), x["B"], x["dZ"],
+                                      b["dX_mlp"], g["dA"], g["db1"], g["dB"], b["mlp_rwork"], stream)
+
+    def attn_bwd_recompute(self, i, stream=None):
+        x, b, g = self.x, self.buf[i], self.grads
+        tp.tp_attn_shard_bwd_recompute(self.dims, i, self.degree, x["X"], x["Wq"], x["Wk"], x["Wv"], x.get("bq"),
+                                       x.get("bk"), x.get("bv"), x["Wo"], x["dZ"], b["dX_attn"], g["dWq"],
+                                       g["dWk"], g["dWv"], g["dbq"], g["dbk"], g["dbv"], g["dWo"],
+                                       b["attn_rwork"], stream)
+
+    def step(self, i, backward=True, stream=None, recompute=False):
+        """One pass of the shard's hot path: forward of both sublayers, then backward (with
+        recompute, the backward rebuilds the forward's activations instead of reading them)."""
         self.mlp_fwd(i, stream)
         self.attn_fwd(i, stream)
-        if backward:
+        if backward and recompute:
+            self.mlp_bwd_recompute(i, stream)
+            self.attn_bwd_recompute(i, stream)
+        elif backward:
             self.mlp_bwd(i, stream)
             self.attn_bwd(i, stream)
 

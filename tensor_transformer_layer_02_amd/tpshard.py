@@ -23,7 +23,8 @@ EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_byte
            "tp_mlp_work_bytes", "tp_attn_work_bytes", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
            "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_sum_partials", "tp_profile_enable",
            "tp_profile_count", "tp_profile_kernels", "tp_residual_layernorm", "tp_layernorm_bwd_work_bytes",
-           "tp_layernorm_bwd"]
+           "tp_layernorm_bwd", "tp_mlp_recompute_work_bytes", "tp_attn_recompute_work_bytes",
+           "tp_mlp_shard_bwd_recompute", "tp_attn_shard_bwd_recompute"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
@@ -60,7 +61,8 @@ def lib() -> ctypes.CDLL:
         L.tp_status_string.restype = ctypes.c_char_p
         L.tp_status_string.argtypes = [i32]
         L.tp_check_dims.argtypes = [D, i32, i32]
-        for n in ("tp_mlp_saved_bytes", "tp_attn_saved_bytes", "tp_mlp_work_bytes", "tp_attn_work_bytes"):
+        for n in ("tp_mlp_saved_bytes", "tp_attn_saved_bytes", "tp_mlp_work_bytes", "tp_attn_work_bytes",
+                  "tp_mlp_recompute_work_bytes", "tp_attn_recompute_work_bytes"):
             getattr(L, n).restype = sz
             getattr(L, n).argtypes = [D, i32, i32]
         L.tp_mlp_shard_fwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -69,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_shard_bwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp,
                                         vp, sz, vp]
         L.tp_sum_partials.argtypes = [i32, i64, i64, ctypes.POINTER(vp), i32, vp, fp, vp]
+        L.tp_mlp_shard_bwd_recompute.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+        L.tp_attn_shard_bwd_recompute.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, fp, fp, fp,
+                                                  fp, fp, fp, fp, vp, sz, vp]
         L.tp_profile_enable.argtypes = [ctypes.POINTER(vp), i32]
         L.tp_profile_count.argtypes = [i32]
         L.tp_profile_kernels.argtypes = [i32]
@@ -166,6 +171,29 @@ def tp_attn_shard_bwd(dims, shard, degree, X, Wq, Wk, Wv, Wo, saved, dZ, dX_part
     return _call("tp_attn_shard_bwd", ctypes.byref(dims), shard, degree, _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv),
                  _ptr(Wo), _ptr(saved), _ptr(dZ), _ptr(dX_part), _ptr(dWq), _ptr(dWk), _ptr(dWv), _ptr(dbq),
                  _ptr(dbk), _ptr(dbv), _ptr(dWo), _ptr(work), nbytes, _stream(stream))
+
+
+def tp_mlp_recompute_work_bytes(dims, shard, degree) -> int:
+    return lib().tp_mlp_recompute_work_bytes(ctypes.byref(dims), shard, degree)
+
+
+def tp_attn_recompute_work_bytes(dims, shard, degree) -> int:
+    return lib().tp_attn_recompute_work_bytes(ctypes.byref(dims), shard, degree)
+
+
+def tp_mlp_shard_bwd_recompute(dims, shard, degree, X, A, b1, B, dZ, dX_part, dA, db1, dB, work, stream=None):
+    nbytes = work.numel() * work.element_size() if hasattr(work, "numel") else 0
+    return _call("tp_mlp_shard_bwd_recompute", ctypes.byref(dims), shard, degree, _ptr(X), _ptr(A), _ptr(b1),
+                 _ptr(B), _ptr(dZ), _ptr(dX_part), _ptr(dA), _ptr(db1), _ptr(dB), _ptr(work), nbytes,
+                 _stream(stream))
+
+
+def tp_attn_shard_bwd_recompute(dims, shard, degree, X, Wq, Wk, Wv, bq, bk, bv, Wo, dZ, dX_part, dWq, dWk, dWv,
+                                dbq, dbk, dbv, dWo, work, stream=None):
+    nbytes = work.numel() * work.element_size() if hasattr(work, "numel") else 0
+    return _call("tp_attn_shard_bwd_recompute", ctypes.byref(dims), shard, degree, _ptr(X), _ptr(Wq), _ptr(Wk),
+                 _ptr(Wv), _ptr(bq), _ptr(bk), _ptr(bv), _ptr(Wo), _ptr(dZ), _ptr(dX_part), _ptr(dWq), _ptr(dWk),
+                 _ptr(dWv), _ptr(dbq), _ptr(dbk), _ptr(dbv), _ptr(dWo), _ptr(work), nbytes, _stream(stream))
 
 
 def tp_sum_partials(dtype, rows, cols, parts, bias, out, stream=None):
