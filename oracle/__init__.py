@@ -33,7 +33,8 @@ def build(force: bool = True) -> str:
 
 class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_long), ("seq", ctypes.c_long), ("hidden", ctypes.c_long),
-                ("heads", ctypes.c_long), ("ffn", ctypes.c_long), ("causal", ctypes.c_int)]
+                ("heads", ctypes.c_long), ("ffn", ctypes.c_long), ("causal", ctypes.c_int),
+                ("gelu", ctypes.c_int)]
 
 
 _lib = None
@@ -68,7 +69,7 @@ def _f64(a):
 
 
 def _dims(d: dict) -> Dims:
-    return Dims(d["batch"], d["seq"], d["hidden"], d["heads"], d["ffn"], int(d["causal"]))
+    return Dims(d["batch"], d["seq"], d["hidden"], d["heads"], d["ffn"], int(d["causal"]), int(d.get("gelu", 0)))
 
 
 def _check(rc, name):
@@ -91,6 +92,20 @@ def gelu_prime(u):
     u = _f64(u)
     y = np.empty_like(u)
     lib().tpo_gelu_prime(_p(u), _p(y), ctypes.c_long(u.size))
+    return y
+
+
+def gelu_tanh(u):
+    u = _f64(u)
+    y = np.empty_like(u)
+    lib().tpo_gelu_tanh(_p(u), _p(y), ctypes.c_long(u.size))
+    return y
+
+
+def gelu_tanh_prime(u):
+    u = _f64(u)
+    y = np.empty_like(u)
+    lib().tpo_gelu_tanh_prime(_p(u), _p(y), ctypes.c_long(u.size))
     return y
 
 

@@ -49,6 +49,37 @@ static double gelu_prime(double u)
     return Phi + u * phi;
 }
 
+/* The tanh approximation of GeLU (selected by tpo_dims.gelu = 1):
+ * 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3), and its derivative
+ * by the chain rule, 0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) dz/du. */
+static double gelu_tanh(double u)
+{
+    const double z = sqrt(2.0 / acos(-1.0)) * (u + 0.044715 * u * u * u);
+    return 0.5 * u * (1.0 + tanh(z));
+}
+
+static double gelu_tanh_prime(double u)
+{
+    const double c = sqrt(2.0 / acos(-1.0));
+    const double th = tanh(c * (u + 0.044715 * u * u * u));
+    const double dz = c * (1.0 + 3.0 * 0.044715 * u * u);
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * dz;
+}
+
+/* The FFN activation and its derivative for the form d->gelu selects. */
+static double act(const tpo_dims* d, double u) { return d->gelu ? gelu_tanh(u) : gelu(u); }
+static double act_prime(const tpo_dims* d, double u) { return d->gelu ? gelu_tanh_prime(u) : gelu_prime(u); }
+
+void tpo_gelu_tanh(const double* u, double* y, long n)
+{
+    for (long i = 0; i < n; ++i) y[i] = gelu_tanh(u[i]);
+}
+
+void tpo_gelu_tanh_prime(const double* u, double* g, long n)
+{
+    for (long i = 0; i < n; ++i) g[i] = gelu_tanh_prime(u[i]);
+}
+
 void tpo_gelu(const double* u, double* y, long n)
 {
     for (long i = 0; i < n; ++i) y[i] = gelu(u[i]);
@@ -101,7 +132,7 @@ int tpo_mlp_shard_fwd(const tpo_dims* d, int shard, int degree,
                 const double* a = A + k * F + c0;
                 for (long c = 0; c < Fs; ++c) u[c] += x * a[c];
             }
-            for (long c = 0; c < Fs; ++c) y[c] = gelu(u[c]);
+            for (long c = 0; c < Fs; ++c) y[c] = act(d, u[c]);
             if (U) memcpy(U + r * Fs, u, (size_t)Fs * sizeof(double));
             if (Y) memcpy(Y + r * Fs, y, (size_t)Fs * sizeof(double));
             /* Z_part[r, n] = sum_c Y[r, c] B[c0 + c, n] */
@@ -145,7 +176,7 @@ int tpo_mlp_shard_bwd(const tpo_dims* d, int shard, int degree,
             const double* b = B + (c0 + c) * h;
             double s = 0.0;
             for (long n = 0; n < h; ++n) s += g[n] * b[n];
-            dU[r * Fs + c] = s * gelu_prime(U[r * Fs + c]);
+            dU[r * Fs + c] = s * act_prime(d, U[r * Fs + c]);
         }
     }
 
@@ -487,7 +518,7 @@ int tpo_mlp_full_fwd(const tpo_dims* d, const double* X, const double* A, const 
     double* H1 = zalloc(T * F);
     mm(T, F, h, X, h, 0, A, F, 0, H1, F);
     for (long r = 0; r < T; ++r)
-        for (long c = 0; c < F; ++c) H1[r * F + c] = gelu(H1[r * F + c] + (b1 ? b1[c] : 0.0));
+        for (long c = 0; c < F; ++c) H1[r * F + c] = act(d, H1[r * F + c] + (b1 ? b1[c] : 0.0));
     mm(T, h, F, H1, F, 0, B, h, 0, Z, h);
     if (b2)
         for (long r = 0; r < T; ++r)
@@ -510,11 +541,11 @@ int tpo_mlp_full_bwd(const tpo_dims* d, const double* X, const double* A, const 
     for (long r = 0; r < T; ++r)
         for (long c = 0; c < F; ++c) {
             Pre[r * F + c] += b1 ? b1[c] : 0.0;
-            Act[r * F + c] = gelu(Pre[r * F + c]);
+            Act[r * F + c] = act(d, Pre[r * F + c]);
         }
     mm(F, h, T, Act, F, 1, G, h, 0, dB, h);          /* dB = Act^T G */
     mm(T, F, h, G, h, 0, B, h, 1, dAct, F);          /* dAct = G B^T */
-    for (long i = 0; i < T * F; ++i) dAct[i] *= gelu_prime(Pre[i]);
+    for (long i = 0; i < T * F; ++i) dAct[i] *= act_prime(d, Pre[i]);
     mm(h, F, T, X, h, 1, dAct, F, 0, dA, F);         /* dA = X^T dPre */
     mm(T, h, F, dAct, F, 0, A, F, 1, dX, h);         /* dX = dPre A^T */
     if (db1)

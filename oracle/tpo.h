@@ -35,11 +35,15 @@ extern "C" {
 typedef struct {
     long batch, seq, hidden, heads, ffn;
     int causal; /* 1: key m allowed for query j iff m <= j; 0: all keys */
+    int gelu;   /* FFN activation: 0 the exact GeLU u * Phi(u), 1 its tanh approximation */
 } tpo_dims;
 
 /* GeLU(u) = u * Phi(u) and its derivative Phi(u) + u * phi(u), elementwise. */
 void tpo_gelu(const double* u, double* y, long n);
 void tpo_gelu_prime(const double* u, double* g, long n);
+/* The tanh approximation 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) and its derivative. */
+void tpo_gelu_tanh(const double* u, double* y, long n);
+void tpo_gelu_tanh_prime(const double* u, double* g, long n);
 
 /* ---- FFN (MLP) shard -------------------------------------------------- */
 /* X [T,h], A [h,F], b1 [F] or NULL, B [F,h].

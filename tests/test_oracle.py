@@ -81,9 +81,29 @@ def test_gelu_matches_torch_library(oracle_lib):
     np.testing.assert_allclose(oracle.gelu_prime(x.detach().numpy()), gy.numpy(), rtol=1e-13, atol=1e-14)
 
 
+def test_gelu_tanh_form_identities_and_library(oracle_lib):
+    """The tanh approximation (tpo_dims.gelu = 1): closed-form facts and torch's
+    gelu(approximate='tanh') with autograd (library), derivative vs central differences."""
+    x = np.linspace(-8, 8, 1601)
+    g = oracle.gelu_tanh(x)
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(g - oracle.gelu_tanh(-x), x, atol=1e-14)  # tanh is odd
+    assert abs(oracle.gelu_tanh_prime(np.array([0.0]))[0] - 0.5) < 1e-15
+    xt = torch.tensor(x, requires_grad=True)
+    yt = torch.nn.functional.gelu(xt, approximate="tanh")
+    (gy,) = torch.autograd.grad(yt.sum(), xt)
+    np.testing.assert_allclose(g, yt.detach().numpy(), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(oracle.gelu_tanh_prime(x), gy.numpy(), rtol=1e-13, atol=1e-14)
+    e = 1e-6
+    np.testing.assert_allclose(oracle.gelu_tanh_prime(x), (oracle.gelu_tanh(x + e) - oracle.gelu_tanh(x - e)) / (2 * e),
+                               atol=1e-8)
+    # the two forms are different functions (by up to ~1e-3)
+    assert 1e-4 < np.max(np.abs(g - oracle.gelu(x))) < 1e-2
+
+
 # --------------------------------------------------- torch CPU float64 reference
 
-def torch_mlp_shard(p, i, t, requires_grad=True):
+def torch_mlp_shard(p, i, t, requires_grad=True, approximate="none"):
     """Library-routine reference: torch float64, autograd for the gradients."""
     F = p["A"].shape[1]
     Fs = F // t
@@ -93,7 +113,7 @@ def torch_mlp_shard(p, i, t, requires_grad=True):
     b1 = torch.tensor(p["b1"], requires_grad=requires_grad)
     B = torch.tensor(p["B"], requires_grad=requires_grad)
     U = X @ A[:, sl] + b1[sl]
-    Y = torch.nn.functional.gelu(U, approximate="none")
+    Y = torch.nn.functional.gelu(U, approximate=approximate)
     Z = Y @ B[sl, :]
     return Z, U, Y, (X, A, b1, B)
 
@@ -344,6 +364,37 @@ def test_numpy_einsum_brute_force_forward(oracle_lib):
             Za += o @ p["Wo"][c, :]
         args = [p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")]
         assert relerr(oracle.attn_shard_fwd(d, i, t, *args)["Z"], Za) < 1e-14
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_mlp_shard_tanh_gelu_matches_torch_and_sums(oracle_lib, t):
+    rng = np.random.default_rng(40 + t)
+    b, s, h, H, F = 2, 3, 8, 4, 32
+    d = {**dims(b, s, h, H, F, True), "gelu": 1}
+    p = rand_params(rng, b * s, h, F)
+    Zsum = np.zeros((b * s, h))
+    grads = {}
+    dXsum = np.zeros((b * s, h))
+    for i in range(t):
+        o = oracle.mlp_shard_fwd(d, i, t, p["X"], p["A"], p["b1"], p["B"])
+        Z, U, Y, (X, A, b1, B) = torch_mlp_shard(p, i, t, approximate="tanh")
+        assert relerr(o["Z"], Z.detach()) < 1e-13 and relerr(o["Y"], Y.detach()) < 1e-13
+        gX, gA, gb1, gB = torch.autograd.grad((Z * torch.tensor(p["G"])).sum(), (X, A, b1, B))
+        r = oracle.mlp_shard_bwd(d, i, t, p["X"], p["A"], p["b1"], p["B"], p["G"],
+                                 grads.get("dA"), grads.get("db1"), grads.get("dB"))
+        grads.update(dA=r["dA"], db1=r["db1"], dB=r["dB"])
+        assert relerr(r["dX"], gX) < 1e-12
+        Zsum += o["Z"]
+        dXsum += r["dX"]
+    # partials sum to the unsharded tanh-form FFN; gradient blocks tile the unsharded ones
+    full = oracle.mlp_full_fwd(d, p["X"], p["A"], p["b1"], p["B"], p["b2"])
+    assert relerr(Zsum + p["b2"][None, :], full) < 1e-13
+    fb = oracle.mlp_full_bwd(d, p["X"], p["A"], p["b1"], p["B"], p["G"])
+    for k in ("dA", "db1", "dB"):
+        assert relerr(grads[k], fb[k]) < 1e-12, k
+    assert relerr(dXsum, fb["dX"]) < 1e-12
+    # and the tanh-form results differ from the erf-form ones
+    assert relerr(oracle.mlp_full_fwd({**d, "gelu": 0}, p["X"], p["A"], p["b1"], p["B"], p["b2"]), full) > 1e-6
 
 
 # --------------------------------------------------------- LN composition
