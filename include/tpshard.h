@@ -77,7 +77,7 @@ extern "C" {
 
 typedef enum {
     TP_OK = 0,
-    TP_EINVAL = 1,        /* NULL required pointer, non-positive size, NULL dims      */
+    TP_EINVAL = 1,        /* NULL required pointer, non-positive size, NULL dims, bad flag */
     TP_EDIVIDE = 2,       /* t does not divide H or F, or H does not divide h         */
     TP_ESHARD = 3,        /* shard index outside [0, t) or t < 1                      */
     TP_EALIGN = 4,        /* pointer not 16-byte aligned or size not a multiple of 8  */
@@ -89,6 +89,11 @@ typedef enum {
 
 typedef enum { TP_FP32 = 0, TP_BF16 = 1 } tp_dtype;
 
+/* GeLU form of the FFN shard.  The pages name only "GeLU"; the default is the
+ * exact u * Phi(u) (erf form).  TP_GELU_TANH selects the tanh approximation
+ * 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) and its derivative. */
+typedef enum { TP_GELU_ERF = 0, TP_GELU_TANH = 1 } tp_gelu;
+
 typedef struct {
     int64_t batch, seq;      /* T = batch * seq tokens                         */
     int64_t hidden;          /* h                                              */
@@ -96,6 +101,7 @@ typedef struct {
     int64_t ffn;             /* F (full, unsharded; 4h in the pages' models)   */
     int32_t causal;          /* 1: causal mask, 0: none                        */
     int32_t act;             /* tp_dtype of activations / weights / partials   */
+    int32_t gelu;            /* tp_gelu (0, the erf form, when zero-filled)    */
 } tp_dims;
 
 /* Library version (major * 10000 + minor * 100 + patch). */

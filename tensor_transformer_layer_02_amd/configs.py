@@ -31,6 +31,7 @@ class LayerConfig:
     dtype: str          # "fp32" or "bf16"
     backward: bool      # whether the workload includes the backward pass
     note: str = ""
+    gelu: str = "erf"   # GeLU form of the FFN: "erf" (exact, the default) or "tanh"
 
     @property
     def tokens(self) -> int:
@@ -55,7 +56,8 @@ class LayerConfig:
 
     def dims(self) -> dict:
         return dict(batch=self.batch, seq=self.seq, hidden=self.hidden,
-                    heads=self.heads, ffn=self.ffn, causal=int(self.causal))
+                    heads=self.heads, ffn=self.ffn, causal=int(self.causal),
+                    gelu=int(self.gelu == "tanh"))
 
     def with_(self, **kw) -> "LayerConfig":
         d = dict(self.__dict__)

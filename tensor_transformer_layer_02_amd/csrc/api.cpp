@@ -35,6 +35,7 @@ constexpr int SEG_NONE = 1 << 30;
 struct Shape {
     int64_t T, b, s, h, H, F, t, i, Fs, Hs, d, w;
     bool causal, bf16;
+    bool gelu_tanh;  // dims.gelu == TP_GELU_TANH
     int64_t e;  // bytes per element of dims.act
 };
 
@@ -44,6 +45,7 @@ int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     if (dims->batch <= 0 || dims->seq <= 0 || dims->hidden <= 0 || dims->heads <= 0 || dims->ffn <= 0)
         return TP_EINVAL;
     if (dims->causal != 0 && dims->causal != 1) return TP_EINVAL;
+    if (dims->gelu != TP_GELU_ERF && dims->gelu != TP_GELU_TANH) return TP_EINVAL;
     if (degree < 1 || shard < 0 || shard >= degree) return TP_ESHARD;
     if (dims->hidden % dims->heads) return TP_EDIVIDE;
     if (dims->heads % degree || dims->ffn % degree) return TP_EDIVIDE;
@@ -53,6 +55,7 @@ int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     s.t = degree; s.i = shard;
     s.Fs = s.F / degree; s.Hs = s.H / degree; s.d = s.h / s.H; s.w = s.Hs * s.d;
     s.causal = dims->causal != 0;
+    s.gelu_tanh = dims->gelu == TP_GELU_TANH;
     s.bf16 = dims->act == TP_BF16;
     s.e = s.bf16 ? 2 : 4;
     if (s.h % 8 || s.Fs % 8 || s.w % 8) return TP_EALIGN;
@@ -240,6 +243,7 @@ hipError_t mlp_fwd_saved(const Shape& s, const void* X, const void* A, const voi
     g1.C[0] = at(saved, L.U, 1); g1.ldc = s.Fs; g1.C2 = at(saved, L.Y, 1); g1.ldc2 = s.Fs;
     g1.bias[0] = b1 ? at(b1, c0, s.e) : nullptr;
     g1.epi = tp::EPI_BIAS_GELU;
+    g1.gelu_tanh = s.gelu_tanh;
     return gemm(s, g1, st, TP_STEP_MLP_UP);
 }
 
@@ -280,7 +284,7 @@ void count_launch() { ++g_launches; }
 
 extern "C" {
 
-int tp_version(void) { return 100; }
+int tp_version(void) { return 200; }
 
 const char* tp_status_string(int status) {
     switch (status) {
@@ -389,6 +393,7 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     g.B[0] = at(B, c0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
     g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
     g.epi = tp::EPI_GELU_BWD;
+    g.gelu_tanh = s.gelu_tanh;
     if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
 
     if (db1) {  // db1[C_i] = column sums of dU, on the auxiliary stream beside the GEMMs below

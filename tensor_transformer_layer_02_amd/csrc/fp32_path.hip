@@ -28,6 +28,7 @@ struct GemmArgsF {
     const float* bias[3];
     const float* aux;
     int64_t ldaux;
+    int gelu_tanh;
 };
 
 __device__ __forceinline__ float ldA(const GemmArgsF& p, int m, int k) {
@@ -92,9 +93,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmArgsF p) {
             } else if constexpr (EPI == EPI_BIAS_GELU) {
                 const float u = v + (p.bias[sg] ? p.bias[sg][nl] : 0.f);
                 *c = u;
-                p.C2[(int64_t)m * p.ldc2 + nl] = gelu_f(u);
+                p.C2[(int64_t)m * p.ldc2 + nl] = gelu_sel(u, p.gelu_tanh != 0);
             } else {
-                *c = v * gelu_prime_f(p.aux[(int64_t)m * p.ldaux + nl]);
+                *c = v * gelu_prime_sel(p.aux[(int64_t)m * p.ldaux + nl], p.gelu_tanh != 0);
             }
         }
     }
@@ -366,6 +367,7 @@ hipError_t gemm_f32(const GemmDesc& d, hipStream_t s) {
     p.ldc = d.ldc; p.cseg = d.cseg;
     p.C2 = static_cast<float*>(d.C2); p.ldc2 = d.ldc2;
     p.aux = static_cast<const float*>(d.aux); p.ldaux = d.ldaux;
+    p.gelu_tanh = d.gelu_tanh ? 1 : 0;
     dim3 grid((d.N + 63) / 64, (d.M + 63) / 64);
     switch (d.epi) {
         case EPI_STORE: hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, dim3(256), 0, s, p); break;

@@ -75,6 +75,7 @@ struct GemmArgs {
     const bf16_t* bias[3];
     const bf16_t* aux;
     int64_t ldaux;
+    int gelu_tanh;
 };
 
 // Up to two independent problems of the same layout and epilogue in one
@@ -505,7 +506,7 @@ constexpr int tile_occupancy() {
 // number of 8-byte pairs) puts the 32 rows of a half-wave on distinct banks.
 template <int FM, int FN, int WTM, int WTN, int SP, bool GELU>
 __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN], const bf16_t* bias, int ncols,
-                                           int wm, int wn, int lane) {
+                                           int wm, int wn, int lane, bool tanh_form = false) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -525,7 +526,7 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[i][j][4 * q + e] + b4[e];
-                    if constexpr (GELU) v[e] = gelu_f(v[e]);
+                    if constexpr (GELU) v[e] = gelu_sel(v[e], tanh_form);
                 }
                 const u32x2 o = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
                 *reinterpret_cast<u32x2*>(st + (wm * WTM + i * 32 + (lane & 31)) * SP + nl * 2) = o;
@@ -601,7 +602,7 @@ __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kern
         store_bf16<BM, BN, SP>(smem, C, p.ldc, rows, ncols, tid);
         if constexpr (EPI == EPI_BIAS_GELU) {
             __syncthreads();
-            stage_bf16<FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane);
+            stage_bf16<FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane, p.gelu_tanh != 0);
             __syncthreads();
             store_bf16<BM, BN, SP>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
         }
@@ -648,8 +649,8 @@ __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kern
                     const u32x4 uw = *reinterpret_cast<const u32x4*>(p.aux + (int64_t)m * p.ldaux + nl);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        v[2 * q] *= gelu_prime_f(__uint_as_float(uw[q] << 16));
-                        v[2 * q + 1] *= gelu_prime_f(__uint_as_float(uw[q] & 0xffff0000u));
+                        v[2 * q] *= gelu_prime_sel(__uint_as_float(uw[q] << 16), p.gelu_tanh != 0);
+                        v[2 * q + 1] *= gelu_prime_sel(__uint_as_float(uw[q] & 0xffff0000u), p.gelu_tanh != 0);
                     }
                     u32x4 o;
 #pragma unroll
@@ -741,6 +742,7 @@ GemmArgs make_args(const GemmDesc& d) {
     a.ldb = d.ldb; a.bseg = d.bseg; a.ldc = d.ldc; a.cseg = d.cseg;
     a.C2 = static_cast<bf16_t*>(d.C2); a.ldc2 = d.ldc2;
     a.aux = static_cast<const bf16_t*>(d.aux); a.ldaux = d.ldaux;
+    a.gelu_tanh = d.gelu_tanh ? 1 : 0;
     return a;
 }
 

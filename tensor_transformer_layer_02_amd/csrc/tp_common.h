@@ -58,6 +58,29 @@ __device__ __forceinline__ float gelu_prime_f(float u) {
     return fmaf(u, pdf, Phi);
 }
 
+// The tanh approximation of GeLU, 0.5 u (1 + tanh(z)) with z = c (u + a u^3),
+// c = sqrt(2/pi), a = 0.044715, evaluated through 1 + tanh(z) = 2 s, s = 1/(1 + e^(-2z))
+// (hardware exp2 and reciprocal): GeLU = u s, with no cancellation where tanh(z)
+// nears -1 (the limits come out exactly: e^(-2z) -> inf gives s = 0, -> 0 gives s = 1).
+__device__ __forceinline__ float gelu_tanh_s(float u) {
+    const float z = 0.7978845608028654f * fmaf(0.044715f * u, u * u, u);
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * z));  // 2 log2(e)
+}
+
+__device__ __forceinline__ float gelu_tanh_f(float u) { return u * gelu_tanh_s(u); }
+
+// Its derivative: s + u * 2 s (1 - s) * dz/du, dz/du = c (1 + 3 a u^2).
+__device__ __forceinline__ float gelu_tanh_prime_f(float u) {
+    const float sg = gelu_tanh_s(u);
+    const float dz = 0.7978845608028654f * fmaf(0.134145f * u, u, 1.0f);
+    return fmaf(2.0f * u * sg * (1.0f - sg), dz, sg);
+}
+
+__device__ __forceinline__ float gelu_sel(float u, bool tanh_form) { return tanh_form ? gelu_tanh_f(u) : gelu_f(u); }
+__device__ __forceinline__ float gelu_prime_sel(float u, bool tanh_form) {
+    return tanh_form ? gelu_tanh_prime_f(u) : gelu_prime_f(u);
+}
+
 // Bit-level reinterpretations between 16-byte vector types.
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

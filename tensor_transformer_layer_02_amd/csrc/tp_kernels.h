@@ -44,6 +44,7 @@ struct GemmDesc {
     const void* aux = nullptr;    // U of EPI_GELU_BWD
     int64_t ldaux = 0;
     int epi = EPI_STORE;
+    bool gelu_tanh = false;       // EPI_BIAS_GELU / EPI_GELU_BWD: the tanh form of GeLU
 };
 
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.

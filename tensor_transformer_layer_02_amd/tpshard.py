@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtpshard.so")
 
 TP_FP32, TP_BF16 = 0, 1
+TP_GELU_ERF, TP_GELU_TANH = 0, 1
 STATUS = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_EDIVIDE", 3: "TP_ESHARD", 4: "TP_EALIGN", 5: "TP_EDTYPE",
           6: "TP_EUNSUPPORTED", 7: "TP_EHIP", 8: "TP_ESIZE"}
 
@@ -40,7 +41,7 @@ class TpError(RuntimeError):
 class tp_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("heads", ctypes.c_int64), ("ffn", ctypes.c_int64), ("causal", ctypes.c_int32),
-                ("act", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("gelu", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,14 +89,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def make_dims(batch, seq, hidden, heads, ffn, causal=True, act=TP_BF16) -> tp_dims:
-    return tp_dims(batch, seq, hidden, heads, ffn, int(bool(causal)), int(act))
+def make_dims(batch, seq, hidden, heads, ffn, causal=True, act=TP_BF16, gelu=TP_GELU_ERF) -> tp_dims:
+    return tp_dims(batch, seq, hidden, heads, ffn, int(bool(causal)), int(act), int(gelu))
 
 
 def dims_of(cfg, act=None) -> tp_dims:
     if act is None:
         act = TP_FP32 if cfg.dtype == "fp32" else TP_BF16
-    return make_dims(cfg.batch, cfg.seq, cfg.hidden, cfg.heads, cfg.ffn, cfg.causal, act)
+    gelu = TP_GELU_TANH if getattr(cfg, "gelu", "erf") == "tanh" else TP_GELU_ERF
+    return make_dims(cfg.batch, cfg.seq, cfg.hidden, cfg.heads, cfg.ffn, cfg.causal, act, gelu)
 
 
 def _ptr(t):

@@ -91,6 +91,17 @@ def test_small_bf16_all_shards(case):
     _say(f"[{name}] " + "; ".join(f"{n}={e:.1e}" for n, e in report))
 
 
+@pytest.mark.parametrize("cfg", [
+    CONFIGS["tiny"].with_(cid=130, name="tiny_tanh", gelu="tanh", backward=True),
+    LayerConfig(131, "bf16_d96_tanh", 2, 130, 384, 4, 1536, 2, True, "bf16", True, gelu="tanh"),
+], ids=["tiny_fp32_tanh", "bf16_d96_tanh"])
+def test_tanh_gelu_variant_all_shards(cfg):
+    """The tanh-form GeLU variant (tp_dims.gelu = TP_GELU_TANH) against the oracle's tanh form."""
+    report = []
+    run_all_shards(cfg, 0.02, report)
+    _say(f"[{cfg.name}] " + "; ".join(f"{n}={e:.1e}" for n, e in report))
+
+
 def test_fp32_ragged_noncausal():
     cfg = LayerConfig(120, "fp32_ragged", 3, 37, 64, 8, 256, 4, False, "fp32", True)
     report = []
