@@ -11,7 +11,10 @@
 //  * 32x32x16 MFMAs: with one wave per SIMD they sustain ~86% of the bf16 peak,
 //    the 16x16x32 form only ~55% (measured on MI355X), and a 256 x 256 tile
 //    needs one wave per SIMD for its 256 accumulator registers.
-//  * A 256-thread workgroup (4 wave64s, 2x2) computes a BM x BN tile.  K
+//  * A workgroup of 4 wave64s (2x2) computes a BM x BN tile; the 256 x 192
+//    tile also comes with 8 (4x2, two waves per SIMD, which hide each
+//    other's latencies: 3-16% faster on the same tile, and picked by the
+//    cost model for most of the layer's GEMMs).  K
 //    advances in steps of 64 (full 128-byte lines of a K-contiguous row) through
 //    two LDS slots, one barrier per step; the pipeline is described at
 //    GemmCore.  Operands travel global -> registers -> LDS: buffer loads are
@@ -50,7 +53,6 @@ namespace tp {
 
 namespace {
 
-constexpr int NT = 256;
 constexpr int BK = 64;      // K elements per pipeline stage (128-byte rows)
 constexpr int STAGES = 2;   // LDS slots
 constexpr uint32_t OOB = 0x80000000u;  // voffset past any buffer: the load returns zeros
@@ -112,22 +114,22 @@ __device__ __forceinline__ int swz_mn(int k) {
         return ((k >> 1) & 1) << 2;
 }
 
-// One stage of a K-contiguous operand, [ROWS][64]: instruction q fills LDS
-// bytes [q*1024, (q+1)*1024) = rows 8q..8q+7, eight lanes per 128-byte row.
-// The per-lane source offset (relative to the stage's k0, which moves the
-// buffer base) is fixed; so is the lane's k chunk, since q = wave + 4i keeps
-// the swizzle of its rows independent of i.
-template <int ROWS>
+// One stage of a K-contiguous operand, [ROWS][64], loaded by NWV waves:
+// instruction q fills LDS bytes [q*1024, (q+1)*1024) = rows 8q..8q+7, eight
+// lanes per 128-byte row.  The per-lane source offset (relative to the stage's
+// k0, which moves the buffer base) is fixed; so is the lane's k chunk, since
+// q = wave + NWV*i keeps the swizzle of its rows independent of i.
+template <int ROWS, int NWV>
 struct KOperand {
-    static constexpr int NI = ROWS / 32;  // instructions per wave
-    static_assert(ROWS % 32 == 0, "rows must be a multiple of 32");
+    static constexpr int NI = ROWS / (8 * NWV);  // instructions per wave
+    static_assert(ROWS % (8 * NWV) == 0, "rows must be a multiple of 8 per wave");
     uint32_t off[NI];
     int koff;
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int rows_valid) {
         koff = ((lane & 7) ^ swz_k(8 * wave + (lane >> 3))) * 8;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int row = 8 * (wave + 4 * i) + (lane >> 3);
+            const int row = 8 * (wave + NWV * i) + (lane >> 3);
             off[i] = row < rows_valid ? (uint32_t)(((int64_t)row * ld + koff) * 2) : OOB;
         }
     }
@@ -142,23 +144,23 @@ struct KOperand {
     }
     __device__ __forceinline__ void store(char* dst, int wave, int lane, const u32x4 (&v)[NI]) const {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + 4 * i) * 1024 + lane * 16) = v[i];
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + NWV * i) * 1024 + lane * 16) = v[i];
     }
 };
 
-// One stage of an M/N-contiguous operand, [64][COLS] (k rows).
-template <int COLS>
+// One stage of an M/N-contiguous operand, [64][COLS] (k rows), loaded by NWV waves.
+template <int COLS, int NWV>
 struct MNOperand {
     static constexpr int ROWB = COLS * 2;
-    static constexpr int NI = COLS / 32;  // instructions per wave
-    static_assert(COLS % 32 == 0, "cols must be a multiple of 32");
+    static constexpr int NI = COLS / (8 * NWV);  // instructions per wave
+    static_assert(COLS % (8 * NWV) == 0, "cols must be a multiple of 8 per wave");
     uint32_t off[NI];
-    int o0;  // LDS byte offset of this lane's first chunk; chunk i is at o0 + 4096 i
+    int o0;  // LDS byte offset of this lane's first chunk; chunk i is at o0 + 1024 NWV i
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int cols_valid) {
         o0 = wave * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int o = o0 + 4096 * i;
+            const int o = o0 + 1024 * NWV * i;
             const int krow = o / ROWB;
             const int p = (o % ROWB) / 16;
             const int col = (p ^ swz_mn<COLS>(krow)) * 8;
@@ -170,13 +172,13 @@ struct MNOperand {
         const int klim = krem >= BK ? BK : krem;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t o = (o0 + 4096 * i) / ROWB < klim ? off[i] : OOB;
+            const uint32_t o = (o0 + 1024 * NWV * i) / ROWB < klim ? off[i] : OOB;
             v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
         }
     }
     __device__ __forceinline__ void store(char* dst, int wave, int lane, const u32x4 (&v)[NI]) const {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + 4 * i) * 1024 + lane * 16) = v[i];
+        for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + NWV * i) * 1024 + lane * 16) = v[i];
     }
 };
 
@@ -308,15 +310,15 @@ __device__ __forceinline__ void interleave() {
 // of the K range load from an empty buffer range (zeros, no memory access);
 // their stores and fragment reads are never consumed, so the steady state has
 // no branches for the scheduler to work around.
-template <int BM, int BN, bool AK, bool BKC, bool BKSEG>
+template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int NWV>
 struct GemmCore {
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int WTM = BM / 2, WTN = BN / 2;
+    static constexpr int WTM = BM / (NWV / 2), WTN = BN / 2;  // waves in NWV/2 rows x 2 columns
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be made of 32x32 blocks");
-    using LA = typename std::conditional<AK, KOperand<BM>, MNOperand<BM>>::type;
-    using LB = typename std::conditional<BKC, KOperand<BN>, MNOperand<BN>>::type;
+    using LA = typename std::conditional<AK, KOperand<BM, NWV>, MNOperand<BM, NWV>>::type;
+    using LB = typename std::conditional<BKC, KOperand<BN, NWV>, MNOperand<BN, NWV>>::type;
     using HF = Half<FM, FN>;
     static constexpr int NM = FM * FN;           // MFMAs per sub-step
     static constexpr int PRE = NM < 2 ? NM : 2;  // last-sub-step MFMAs issued before the barrier
@@ -326,7 +328,7 @@ struct GemmCore {
     // global loads run two steps ahead; the 256 x 256 tile has no room for
     // the second set (except with two plain K-contiguous operands) and loads
     // one step ahead.
-    static constexpr int NSET = (BM == 256 && BN == 256 && !(AK && BKC && !BKSEG)) ? 1 : 2;
+    static constexpr int NSET = (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG))) ? 1 : 2;
 
     char* smem;
     int lane, wave, wm, wn, nk;
@@ -495,9 +497,9 @@ struct GemmCore {
 };
 
 // Workgroups per CU a tile shape is built for (registers: 512 / occupancy per lane).
-template <int BM, int BN>
+template <int BM, int BN, int NWV>
 constexpr int tile_occupancy() {
-    return BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
+    return NWV == 8 ? 1 : BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
 }
 
 // bf16 epilogue, first half: the tile's values (plus bias, through GeLU when
@@ -536,14 +538,14 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
 
 // bf16 epilogue, second half: the LDS image to C rows m0.. (8 columns, 16
 // bytes, per thread and item; rows past M and columns past ncols skipped).
-template <int BM, int BN, int SP>
+template <int BM, int BN, int SP, int NTH>
 __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ldc, int rows, int ncols, int tid) {
     constexpr int GPR = BN / 8;  // 8-column groups per row
-    constexpr int ITEMS = BM * GPR / NT;
-    static_assert((BM * GPR) % NT == 0, "epilogue split");
+    constexpr int ITEMS = BM * GPR / NTH;
+    static_assert((BM * GPR) % NTH == 0, "epilogue split");
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int e = tid + it * NT;
+        const int e = tid + it * NTH;
         const int lr = e / GPR, cg = e % GPR;
         if (lr >= rows || cg * 8 >= ncols) continue;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16);
@@ -552,9 +554,11 @@ __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ld
     }
 }
 
-template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
-__global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kernel(const GemmBatch batch) {
-    using Core = GemmCore<BM, BN, AK, BKC, BKSEG>;
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
+__global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gemm_bf16_kernel(const GemmBatch batch) {
+    using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV>;
+    constexpr int NT = 64 * NWV;
+    constexpr int HR = NWV / 4;  // wave rows per half tile
     constexpr int RING = STAGES * Core::STAGE;
     // fp32 epilogues (weight gradients, GeLU') stage half a tile at a time as
     // fp32; the bf16 ones stage the whole tile as bf16.
@@ -599,29 +603,30 @@ __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kern
         __syncthreads();  // every wave is done with the operand ring
         stage_bf16<FM, FN, WTM, WTN, SP, false>(smem, acc, bias, ncols, wm, wn, lane);
         __syncthreads();
-        store_bf16<BM, BN, SP>(smem, C, p.ldc, rows, ncols, tid);
+        store_bf16<BM, BN, SP, NT>(smem, C, p.ldc, rows, ncols, tid);
         if constexpr (EPI == EPI_BIAS_GELU) {
             __syncthreads();
             stage_bf16<FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane, p.gelu_tanh != 0);
             __syncthreads();
-            store_bf16<BM, BN, SP>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
+            store_bf16<BM, BN, SP, NT>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
         }
     } else {
-        // fp32 staging, half a tile (the rows of wave-row wm == half) at a time,
+        // fp32 staging, half a tile (the rows of wave rows wm / HR == half) at a time,
         // 16 bytes per lane and store; every thread then handles 8 consecutive
         // columns of a row (16-byte loads of U and stores of the outputs).
         float* stage = reinterpret_cast<float*>(smem);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             __syncthreads();
-            if (wm == half) {
+            if (wm / HR == half) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<f32x4*>(stage + (i * 32 + (lane & 31)) * ELD + wn * WTN + j * 32 + 8 * q +
+                            *reinterpret_cast<f32x4*>(stage + ((wm % HR) * WTM + i * 32 + (lane & 31)) * ELD +
+                                                      wn * WTN + j * 32 + 8 * q +
                                                       4 * (lane >> 5)) =
                                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
             }
@@ -679,39 +684,40 @@ __global__ void __launch_bounds__(NT, (tile_occupancy<BM, BN>())) gemm_bf16_kern
     }
 }
 
-template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
 hipError_t launch(GemmBatch b, hipStream_t s) {
     b.tiles0 = ((b.g[0].N + BN - 1) / BN) * ((b.g[0].M + BM - 1) / BM);
     b.tiles = b.tiles0;
     if (b.n > 1) b.tiles += ((b.g[1].N + BN - 1) / BN) * ((b.g[1].M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, BKSEG, EPI, OUTF32>), dim3(b.tiles * b.ksplit), dim3(NT),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NWV, AK, BKC, BKSEG, EPI, OUTF32>), dim3(b.tiles * b.ksplit),
+                       dim3(64 * NWV),
                        0, s, b);
     count_launch();
     return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NWV>
 hipError_t dispatch(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
     const bool ak = d.a_kcontig, bk = d.b_kcontig;
     if (ak && !bk && !d.b_kseg && !d.out_f32) {
-        if (d.epi == EPI_BIAS_GELU) return launch<BM, BN, true, false, false, EPI_BIAS_GELU, false>(a, s);
-        if (d.epi == EPI_BIAS) return launch<BM, BN, true, false, false, EPI_BIAS, false>(a, s);
-        if (d.epi == EPI_STORE) return launch<BM, BN, true, false, false, EPI_STORE, false>(a, s);
+        if (d.epi == EPI_BIAS_GELU) return launch<BM, BN, NWV, true, false, false, EPI_BIAS_GELU, false>(a, s);
+        if (d.epi == EPI_BIAS) return launch<BM, BN, NWV, true, false, false, EPI_BIAS, false>(a, s);
+        if (d.epi == EPI_STORE) return launch<BM, BN, NWV, true, false, false, EPI_STORE, false>(a, s);
     } else if (ak && bk && !d.out_f32) {
-        if (d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, true, true, true, EPI_STORE, false>(a, s);
-        if (!d.b_kseg && d.epi == EPI_GELU_BWD) return launch<BM, BN, true, true, false, EPI_GELU_BWD, false>(a, s);
-        if (!d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, true, true, false, EPI_STORE, false>(a, s);
+        if (d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, true, EPI_STORE, false>(a, s);
+        if (!d.b_kseg && d.epi == EPI_GELU_BWD) return launch<BM, BN, NWV, true, true, false, EPI_GELU_BWD, false>(a, s);
+        if (!d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, false, EPI_STORE, false>(a, s);
     } else if (!ak && !bk && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE) {
-        return launch<BM, BN, false, false, false, EPI_STORE, true>(a, s);
+        return launch<BM, BN, NWV, false, false, false, EPI_STORE, true>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
 // The 192 x 192 tile serves only the fp32-output weight-gradient GEMMs.
 template <>
-hipError_t dispatch<192, 192>(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
+hipError_t dispatch<192, 192, 4>(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
     if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
-        return launch<192, 192, false, false, false, EPI_STORE, true>(a, s);
+        return launch<192, 192, 4, false, false, false, EPI_STORE, true>(a, s);
     return hipErrorInvalidValue;
 }
 
@@ -751,22 +757,25 @@ struct Cand {
     double eff;       // throughput of the shape relative to 256 x 256 (measured on MI355X)
     bool f32_tn_only;
 };
+// The last is the 256 x 192 tile with 8 waves (two per SIMD): 3-16% faster than
+// with 4 waves on the same tile in a shape sweep.
 const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
                        {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
-                       {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}};
+                       {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false}};
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
 constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
 
 hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_t s) {
     switch (c) {
-        case 0: return dispatch<256, 256>(d, b, s);
-        case 1: return dispatch<256, 192>(d, b, s);
-        case 2: return dispatch<192, 192>(d, b, s);
-        case 3: return dispatch<256, 128>(d, b, s);
-        case 4: return dispatch<128, 128>(d, b, s);
-        case 5: return dispatch<64, 192>(d, b, s);
-        case 6: return dispatch<64, 64>(d, b, s);
-        default: return dispatch<128, 192>(d, b, s);
+        case 0: return dispatch<256, 256, 4>(d, b, s);
+        case 1: return dispatch<256, 192, 4>(d, b, s);
+        case 2: return dispatch<192, 192, 4>(d, b, s);
+        case 3: return dispatch<256, 128, 4>(d, b, s);
+        case 4: return dispatch<128, 128, 4>(d, b, s);
+        case 5: return dispatch<64, 192, 4>(d, b, s);
+        case 6: return dispatch<64, 64, 4>(d, b, s);
+        case 7: return dispatch<128, 192, 4>(d, b, s);
+        default: return dispatch<256, 192, 8>(d, b, s);
     }
 }
 
