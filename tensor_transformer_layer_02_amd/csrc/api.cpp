@@ -529,6 +529,7 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
     gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
     gx.C[0] = dX_part; gx.ldc = s.h;
+    gx.concurrent = true;
     if (gemm(s, gx, aux.a->st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
 
     tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV

@@ -805,6 +805,9 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
+        // The 8-wave tile takes a whole CU's registers; beside another launch the
+        // co-resident 4-wave tiles do better (attention dX beside dWqkv: +1% per step).
+        if (c == 8 && d[0].concurrent) continue;
         bool ok = true;
         int64_t t = 0;
         for (int i = 0; i < n; ++i) {

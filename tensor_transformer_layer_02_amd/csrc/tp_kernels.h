@@ -45,6 +45,7 @@ struct GemmDesc {
     int64_t ldaux = 0;
     int epi = EPI_STORE;
     bool gelu_tanh = false;       // EPI_BIAS_GELU / EPI_GELU_BWD: the tanh form of GeLU
+    bool concurrent = false;      // runs beside another launch (tile choice: co-resident tiles)
 };
 
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
