@@ -14,7 +14,11 @@
 //  * A workgroup of 4 wave64s (2x2) computes a BM x BN tile; the 256 x 192
 //    tile also comes with 8 (4x2, two waves per SIMD, which hide each
 //    other's latencies: 3-16% faster on the same tile, and picked by the
-//    cost model for most of the layer's GEMMs).  K
+//    cost model for most of the layer's GEMMs), and the 192 x 192 fp32
+//    weight-gradient tile with 8 waves in two K groups (each group runs two
+//    of the four k16 sub-steps of every step on the shared LDS stage; the
+//    second group's sums are added into the first's at the end, in a fixed
+//    order).  K
 //    advances in steps of 64 (full 128-byte lines of a K-contiguous row) through
 //    two LDS slots, one barrier per step; the pipeline is described at
 //    GemmCore.  Operands travel global -> registers -> LDS: buffer loads are
@@ -310,11 +314,12 @@ __device__ __forceinline__ void interleave() {
 // of the K range load from an empty buffer range (zeros, no memory access);
 // their stores and fragment reads are never consumed, so the steady state has
 // no branches for the scheduler to work around.
-template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int NWV>
+template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int NWV, int KG = 1>
 struct GemmCore {
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int WTM = BM / (NWV / 2), WTN = BN / 2;  // waves in NWV/2 rows x 2 columns
+    // waves in (NWV/KG)/2 rows x 2 columns; KG groups of them split each K step
+    static constexpr int WTM = BM / (NWV / KG / 2), WTN = BN / 2;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be made of 32x32 blocks");
     using LA = typename std::conditional<AK, KOperand<BM, NWV>, MNOperand<BM, NWV>>::type;
@@ -328,10 +333,10 @@ struct GemmCore {
     // global loads run two steps ahead; the 256 x 256 tile has no room for
     // the second set (except with two plain K-contiguous operands) and loads
     // one step ahead.
-    static constexpr int NSET = (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG))) ? 1 : 2;
+    static constexpr int NSET = (KG == 2 || (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG)))) ? 1 : 2;
 
     char* smem;
-    int lane, wave, wm, wn, nk;
+    int lane, wave, wm, wn, nk, kk0;
     int kbase;  // first k-step of this workgroup's K range
     int kend;   // end of this workgroup's K range (elements)
     const bf16_t* abase;
@@ -349,8 +354,9 @@ struct GemmCore {
         const int tid = threadIdx.x;
         lane = tid & 63;
         wave = tid >> 6;
-        wm = wave >> 1;
+        wm = (wave % (NWV / KG)) >> 1;
         wn = wave & 1;
+        kk0 = KG == 2 ? 2 * (wave / (NWV / KG)) : 0;  // first k16 sub-step of this wave's group
         lda = p.lda;
         ldb = p.ldb;
         bseg = p.bseg;
@@ -470,8 +476,46 @@ struct GemmCore {
         interleave<NM - PRE, NRD, 0, 0>();
     }
 
+    // KG == 2: the group's two sub-steps kk0, kk0+1 of step kt; on entry Fa holds kk0.
+    template <int P>
+    __device__ __forceinline__ void step2(int kt, HF& Fa, HF& Fb) {
+        constexpr int R = 0;
+        run_mfmas<0, NM>(acc, Fa);
+        read_sub(P, kk0 + 1, Fb);
+        store_a(P ^ 1, ra[R]);
+        load_a(kt + 2, ra[R]);
+        store_b(P ^ 1, rb[R]);
+        load_b(kt + 2, rb[R]);
+        interleave<NM, NRD, LA::NI + LB::NI, LA::NI + LB::NI>();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm();
+        run_mfmas<0, PRE>(acc, Fb);
+        stage_barrier();
+        run_mfmas<PRE, NM>(acc, Fb);
+        read_sub(P ^ 1, kk0, Fa);
+        interleave<NM - PRE, NRD, 0, 0>();
+    }
+
     __device__ __forceinline__ void run() {
         if (nk <= 0) return;
+        if constexpr (KG == 2) {
+            load_a(0, ra[0]);
+            load_b(0, rb[0]);
+            store_a(0, ra[0]);
+            store_b(0, rb[0]);
+            load_a(1, ra[0]);
+            load_b(1, rb[0]);
+            wait_lgkm();
+            stage_barrier();
+            HF Fa, Fb;
+            read_sub(0, kk0, Fa);
+            for (int kt = 0; kt < nk; kt += 2) {
+                step2<0>(kt, Fa, Fb);
+                step2<1>(kt + 1, Fa, Fb);
+            }
+            wait_vm_lgkm<0>();
+            return;
+        }
         load_a(0, ra[0]);
         load_b(0, rb[0]);
         if constexpr (NSET == 2) {
@@ -554,11 +598,11 @@ __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ld
     }
 }
 
-template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG = 1>
 __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gemm_bf16_kernel(const GemmBatch batch) {
-    using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV>;
-    constexpr int NT = 64 * NWV;
-    constexpr int HR = NWV / 4;  // wave rows per half tile
+    using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV, KG>;
+    constexpr int NT = 64 * NWV / KG;  // epilogue threads (the first K group)
+    constexpr int HR = NWV / KG / 4;   // wave rows per half tile
     constexpr int RING = STAGES * Core::STAGE;
     // fp32 epilogues (weight gradients, GeLU') stage half a tile at a time as
     // fp32; the bf16 ones stage the whole tile as bf16.
@@ -571,7 +615,8 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = (wave % (NWV / KG)) >> 1, wn = wave & 1;
+    const bool epi_wave = wave < NWV / KG;  // the waves that hold the final sums
     // workgroup -> (K split, problem, tile)
     const int split = (int)blockIdx.x / batch.tiles;
     int t = (int)blockIdx.x - split * batch.tiles;
@@ -590,6 +635,30 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     Core core(p, smem, m0, n0, kb, kn);
     core.run();
     auto& acc = core.acc;
+    if constexpr (KG == 2) {
+        // the second K group adds its partial sums into the first's, one 32-column
+        // block of the wave tile at a time (fixed order: deterministic)
+        static_assert(OUTF32, "the K-group split serves the fp32 weight gradients");
+        float* mg = reinterpret_cast<float*>(smem);
+        const int wl = wave % 4, g = wave / 4;
+#pragma unroll
+        for (int j = 0; j < Core::FN; ++j) {
+            __syncthreads();
+            if (g == 1) {
+#pragma unroll
+                for (int i = 0; i < Core::FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mg[((i * 16 + r) * 4 + wl) * 64 + lane] = acc[i][j][r];
+            }
+            __syncthreads();
+            if (g == 0) {
+#pragma unroll
+                for (int i = 0; i < Core::FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += mg[((i * 16 + r) * 4 + wl) * 64 + lane];
+            }
+        }
+    }
 
     const int csg = n0 / p.cseg;
     const int cofs = csg * p.cseg;
@@ -618,7 +687,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             __syncthreads();
-            if (wm / HR == half) {
+            if (epi_wave && wm / HR == half) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -639,7 +708,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                 const int e = tid + it * NT;
                 const int lr = e / GPR, cg = e % GPR;
                 const int m = m0 + half * EROWS + lr, n = n0 + cg * 8;
-                if (m >= p.M || n >= p.N) continue;
+                if (!epi_wave || m >= p.M || n >= p.N) continue;
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8);
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8 + 4);
                 const int nl = n - cofs;
@@ -674,7 +743,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                         const int e = tid + it * NT;
                         const int lr = e / BN, c = e % BN;
                         const int m = m0 + half * EROWS + lr, n = n0 + c;
-                        if (m < p.M && n < p.N)
+                        if (epi_wave && m < p.M && n < p.N)
                             atomicAdd(reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + (n - cofs),
                                       stage[lr * ELD + c]);
                     }
@@ -684,12 +753,12 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     }
 }
 
-template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32>
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG = 1>
 hipError_t launch(GemmBatch b, hipStream_t s) {
     b.tiles0 = ((b.g[0].N + BN - 1) / BN) * ((b.g[0].M + BM - 1) / BM);
     b.tiles = b.tiles0;
     if (b.n > 1) b.tiles += ((b.g[1].N + BN - 1) / BN) * ((b.g[1].M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NWV, AK, BKC, BKSEG, EPI, OUTF32>), dim3(b.tiles * b.ksplit),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NWV, AK, BKC, BKSEG, EPI, OUTF32, KG>), dim3(b.tiles * b.ksplit),
                        dim3(64 * NWV),
                        0, s, b);
     count_launch();
@@ -757,11 +826,14 @@ struct Cand {
     double eff;       // throughput of the shape relative to 256 x 256 (measured on MI355X)
     bool f32_tn_only;
 };
-// The last is the 256 x 192 tile with 8 waves (two per SIMD): 3-16% faster than
-// with 4 waves on the same tile in a shape sweep.
+// Index 8 is the 256 x 192 tile with 8 waves (two per SIMD): 3-16% faster than
+// with 4 waves on the same tile in a shape sweep.  Index 9 is the 192 x 192
+// fp32 weight-gradient tile with 8 waves in two K groups: 4-6% faster than its
+// 4-wave form on the MLP weight-gradient pair.
 const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
                        {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
-                       {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false}};
+                       {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false},
+                       {192, 192, 1, 0.975, true}};
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
 constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
 
@@ -775,7 +847,11 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
         case 5: return dispatch<64, 192, 4>(d, b, s);
         case 6: return dispatch<64, 64, 4>(d, b, s);
         case 7: return dispatch<128, 192, 4>(d, b, s);
-        default: return dispatch<256, 192, 8>(d, b, s);
+        case 8: return dispatch<256, 192, 8>(d, b, s);
+        default:  // 9: fp32 weight gradients only
+            if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
+                return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2>(b, s);
+            return hipErrorInvalidValue;
     }
 }
 
@@ -805,9 +881,9 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
-        // The 8-wave tile takes a whole CU's registers; beside another launch the
+        // The 8-wave tiles take a whole CU's registers; beside another launch the
         // co-resident 4-wave tiles do better (attention dX beside dWqkv: +1% per step).
-        if (c == 8 && d[0].concurrent) continue;
+        if ((c == 8 || c == 9) && d[0].concurrent) continue;
         bool ok = true;
         int64_t t = 0;
         for (int i = 0; i < n; ++i) {
