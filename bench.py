@@ -30,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "shard-layer fwd+bwd TFLOP/s and % of bf16 MFMA peak, 8.3B-shape t=8 shard"
-PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense); fp16 has the same peak
 PEAK_HBM_GBS = 8000.0
 # HBM bytes per step launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (copy-calibrated),
 # valid while the kernel sources hash to the value recorded in the file
@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt8b")
     ap.add_argument("--shard", type=int, default=0)
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
+                    help="16-bit storage format (fp16: IEEE half with fp16 MFMAs; same dense peak)")
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -175,6 +177,8 @@ def main():
     cfg = CONFIGS[args.config]
     if not cfg.backward:
         cfg = cfg.with_(backward=True)
+    if cfg.dtype != args.dtype and cfg.dtype != "fp32":
+        cfg = cfg.with_(dtype=args.dtype)
     K, W = args.steps, args.warmup
     if args.layer:
         return bench_layer(cfg, K, W)
@@ -246,7 +250,7 @@ def main():
         fl, by = costs[dom["step"]]
         ach = fl / (dom["avg_us"] * 1e-6) / 1e12
         traffic, tnote = None, "no counter table for this workload"
-        if cfg.name == "gpt8b" and args.shard == 0:
+        if cfg.name == "gpt8b" and cfg.dtype == "bf16" and args.shard == 0:
             from tensor_transformer_layer_02_amd.profiling import read_traffic, source_hash
             tab, h = read_traffic(TRAFFIC_FILE)
             if h is None:
@@ -278,7 +282,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": cfg.dtype,
         "data": "synthetic",
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": cfg.batch, "seq": cfg.seq,
@@ -346,7 +350,7 @@ def bench_layer(cfg, K, W):
         "metric": "pre-LN layer fwd+bwd TFLOP/s, all t shards on one GPU, 8.3B shape",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic", "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "dtype": cfg.dtype, "data": "synthetic", "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": f"{cfg.name} pre-LN layer: {cfg.degree} shards + residual/LayerNorm kernels",
                    "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn,
                    "degree": cfg.degree, "flops_per_step": flops},

@@ -36,6 +36,9 @@
  *   - Data types: dims.act = TP_BF16: X, weights, biases, activations,
  *     saved tensors and partial outputs are bfloat16; GEMMs and softmax
  *     accumulate in fp32; weight and bias gradients are fp32.
+ *     dims.act = TP_FP16: the same with IEEE half (binary16) storage in place
+ *     of bfloat16 (fp16 MFMAs, fp32 accumulation; values are rounded to
+ *     nearest even and overflow to +-inf past 65504: the caller scales).
  *     dims.act = TP_FP32: everything is fp32 (fp32 FMA arithmetic).
  *   - Gradients are written (overwritten), never accumulated, into the
  *     shard's block of the full-size caller buffers; entries outside the
@@ -61,7 +64,7 @@
  *     crosses this boundary.
  *   - Alignment: every device pointer must be 16-byte aligned; hidden,
  *     F/t and (H/t)*d must be multiples of 8.  Supported head dims:
- *     32, 64, 96, 128 (bf16) and 8..128 in steps of 8 (fp32).
+ *     32, 64, 96, 128 (bf16, fp16) and 8..128 in steps of 8 (fp32).
  *   - Calls on different streams may run concurrently if their output
  *     buffers do not overlap.
  */
@@ -81,13 +84,13 @@ typedef enum {
     TP_EDIVIDE = 2,       /* t does not divide H or F, or H does not divide h         */
     TP_ESHARD = 3,        /* shard index outside [0, t) or t < 1                      */
     TP_EALIGN = 4,        /* pointer not 16-byte aligned or size not a multiple of 8  */
-    TP_EDTYPE = 5,        /* dims.act is neither TP_FP32 nor TP_BF16                  */
+    TP_EDTYPE = 5,        /* dims.act is not one of TP_FP32, TP_BF16, TP_FP16         */
     TP_EUNSUPPORTED = 6,  /* head dimension not supported                             */
     TP_EHIP = 7,          /* a kernel launch failed                                   */
     TP_ESIZE = 8          /* work buffer smaller than tp_*_work_bytes                 */
 } tp_status;
 
-typedef enum { TP_FP32 = 0, TP_BF16 = 1 } tp_dtype;
+typedef enum { TP_FP32 = 0, TP_BF16 = 1, TP_FP16 = 2 } tp_dtype;
 
 /* GeLU form of the FFN shard.  The pages name only "GeLU"; the default is the
  * exact u * Phi(u) (erf form).  TP_GELU_TANH selects the tanh approximation

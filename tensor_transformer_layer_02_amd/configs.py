@@ -28,7 +28,7 @@ class LayerConfig:
     ffn: int
     degree: int         # tensor-parallel degree t
     causal: bool
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp16"
     backward: bool      # whether the workload includes the backward pass
     note: str = ""
     gelu: str = "erf"   # GeLU form of the FFN: "erf" (exact, the default) or "tanh"

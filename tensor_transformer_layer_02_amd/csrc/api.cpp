@@ -34,14 +34,16 @@ constexpr int SEG_NONE = 1 << 30;
 
 struct Shape {
     int64_t T, b, s, h, H, F, t, i, Fs, Hs, d, w;
-    bool causal, bf16;
+    bool causal;
+    bool h16;        // 16-bit storage (bfloat16 or IEEE half)
+    bool fp16;       // dims.act == TP_FP16
     bool gelu_tanh;  // dims.gelu == TP_GELU_TANH
     int64_t e;  // bytes per element of dims.act
 };
 
 int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     if (!dims) return TP_EINVAL;
-    if (dims->act != TP_FP32 && dims->act != TP_BF16) return TP_EDTYPE;
+    if (dims->act != TP_FP32 && dims->act != TP_BF16 && dims->act != TP_FP16) return TP_EDTYPE;
     if (dims->batch <= 0 || dims->seq <= 0 || dims->hidden <= 0 || dims->heads <= 0 || dims->ffn <= 0)
         return TP_EINVAL;
     if (dims->causal != 0 && dims->causal != 1) return TP_EINVAL;
@@ -56,10 +58,11 @@ int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     s.Fs = s.F / degree; s.Hs = s.H / degree; s.d = s.h / s.H; s.w = s.Hs * s.d;
     s.causal = dims->causal != 0;
     s.gelu_tanh = dims->gelu == TP_GELU_TANH;
-    s.bf16 = dims->act == TP_BF16;
-    s.e = s.bf16 ? 2 : 4;
+    s.h16 = dims->act != TP_FP32;
+    s.fp16 = dims->act == TP_FP16;
+    s.e = s.h16 ? 2 : 4;
     if (s.h % 8 || s.Fs % 8 || s.w % 8) return TP_EALIGN;
-    if (s.bf16) {
+    if (s.h16) {
         if (s.d != 32 && s.d != 64 && s.d != 96 && s.d != 128) return TP_EUNSUPPORTED;
         if (s.w % 64) return TP_EUNSUPPORTED;  // K-segment of the fused QKV backward GEMM
     } else {
@@ -71,6 +74,8 @@ int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     if (o) *o = s;
     return TP_OK;
 }
+
+inline int fmt(const Shape& s) { return s.fp16 ? tp::FMT_F16 : s.h16 ? tp::FMT_BF16 : tp::FMT_F32; }
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
@@ -153,15 +158,23 @@ struct StepTimer {
     }
 };
 
+// The GEMM descriptor with the storage format of the call.
+inline tp::GemmDesc fmt_of(const Shape& s, const tp::GemmDesc& g) {
+    tp::GemmDesc d = g;
+    d.fp16 = s.fp16;
+    return d;
+}
+
 inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
     StepTimer t(step, st);
-    return s.bf16 ? tp::gemm_bf16(g, st) : tp::gemm_f32(g, st);
+    return s.h16 ? tp::gemm_bf16(fmt_of(s, g), st) : tp::gemm_f32(g, st);
 }
 
 // A weight-gradient GEMM (fp32 output; the bf16 path may split K in two).
 inline hipError_t gemm_w(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
     StepTimer t(step, st);
-    return s.bf16 ? tp::gemm_bf16_batch(&g, 1, true, nullptr, st) : tp::gemm_f32(g, st);
+    const tp::GemmDesc d = fmt_of(s, g);
+    return s.h16 ? tp::gemm_bf16_batch(&d, 1, true, nullptr, st) : tp::gemm_f32(g, st);
 }
 
 // Per-device auxiliary stream for launches that are independent of the main
@@ -225,7 +238,10 @@ struct AuxScope {
 // (bf16 path; may split K in two with zeroed outputs), or one after the other.
 inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, int step) {
     StepTimer t(step, st);
-    if (s.bf16) return tp::gemm_bf16_batch(g, 2, true, nullptr, st);
+    if (s.h16) {
+        const tp::GemmDesc d[2] = {fmt_of(s, g[0]), fmt_of(s, g[1])};
+        return tp::gemm_bf16_batch(d, 2, true, nullptr, st);
+    }
     hipError_t e = tp::gemm_f32(g[0], st);
     return e != hipSuccess ? e : tp::gemm_f32(g[1], st);
 }
@@ -273,7 +289,8 @@ hipError_t attn_fwd_saved(const Shape& s, const void* X, const void* Wq, const v
     ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = at(saved, L.O, 1); ad.ld_o = s.w;
     ad.lse = static_cast<float*>(at(saved, L.LSE, 1));
     StepTimer t(TP_STEP_ATTN_CORE, st);
-    return s.bf16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st);
+    ad.fp16 = s.fp16;
+    return s.h16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st);
 }
 
 }  // namespace
@@ -284,7 +301,7 @@ void count_launch() { ++g_launches; }
 
 extern "C" {
 
-int tp_version(void) { return 200; }
+int tp_version(void) { return 300; }
 
 const char* tp_status_string(int status) {
     switch (status) {
@@ -400,7 +417,7 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
         float* outs[3] = {db1 + c0, nullptr, nullptr};
         if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
         StepTimer t(TP_STEP_MLP_DB1, aux.a->st);
-        if (tp::colsum(s.bf16, dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, aux.a->st) != hipSuccess) return TP_EHIP;
+        if (tp::colsum(fmt(s), dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, aux.a->st) != hipSuccess) return TP_EHIP;
     }
 
     tp::GemmDesc gw[2];  // one launch: dB[C_i, :] = Y^T dZ and dA[:, C_i] = X^T dU
@@ -501,8 +518,9 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;
     ad.qkv = QKV; ad.ld_qkv = 3 * s.w; ad.O = const_cast<void*>(O); ad.ld_o = s.w;
     ad.lse = const_cast<float*>(lse); ad.dO = dO; ad.Dq = Dq; ad.dqkv = dQKV;
+    ad.fp16 = s.fp16;
     auto core = [&](int part, hipStream_t q) {
-        return s.bf16 ? tp::attn_bwd_bf16(ad, part, q) : tp::attn_bwd_f32(ad, part, q);
+        return s.h16 ? tp::attn_bwd_bf16(ad, part, q) : tp::attn_bwd_f32(ad, part, q);
     };
     {   // D = rowsum(dO * O), the dK/dV pass, the dQ pass (running the last two
         // concurrently measured slower: their workgroups compete for the same CUs)
@@ -519,7 +537,7 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     if (bias_grads) {
         float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
         StepTimer t(TP_STEP_ATTN_DBIAS, aux.a->st);
-        if (tp::colsum(s.bf16, dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, aux.a->st) != hipSuccess)
+        if (tp::colsum(fmt(s), dQKV, s.T, 3 * s.w, 3 * s.w, outs, (int)s.w, cs, aux.a->st) != hipSuccess)
             return TP_EHIP;
     }
     tp::GemmDesc gx;
@@ -545,14 +563,14 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
 
 int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts, const void* bias,
                     float* out, void* stream) {
-    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (dtype != TP_FP32 && dtype != TP_BF16 && dtype != TP_FP16) return TP_EDTYPE;
     if (rows <= 0 || cols <= 0 || nparts < 1 || !parts || !out) return TP_EINVAL;
     for (int k = 0; k < nparts; ++k) {
         if (!parts[k]) return TP_EINVAL;
         if (!aligned16(parts[k])) return TP_EALIGN;
     }
     if (!aligned16(out) || (bias && !aligned16(bias))) return TP_EALIGN;
-    return hip_status(tp::sum_partials(dtype == TP_BF16, rows, cols, parts, nparts, bias, out,
+    return hip_status(tp::sum_partials(dtype, rows, cols, parts, nparts, bias, out,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -613,7 +631,7 @@ bool ln_cols_ok(int64_t cols) { return cols % 8 == 0; }
 int tp_residual_layernorm(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts,
                           const void* bias, const float* residual, float* out, const float* gamma,
                           const float* beta, double eps, void* y, float* mean, float* rstd, void* stream) {
-    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (dtype != TP_FP32 && dtype != TP_BF16 && dtype != TP_FP16) return TP_EDTYPE;
     if (rows <= 0 || cols <= 0 || nparts < 0 || nparts > tp::LN_MAXP || (nparts > 0 && !parts) || (!out && !y) ||
         !(eps > 0.0))
         return TP_EINVAL;
@@ -628,7 +646,7 @@ int tp_residual_layernorm(int dtype, int64_t rows, int64_t cols, const void* con
     const void* ptrs[] = {bias, residual, out, gamma, beta, y, mean, rstd};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return TP_EALIGN;
-    d.rows = rows; d.cols = (int)cols; d.bf16 = dtype == TP_BF16; d.nparts = nparts;
+    d.rows = rows; d.cols = (int)cols; d.fmt = dtype; d.nparts = nparts;
     d.bias = bias; d.residual = residual; d.out = out; d.gamma = gamma; d.beta = beta; d.eps = (float)eps;
     d.y = y; d.mean = mean; d.rstd = rstd;
     return hip_status(tp::residual_layernorm(d, static_cast<hipStream_t>(stream)));
@@ -643,7 +661,7 @@ int tp_layernorm_bwd(int dtype, int64_t rows, int64_t cols, const float* x, cons
                      const float* rstd, const void* const* dparts, int nparts, const float* dres, float* dx,
                      void* dx_act, float* dgamma, float* dbeta, float* dres_sum, float* dx_sum, void* work,
                      size_t work_bytes, void* stream) {
-    if (dtype != TP_FP32 && dtype != TP_BF16) return TP_EDTYPE;
+    if (dtype != TP_FP32 && dtype != TP_BF16 && dtype != TP_FP16) return TP_EDTYPE;
     if (rows <= 0 || cols <= 0 || nparts < 1 || nparts > tp::LN_MAXP || !dparts || !x || !mean || !rstd || !dx ||
         !work)
         return TP_EINVAL;
@@ -659,7 +677,7 @@ int tp_layernorm_bwd(int dtype, int64_t rows, int64_t cols, const float* x, cons
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return TP_EALIGN;
     if (work_bytes < tp_layernorm_bwd_work_bytes(rows, cols)) return TP_ESIZE;
-    d.rows = rows; d.cols = (int)cols; d.bf16 = dtype == TP_BF16; d.nparts = nparts;
+    d.rows = rows; d.cols = (int)cols; d.fmt = dtype; d.nparts = nparts;
     d.x = x; d.gamma = gamma; d.mean = mean; d.rstd = rstd; d.dres = dres; d.dx = dx; d.dx_act = dx_act;
     d.dgamma = dgamma; d.dbeta = dbeta; d.dres_sum = dres_sum; d.dx_sum = dx_sum;
     d.work = static_cast<float*>(work);

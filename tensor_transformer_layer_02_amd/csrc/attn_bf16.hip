@@ -1,11 +1,12 @@
-// Fused per-head softmax attention on gfx950 matrix cores, bf16 in / fp32 math.
+// Fused per-head softmax attention on gfx950 matrix cores, 16-bit in (bf16 or
+// IEEE half, the template parameter ST) / fp32 math.
 //
 // Each shard runs full attention for its own heads with no communication
 // (page "Megatron-LM: what the tensor parallelism paper actually says",
 // section "The attention heads split").  Scores are Q K^T / sqrt(d) with an
 // optional causal mask (key m allowed for query j iff m <= j).
 //
-// All products use v_mfma_f32_32x32x16_bf16.  For an operand tile the lane
+// All products use v_mfma_f32_32x32x16_bf16 (_f16 for half storage).  For an operand tile the lane
 // l holds row (or column) l % 32 and, per k16 chunk, the 8 k-slots
 // 8*(l/32) .. +7; the 32x32 result gives lane l column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
@@ -193,10 +194,12 @@ struct FragAddr {
 
 // bf16 operand fragment (k16 chunk kc of a 64-row block) from the fp32
 // result registers of its 32-row half: slots s = values r = 8*(kc%2) + s.
+template <typename ST>
 __device__ __forceinline__ u32x4 pack_chunk(const f32x16& v, int half) {
     const int o = 8 * half;
-    return u32x4{pack_bf2(v[o], v[o + 1]), pack_bf2(v[o + 2], v[o + 3]), pack_bf2(v[o + 4], v[o + 5]),
-                 pack_bf2(v[o + 6], v[o + 7])};
+    using S = Store16<ST>;
+    return u32x4{S::pack2(v[o], v[o + 1]), S::pack2(v[o + 2], v[o + 3]), S::pack2(v[o + 4], v[o + 5]),
+                 S::pack2(v[o + 6], v[o + 7])};
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -211,15 +214,15 @@ __device__ __forceinline__ int res_row(int r, int lane) { return 8 * (r >> 2) + 
 
 // Store a [D x 32] transposed fp32 accumulator (rows = d, lane column = one
 // token row of `out`) as bf16, times `mul`: 4 consecutive d per 8-byte store.
-template <int D>
+template <int D, typename ST>
 __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x16 (&acc)[D / 32], float mul, int lane) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             u32x2 t;
-            t[0] = pack_bf2(acc[db][4 * q] * mul, acc[db][4 * q + 1] * mul);
-            t[1] = pack_bf2(acc[db][4 * q + 2] * mul, acc[db][4 * q + 3] * mul);
+            t[0] = Store16<ST>::pack2(acc[db][4 * q] * mul, acc[db][4 * q + 1] * mul);
+            t[1] = Store16<ST>::pack2(acc[db][4 * q + 2] * mul, acc[db][4 * q + 3] * mul);
             *reinterpret_cast<u32x2*>(row + 32 * db + 8 * q + 4 * (lane >> 5)) = t;
         }
 }
@@ -251,7 +254,7 @@ struct PairRows {
 // reference that moves only when some row's block max exceeds it by more
 // than 2^8 (in the exponent's base 2): the softmax is the same for any
 // reference, P stays <= 256, and O is rescaled rarely.
-template <int D>
+template <int D, typename ST>
 __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;  // one [128][D] pair tile
     constexpr int SLOT = 2 * PT;                                   // K pair, V pair
@@ -310,7 +313,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
             for (int h = 0; h < 2; ++h) {
                 sacc[h] = zero16();
 #pragma unroll
-                for (int c = 0; c < KC; ++c) sacc[h] = mfma32x32x16(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+                for (int c = 0; c < KC; ++c) sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
             }
             // Masks only where the block reaches past the diagonal or the
             // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
@@ -351,9 +354,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
                 }
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const u32x4 pf = pack_chunk(sacc[kc >> 1], kc & 1);
+                const u32x4 pf = pack_chunk<ST>(sacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(fa.frag_tr(Vt, rb, db, kc), pf, oacc[db]);
+                for (int db = 0; db < DB; ++db) oacc[db] = Store16<ST>::mfma(fa.frag_tr(Vt, rb, db, kc), pf, oacc[db]);
             }
         }
         if (more) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
@@ -388,14 +391,14 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
             for (int r = 0; r < 16; ++r)
                 oacc[db][r] = oacc[db][r] * a0 + mg[((2 + 16 * db + r) * 4 + qg) * 64 + lane] * a1;
         if (qw < s) {
-            store_rowT<D>(a.O + ((int64_t)b * s + qw) * a.ld_o + g * D, oacc, 1.f / l, lane);
+            store_rowT<D, ST>(a.O + ((int64_t)b * s + qw) * a.ld_o + g * D, oacc, 1.f / l, lane);
             if (lane < 32) a.lse[((int64_t)b * a.heads + g) * s + qw] = (mm + log2f(l)) * LN2;
         }
     }
 }
 
 // D[b, g, j] = dO_j . O_j per head (fp32).
-template <int D>
+template <int D, typename ST>
 __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;  // (token, head)
     const int64_t T = (int64_t)a.batch * a.seq;
@@ -410,8 +413,8 @@ __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
         const u32x4 ov = ld16(o + c), dv = ld16(d + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc += __uint_as_float(ov[i] << 16) * __uint_as_float(dv[i] << 16);
-            acc += __uint_as_float(ov[i] & 0xffff0000u) * __uint_as_float(dv[i] & 0xffff0000u);
+            acc += Store16<ST>::lo(ov[i]) * Store16<ST>::lo(dv[i]);
+            acc += Store16<ST>::hi(ov[i]) * Store16<ST>::hi(dv[i]);
         }
     }
     const int b = (int)(r / a.seq), j = (int)(r % a.seq);
@@ -446,7 +449,7 @@ __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DB], float* mg, int q
 // stream through LDS; the two waves of a key group take the two 32-query
 // halves of each block, and their dK, dV partial sums add through LDS at the
 // end (in a fixed order: deterministic).
-template <int D>
+template <int D, typename ST>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
     constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, LSE, D
@@ -530,8 +533,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
             f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
-                sacc = mfma32x32x16(fa.frag_rows(Qt, 32 * qh, c), kf[c], sacc);
-                pacc = mfma32x32x16(fa.frag_rows(dOt, 32 * qh, c), vf[c], pacc);
+                sacc = Store16<ST>::mfma(fa.frag_rows(Qt, 32 * qh, c), kf[c], sacc);
+                pacc = Store16<ST>::mfma(fa.frag_rows(dOt, 32 * qh, c), vf[c], pacc);
             }
             // rows = queries qh0 + res_row(r), column = this lane's key
             const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
@@ -551,12 +554,12 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
             }
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const u32x4 pf = pack_chunk(sacc, half), sf = pack_chunk(pacc, half);
+                const u32x4 pf = pack_chunk<ST>(sacc, half), sf = pack_chunk<ST>(pacc, half);
                 const int kc = 2 * qh + half;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dv[db] = mfma32x32x16(pf, fa.frag_tr(dOt, 0, db, kc), dv[db]);
-                    dk[db] = mfma32x32x16(sf, fa.frag_tr(Qt, 0, db, kc), dk[db]);
+                    dv[db] = Store16<ST>::mfma(pf, fa.frag_tr(dOt, 0, db, kc), dv[db]);
+                    dk[db] = Store16<ST>::mfma(sf, fa.frag_tr(Qt, 0, db, kc), dk[db]);
                 }
             }
         }
@@ -586,8 +589,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int c = 32 * db + (lane & 31);
-                dKg[(int64_t)key * a.ld_qkv + c] = f2bf(dk[db][r] * a.scale);
-                dVg[(int64_t)key * a.ld_qkv + c] = f2bf(dv[db][r]);
+                dKg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dk[db][r] * a.scale);
+                dVg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dv[db][r]);
             }
         }
     }
@@ -596,7 +599,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
 // dQ for two 64-query blocks (rows as in the forward).  The two waves of a
 // row group take alternate 64-key blocks of each streamed pair; their dQ^T
 // sums add through LDS at the end (in a fixed order: deterministic).
-template <int D>
+template <int D, typename ST>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
     constexpr int SLOT = 2 * PT;  // K pair, V pair
@@ -660,8 +663,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
                 sacc[h] = pacc[h] = zero16();
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    sacc[h] = mfma32x32x16(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
-                    pacc[h] = mfma32x32x16(fa.frag_rows(Vt, rb + 32 * h, c), of[c], pacc[h]);
+                    sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+                    pacc[h] = Store16<ST>::mfma(fa.frag_rows(Vt, rb + 32 * h, c), of[c], pacc[h]);
                 }
             }
             const bool edge = (a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s || qw0 + 32 > s;
@@ -676,9 +679,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
                 }
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const u32x4 sf = pack_chunk(pacc[kc >> 1], kc & 1);
+                const u32x4 sf = pack_chunk<ST>(pacc[kc >> 1], kc & 1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(fa.frag_tr(Kt, rb, db, kc), sf, dq[db]);
+                for (int db = 0; db < DB; ++db) dq[db] = Store16<ST>::mfma(fa.frag_tr(Kt, rb, db, kc), sf, dq[db]);
             }
         }
         if (more) {
@@ -702,7 +705,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dq[db][r] += mg[((16 * db + r) * 4 + qg) * 64 + lane];
-        if (qw < s) store_rowT<D>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
+        if (qw < s) store_rowT<D, ST>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
     }
 }
 
@@ -721,52 +724,62 @@ AttnArgs make_args(const AttnDesc& d) {
     return a;
 }
 
-template <int D>
+template <int D, typename ST>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
     dim3 grid(((a.seq + BKV - 1) / BKV + 1) / 2, a.batch * a.heads);
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(NT8), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, ST>), grid, dim3(NT8), 0, s, a);
     count_launch();
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename ST>
 hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
     const int64_t T = (int64_t)a.batch * a.seq;
     dim3 grid_pair(((a.seq + BKV - 1) / BKV + 1) / 2, a.batch * a.heads);
     if (part == ATTN_BWD_ROWDOT)
-        hipLaunchKernelGGL(attn_rowdot_kernel<D>, dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((attn_rowdot_kernel<D, ST>), dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
     else if (part == ATTN_BWD_DKDV)
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, grid_pair, dim3(NT8), 0, s, a);
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
     else if (part == ATTN_BWD_DQ)
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, grid_pair, dim3(NT8), 0, s, a);
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
     else
         return hipErrorInvalidValue;
     count_launch();
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t attn_fwd_bf16(const AttnDesc& d, hipStream_t s) {
-    const AttnArgs a = make_args(d);
-    switch (d.dh) {
-        case 32: return fwd_d<32>(a, s);
-        case 64: return fwd_d<64>(a, s);
-        case 96: return fwd_d<96>(a, s);
-        case 128: return fwd_d<128>(a, s);
+template <typename ST>
+hipError_t fwd_st(const AttnArgs& a, int dh, hipStream_t s) {
+    switch (dh) {
+        case 32: return fwd_d<32, ST>(a, s);
+        case 64: return fwd_d<64, ST>(a, s);
+        case 96: return fwd_d<96, ST>(a, s);
+        case 128: return fwd_d<128, ST>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t attn_bwd_bf16(const AttnDesc& d, int part, hipStream_t s) {
-    const AttnArgs a = make_args(d);
-    switch (d.dh) {
-        case 32: return bwd_d<32>(a, part, s);
-        case 64: return bwd_d<64>(a, part, s);
-        case 96: return bwd_d<96>(a, part, s);
-        case 128: return bwd_d<128>(a, part, s);
+template <typename ST>
+hipError_t bwd_st(const AttnArgs& a, int dh, int part, hipStream_t s) {
+    switch (dh) {
+        case 32: return bwd_d<32, ST>(a, part, s);
+        case 64: return bwd_d<64, ST>(a, part, s);
+        case 96: return bwd_d<96, ST>(a, part, s);
+        case 128: return bwd_d<128, ST>(a, part, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t attn_fwd_bf16(const AttnDesc& d, hipStream_t s) {
+    const AttnArgs a = make_args(d);
+    return d.fp16 ? fwd_st<f16_t>(a, d.dh, s) : fwd_st<bf16_t>(a, d.dh, s);
+}
+
+hipError_t attn_bwd_bf16(const AttnDesc& d, int part, hipStream_t s) {
+    const AttnArgs a = make_args(d);
+    return d.fp16 ? bwd_st<f16_t>(a, d.dh, part, s) : bwd_st<bf16_t>(a, d.dh, part, s);
 }
 
 }  // namespace tp

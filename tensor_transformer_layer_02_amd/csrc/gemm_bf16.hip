@@ -1,4 +1,7 @@
-// bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
+// 16-bit GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, or _f16 for
+// IEEE half storage), fp32 accumulation.  The storage format is a template
+// parameter (ST: bf16_t or f16_t) that only selects the MFMA and the
+// conversions of the epilogue; loads, LDS layout and tiling are shared.
 //
 // Every projection of the layer shard is one of these GEMMs (page "Megatron-LM:
 // what the tensor parallelism paper actually says", sections "How transformer
@@ -267,12 +270,12 @@ struct Half {
 // goes in as the first operand, so block (i, j) accumulates C^T: lane l holds
 // row l%32 of the block and the 4 consecutive columns 8q + 4*(l/32) .. +3 in
 // values 4q .. 4q+3 (q = 0..3), which the epilogue writes 8 or 16 bytes at a time.
-template <int FROM, int TO, int FM, int FN>
+template <typename ST, int FROM, int TO, int FM, int FN>
 __device__ __forceinline__ void run_mfmas(f32x16 (&acc)[FM][FN], const Half<FM, FN>& F) {
 #pragma unroll
     for (int idx = FROM; idx < TO; ++idx) {
         const int i = idx / FN, j = idx % FN;
-        acc[i][j] = mfma32x32x16(F.b[j], F.a[i], acc[i][j]);
+        acc[i][j] = Store16<ST>::mfma(F.b[j], F.a[i], acc[i][j]);
     }
 }
 
@@ -314,7 +317,7 @@ __device__ __forceinline__ void interleave() {
 // of the K range load from an empty buffer range (zeros, no memory access);
 // their stores and fragment reads are never consumed, so the steady state has
 // no branches for the scheduler to work around.
-template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int NWV, int KG = 1>
+template <int BM, int BN, bool AK, bool BKC, bool BKSEG, int NWV, int KG = 1, typename ST = bf16_t>
 struct GemmCore {
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -454,24 +457,24 @@ struct GemmCore {
     template <int P>
     __device__ __forceinline__ void step(int kt, HF& Fa, HF& Fb) {
         constexpr int R = (P ^ 1) % NSET;  // registers holding step kt+1
-        run_mfmas<0, NM>(acc, Fa);
+        run_mfmas<ST, 0, NM>(acc, Fa);
         read_sub(P, 1, Fb);
         store_a(P ^ 1, ra[R]);
         load_a(kt + 1 + NSET, ra[R]);
         interleave<NM, NRD, LA::NI, LA::NI>();
-        run_mfmas<0, NM>(acc, Fb);
+        run_mfmas<ST, 0, NM>(acc, Fb);
         read_sub(P, 2, Fa);
         store_b(P ^ 1, rb[R]);
         load_b(kt + 1 + NSET, rb[R]);
         interleave<NM, NRD, LB::NI, LB::NI>();
-        run_mfmas<0, NM>(acc, Fa);
+        run_mfmas<ST, 0, NM>(acc, Fa);
         read_sub(P, 3, Fb);
         interleave<NM, NRD, 0, 0>();
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm();
-        run_mfmas<0, PRE>(acc, Fb);
+        run_mfmas<ST, 0, PRE>(acc, Fb);
         stage_barrier();
-        run_mfmas<PRE, NM>(acc, Fb);
+        run_mfmas<ST, PRE, NM>(acc, Fb);
         read_sub(P ^ 1, 0, Fa);
         interleave<NM - PRE, NRD, 0, 0>();
     }
@@ -480,7 +483,7 @@ struct GemmCore {
     template <int P>
     __device__ __forceinline__ void step2(int kt, HF& Fa, HF& Fb) {
         constexpr int R = 0;
-        run_mfmas<0, NM>(acc, Fa);
+        run_mfmas<ST, 0, NM>(acc, Fa);
         read_sub(P, kk0 + 1, Fb);
         store_a(P ^ 1, ra[R]);
         load_a(kt + 2, ra[R]);
@@ -489,9 +492,9 @@ struct GemmCore {
         interleave<NM, NRD, LA::NI + LB::NI, LA::NI + LB::NI>();
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm();
-        run_mfmas<0, PRE>(acc, Fb);
+        run_mfmas<ST, 0, PRE>(acc, Fb);
         stage_barrier();
-        run_mfmas<PRE, NM>(acc, Fb);
+        run_mfmas<ST, PRE, NM>(acc, Fb);
         read_sub(P ^ 1, kk0, Fa);
         interleave<NM - PRE, NRD, 0, 0>();
     }
@@ -550,7 +553,7 @@ constexpr int tile_occupancy() {
 // GELU) as bf16 into a [BM][SP bytes] LDS image.  Each lane writes 8 bytes (4
 // columns of one row) per store; a row pitch of SP = 2*BN + 8 bytes (an odd
 // number of 8-byte pairs) puts the 32 rows of a half-wave on distinct banks.
-template <int FM, int FN, int WTM, int WTN, int SP, bool GELU>
+template <typename ST, int FM, int FN, int WTM, int WTN, int SP, bool GELU>
 __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN], const bf16_t* bias, int ncols,
                                            int wm, int wn, int lane, bool tanh_form = false) {
 #pragma unroll
@@ -561,10 +564,10 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
             float b4[4] = {0.f, 0.f, 0.f, 0.f};
             if (bias && nl < ncols) {
                 const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + nl);
-                b4[0] = __uint_as_float(bw[0] << 16);
-                b4[1] = __uint_as_float(bw[0] & 0xffff0000u);
-                b4[2] = __uint_as_float(bw[1] << 16);
-                b4[3] = __uint_as_float(bw[1] & 0xffff0000u);
+                b4[0] = Store16<ST>::lo(bw[0]);
+                b4[1] = Store16<ST>::hi(bw[0]);
+                b4[2] = Store16<ST>::lo(bw[1]);
+                b4[3] = Store16<ST>::hi(bw[1]);
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -574,7 +577,7 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
                     v[e] = acc[i][j][4 * q + e] + b4[e];
                     if constexpr (GELU) v[e] = gelu_sel(v[e], tanh_form);
                 }
-                const u32x2 o = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+                const u32x2 o = {Store16<ST>::pack2(v[0], v[1]), Store16<ST>::pack2(v[2], v[3])};
                 *reinterpret_cast<u32x2*>(st + (wm * WTM + i * 32 + (lane & 31)) * SP + nl * 2) = o;
             }
         }
@@ -598,9 +601,10 @@ __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ld
     }
 }
 
-template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG = 1>
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG = 1,
+          typename ST = bf16_t>
 __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gemm_bf16_kernel(const GemmBatch batch) {
-    using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV, KG>;
+    using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV, KG, ST>;
     constexpr int NT = 64 * NWV / KG;  // epilogue threads (the first K group)
     constexpr int HR = NWV / KG / 4;   // wave rows per half tile
     constexpr int RING = STAGES * Core::STAGE;
@@ -670,12 +674,12 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
         if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias = p.bias[csg] ? p.bias[csg] + (n0 - cofs) : nullptr;
         bf16_t* C = reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m0 * p.ldc + (n0 - cofs);
         __syncthreads();  // every wave is done with the operand ring
-        stage_bf16<FM, FN, WTM, WTN, SP, false>(smem, acc, bias, ncols, wm, wn, lane);
+        stage_bf16<ST, FM, FN, WTM, WTN, SP, false>(smem, acc, bias, ncols, wm, wn, lane);
         __syncthreads();
         store_bf16<BM, BN, SP, NT>(smem, C, p.ldc, rows, ncols, tid);
         if constexpr (EPI == EPI_BIAS_GELU) {
             __syncthreads();
-            stage_bf16<FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane, p.gelu_tanh != 0);
+            stage_bf16<ST, FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane, p.gelu_tanh != 0);
             __syncthreads();
             store_bf16<BM, BN, SP, NT>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
         }
@@ -723,12 +727,12 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                     const u32x4 uw = *reinterpret_cast<const u32x4*>(p.aux + (int64_t)m * p.ldaux + nl);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        v[2 * q] *= gelu_prime_sel(__uint_as_float(uw[q] << 16), p.gelu_tanh != 0);
-                        v[2 * q + 1] *= gelu_prime_sel(__uint_as_float(uw[q] & 0xffff0000u), p.gelu_tanh != 0);
+                        v[2 * q] *= gelu_prime_sel(Store16<ST>::lo(uw[q]), p.gelu_tanh != 0);
+                        v[2 * q + 1] *= gelu_prime_sel(Store16<ST>::hi(uw[q]), p.gelu_tanh != 0);
                     }
                     u32x4 o;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
+                    for (int q = 0; q < 4; ++q) o[q] = Store16<ST>::pack2(v[2 * q], v[2 * q + 1]);
                     *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
                 }
             }
@@ -753,40 +757,49 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     }
 }
 
-template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG = 1>
+template <int BM, int BN, int NWV, bool AK, bool BKC, bool BKSEG, int EPI, bool OUTF32, int KG, typename ST>
 hipError_t launch(GemmBatch b, hipStream_t s) {
     b.tiles0 = ((b.g[0].N + BN - 1) / BN) * ((b.g[0].M + BM - 1) / BM);
     b.tiles = b.tiles0;
     if (b.n > 1) b.tiles += ((b.g[1].N + BN - 1) / BN) * ((b.g[1].M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NWV, AK, BKC, BKSEG, EPI, OUTF32, KG>), dim3(b.tiles * b.ksplit),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NWV, AK, BKC, BKSEG, EPI, OUTF32, KG, ST>), dim3(b.tiles * b.ksplit),
                        dim3(64 * NWV),
                        0, s, b);
     count_launch();
     return hipGetLastError();
 }
 
-template <int BM, int BN, int NWV>
+template <int BM, int BN, int NWV, typename ST>
+hipError_t dispatch_general(const GemmDesc& d, const GemmBatch& a, hipStream_t s);
+
+// The 192 x 192 tile with 4 waves serves only the fp32-output weight-gradient GEMMs.
+template <int BM, int BN, int NWV, typename ST>
 hipError_t dispatch(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
     const bool ak = d.a_kcontig, bk = d.b_kcontig;
-    if (ak && !bk && !d.b_kseg && !d.out_f32) {
-        if (d.epi == EPI_BIAS_GELU) return launch<BM, BN, NWV, true, false, false, EPI_BIAS_GELU, false>(a, s);
-        if (d.epi == EPI_BIAS) return launch<BM, BN, NWV, true, false, false, EPI_BIAS, false>(a, s);
-        if (d.epi == EPI_STORE) return launch<BM, BN, NWV, true, false, false, EPI_STORE, false>(a, s);
-    } else if (ak && bk && !d.out_f32) {
-        if (d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, true, EPI_STORE, false>(a, s);
-        if (!d.b_kseg && d.epi == EPI_GELU_BWD) return launch<BM, BN, NWV, true, true, false, EPI_GELU_BWD, false>(a, s);
-        if (!d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, false, EPI_STORE, false>(a, s);
-    } else if (!ak && !bk && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE) {
-        return launch<BM, BN, NWV, false, false, false, EPI_STORE, true>(a, s);
+    if constexpr (BM == 192 && BN == 192 && NWV == 4) {
+        if (!ak && !bk && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
+            return launch<192, 192, 4, false, false, false, EPI_STORE, true, 1, ST>(a, s);
+        return hipErrorInvalidValue;
+    } else {
+        return dispatch_general<BM, BN, NWV, ST>(d, a, s);
     }
-    return hipErrorInvalidValue;
 }
 
-// The 192 x 192 tile serves only the fp32-output weight-gradient GEMMs.
-template <>
-hipError_t dispatch<192, 192, 4>(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
-    if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
-        return launch<192, 192, 4, false, false, false, EPI_STORE, true>(a, s);
+template <int BM, int BN, int NWV, typename ST>
+hipError_t dispatch_general(const GemmDesc& d, const GemmBatch& a, hipStream_t s) {
+    const bool ak = d.a_kcontig, bk = d.b_kcontig;
+    if (ak && !bk && !d.b_kseg && !d.out_f32) {
+        if (d.epi == EPI_BIAS_GELU) return launch<BM, BN, NWV, true, false, false, EPI_BIAS_GELU, false, 1, ST>(a, s);
+        if (d.epi == EPI_BIAS) return launch<BM, BN, NWV, true, false, false, EPI_BIAS, false, 1, ST>(a, s);
+        if (d.epi == EPI_STORE) return launch<BM, BN, NWV, true, false, false, EPI_STORE, false, 1, ST>(a, s);
+    } else if (ak && bk && !d.out_f32) {
+        if (d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, true, EPI_STORE, false, 1, ST>(a, s);
+        if (!d.b_kseg && d.epi == EPI_GELU_BWD)
+            return launch<BM, BN, NWV, true, true, false, EPI_GELU_BWD, false, 1, ST>(a, s);
+        if (!d.b_kseg && d.epi == EPI_STORE) return launch<BM, BN, NWV, true, true, false, EPI_STORE, false, 1, ST>(a, s);
+    } else if (!ak && !bk && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE) {
+        return launch<BM, BN, NWV, false, false, false, EPI_STORE, true, 1, ST>(a, s);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -837,20 +850,21 @@ const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
 constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
 
+template <typename ST>
 hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_t s) {
     switch (c) {
-        case 0: return dispatch<256, 256, 4>(d, b, s);
-        case 1: return dispatch<256, 192, 4>(d, b, s);
-        case 2: return dispatch<192, 192, 4>(d, b, s);
-        case 3: return dispatch<256, 128, 4>(d, b, s);
-        case 4: return dispatch<128, 128, 4>(d, b, s);
-        case 5: return dispatch<64, 192, 4>(d, b, s);
-        case 6: return dispatch<64, 64, 4>(d, b, s);
-        case 7: return dispatch<128, 192, 4>(d, b, s);
-        case 8: return dispatch<256, 192, 8>(d, b, s);
+        case 0: return dispatch<256, 256, 4, ST>(d, b, s);
+        case 1: return dispatch<256, 192, 4, ST>(d, b, s);
+        case 2: return dispatch<192, 192, 4, ST>(d, b, s);
+        case 3: return dispatch<256, 128, 4, ST>(d, b, s);
+        case 4: return dispatch<128, 128, 4, ST>(d, b, s);
+        case 5: return dispatch<64, 192, 4, ST>(d, b, s);
+        case 6: return dispatch<64, 64, 4, ST>(d, b, s);
+        case 7: return dispatch<128, 192, 4, ST>(d, b, s);
+        case 8: return dispatch<256, 192, 8, ST>(d, b, s);
         default:  // 9: fp32 weight gradients only
             if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
-                return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2>(b, s);
+                return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2, ST>(b, s);
             return hipErrorInvalidValue;
     }
 }
@@ -924,7 +938,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
         hipError_t e = zero_f32_2d(zp, zr, zc, zl, nz, s);
         if (e != hipSuccess) return e;
     }
-    return dispatch_idx(best, d[0], b, s);
+    return d[0].fp16 ? dispatch_idx<f16_t>(best, d[0], b, s) : dispatch_idx<bf16_t>(best, d[0], b, s);
 }
 
 hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s) { return gemm_bf16_batch(&d, 1, false, nullptr, s); }

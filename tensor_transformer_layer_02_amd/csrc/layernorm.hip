@@ -48,6 +48,13 @@ __device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t* p) {
                  __uint_as_float(w[1] & 0xffff0000u)};
 }
 
+template <>
+__device__ __forceinline__ f32x4 ld4<f16_t>(const f16_t* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    using S = Store16<f16_t>;
+    return f32x4{S::lo(w[0]), S::hi(w[0]), S::lo(w[1]), S::hi(w[1])};
+}
+
 template <typename T>
 __device__ __forceinline__ void st4(T* p, const f32x4& v);
 template <>
@@ -57,6 +64,12 @@ __device__ __forceinline__ void st4<float>(float* p, const f32x4& v) {
 template <>
 __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const f32x4& v) {
     *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+}
+
+template <>
+__device__ __forceinline__ void st4<f16_t>(f16_t* p, const f32x4& v) {
+    using S = Store16<f16_t>;
+    *reinterpret_cast<u32x2*>(p) = u32x2{S::pack2(v[0], v[1]), S::pack2(v[2], v[3])};
 }
 
 // Sum of v over the workgroup, the same value in every thread.  red: 4 floats of LDS.
@@ -286,23 +299,37 @@ int nch_for(int cols) {
 // kernel's registers allow three 4-wave workgroups).
 int ln_bwd_bands(int64_t rows) { return (int)(rows < 768 ? rows : 768); }
 
+template <int NCH>
+hipError_t fwd_fmt(const LnFwdDesc& d, hipStream_t s) {
+    if (d.fmt == FMT_BF16) return launch_fwd<bf16_t, NCH>(d, s);
+    if (d.fmt == FMT_F16) return launch_fwd<f16_t, NCH>(d, s);
+    return launch_fwd<float, NCH>(d, s);
+}
+
+template <int NCH>
+hipError_t bwd_fmt(const LnBwdDesc& d, hipStream_t s) {
+    if (d.fmt == FMT_BF16) return launch_bwd<bf16_t, NCH>(d, s);
+    if (d.fmt == FMT_F16) return launch_bwd<f16_t, NCH>(d, s);
+    return launch_bwd<float, NCH>(d, s);
+}
+
 hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s) {
     if (d.rows <= 0) return hipSuccess;
     switch (nch_for(d.cols)) {
-        case 1: return d.bf16 ? launch_fwd<bf16_t, 1>(d, s) : launch_fwd<float, 1>(d, s);
-        case 2: return d.bf16 ? launch_fwd<bf16_t, 2>(d, s) : launch_fwd<float, 2>(d, s);
-        case 4: return d.bf16 ? launch_fwd<bf16_t, 4>(d, s) : launch_fwd<float, 4>(d, s);
-        default: return d.bf16 ? launch_fwd<bf16_t, 8>(d, s) : launch_fwd<float, 8>(d, s);
+        case 1: return fwd_fmt<1>(d, s);
+        case 2: return fwd_fmt<2>(d, s);
+        case 4: return fwd_fmt<4>(d, s);
+        default: return fwd_fmt<8>(d, s);
     }
 }
 
 hipError_t layernorm_bwd(const LnBwdDesc& d, hipStream_t s) {
     if (d.rows <= 0) return hipSuccess;
     switch (nch_for(d.cols)) {
-        case 1: return d.bf16 ? launch_bwd<bf16_t, 1>(d, s) : launch_bwd<float, 1>(d, s);
-        case 2: return d.bf16 ? launch_bwd<bf16_t, 2>(d, s) : launch_bwd<float, 2>(d, s);
-        case 4: return d.bf16 ? launch_bwd<bf16_t, 4>(d, s) : launch_bwd<float, 4>(d, s);
-        default: return d.bf16 ? launch_bwd<bf16_t, 8>(d, s) : launch_bwd<float, 8>(d, s);
+        case 1: return bwd_fmt<1>(d, s);
+        case 2: return bwd_fmt<2>(d, s);
+        case 4: return bwd_fmt<4>(d, s);
+        default: return bwd_fmt<8>(d, s);
     }
 }
 

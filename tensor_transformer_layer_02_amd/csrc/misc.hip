@@ -15,7 +15,7 @@ constexpr int CS_COLS = 64;         // columns per workgroup (8 groups of 8)
 
 // Partial column sums of a [rows, cols] matrix over one band of rows.  Thread
 // (row lane rl, column group cg) reads 8 consecutive columns per row with a
-// 16-byte load (bf16) or two (fp32); a wave covers 8 rows x 64 columns.
+// 16-byte load (16-bit formats) or two (fp32); a wave covers 8 rows x 64 columns.
 template <typename T>
 __global__ void __launch_bounds__(256) colsum_partial_kernel(const T* __restrict__ X, int64_t rows, int64_t cols,
                                                              int64_t ld, float* __restrict__ work) {
@@ -32,8 +32,8 @@ __global__ void __launch_bounds__(256) colsum_partial_kernel(const T* __restrict
                 const u32x4 v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] += __uint_as_float(v[q] << 16);
-                    acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+                    acc[2 * q] += Store16<T>::lo(v[q]);
+                    acc[2 * q + 1] += Store16<T>::hi(v[q]);
                 }
             } else {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(src);
@@ -109,12 +109,15 @@ __global__ void __launch_bounds__(256) sum_partials_kernel(int64_t rows, int64_t
 
 int64_t colsum_work_floats(int64_t cols) { return (int64_t)COLSUM_SPLITS * cols; }
 
-hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t ld, float* const out[3],
+hipError_t colsum(int fmt, const void* X, int64_t rows, int64_t cols, int64_t ld, float* const out[3],
                   int seg, float* work, hipStream_t s) {
     if (cols <= 0) return hipSuccess;
     dim3 g1((unsigned)((cols + CS_COLS - 1) / CS_COLS), COLSUM_SPLITS);
-    if (bf16)
+    if (fmt == FMT_BF16)
         hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, g1, dim3(256), 0, s, static_cast<const bf16_t*>(X), rows,
+                           cols, ld, work);
+    else if (fmt == FMT_F16)
+        hipLaunchKernelGGL(colsum_partial_kernel<f16_t>, g1, dim3(256), 0, s, static_cast<const f16_t*>(X), rows,
                            cols, ld, work);
     else
         hipLaunchKernelGGL(colsum_partial_kernel<float>, g1, dim3(256), 0, s, static_cast<const float*>(X), rows,
@@ -150,7 +153,7 @@ hipError_t zero_f32_2d(const float* const* p, const int64_t* rows, const int64_t
     return hipGetLastError();
 }
 
-hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const* parts, int nparts,
+hipError_t sum_partials(int fmt, int64_t rows, int64_t cols, const void* const* parts, int nparts,
                         const void* bias, float* out, hipStream_t s) {
     const int64_t n = rows * cols;
     if (n <= 0) return hipSuccess;
@@ -159,9 +162,12 @@ hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const
         Parts P;
         const int cnt = nparts - k0 < MAXP ? nparts - k0 : MAXP;
         for (int i = 0; i < MAXP; ++i) P.p[i] = i < cnt ? parts[k0 + i] : nullptr;
-        if (bf16)
+        if (fmt == FMT_BF16)
             hipLaunchKernelGGL(sum_partials_kernel<bf16_t>, grid, dim3(256), 0, s, rows, cols, P, cnt,
                                static_cast<const bf16_t*>(bias), k0 > 0 ? 1 : 0, out);
+        else if (fmt == FMT_F16)
+            hipLaunchKernelGGL(sum_partials_kernel<f16_t>, grid, dim3(256), 0, s, rows, cols, P, cnt,
+                               static_cast<const f16_t*>(bias), k0 > 0 ? 1 : 0, out);
         else
             hipLaunchKernelGGL(sum_partials_kernel<float>, grid, dim3(256), 0, s, rows, cols, P, cnt,
                                static_cast<const float*>(bias), k0 > 0 ? 1 : 0, out);

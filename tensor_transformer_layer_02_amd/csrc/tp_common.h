@@ -8,6 +8,10 @@
 namespace tp {
 
 typedef uint16_t bf16_t;  // bfloat16 storage (raw bits)
+struct f16_t {            // IEEE half storage (raw bits; a distinct type so templates can tell it apart)
+    uint16_t bits;
+};
+static_assert(sizeof(f16_t) == 2, "f16_t is two bytes");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -81,6 +85,9 @@ __device__ __forceinline__ float gelu_prime_sel(float u, bool tanh_form) {
     return tanh_form ? gelu_tanh_prime_f(u) : gelu_prime_f(u);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_hw;
+
 // Bit-level reinterpretations between 16-byte vector types.
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -97,12 +104,48 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// 32x32x16 fp16 MFMA, same operand and result layout as the bf16 one.
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// The 16-bit storage formats: widening of the low / high half of a packed
+// word, rounding of a pair to a packed word (round to nearest even), and the
+// matching 32x32x16 MFMA.
+template <typename T> struct Store16;
+template <> struct Store16<bf16_t> {
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf2(a, b); }
+    static __device__ __forceinline__ uint16_t from_f(float f) { return f2bf(f); }
+    static __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return mfma32x32x16(a, b, c);
+    }
+};
+template <> struct Store16<f16_t> {
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+        const f16x2_hw v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static __device__ __forceinline__ uint16_t from_f(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+    static __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return mfma32x32x16_f16(a, b, c);
+    }
+};
+
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f<f16_t>(f16_t v) { return (float)__builtin_bit_cast(_Float16, v.bits); }
 
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ f16_t from_f<f16_t>(float v) { return f16_t{__builtin_bit_cast(uint16_t, (_Float16)v)}; }
 
 }  // namespace tp

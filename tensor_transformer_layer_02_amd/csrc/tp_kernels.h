@@ -11,6 +11,9 @@ namespace tp {
 // to tell single-launch steps apart).
 void count_launch();
 
+// Storage formats of activations, weights and partials (the values of tp_dtype).
+enum Fmt : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_F16 = 2 };
+
 enum Epi : int {
     EPI_STORE = 0,      // C = acc (act dtype, or fp32 when out_f32)
     EPI_BIAS = 1,       // C = acc + bias[n]
@@ -46,6 +49,7 @@ struct GemmDesc {
     int epi = EPI_STORE;
     bool gelu_tanh = false;       // EPI_BIAS_GELU / EPI_GELU_BWD: the tanh form of GeLU
     bool concurrent = false;      // runs beside another launch (tile choice: co-resident tiles)
+    bool fp16 = false;            // 16-bit operands / outputs are IEEE half (else bfloat16)
 };
 
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
@@ -84,6 +88,7 @@ struct AttnDesc {
     const void* dO = nullptr;           // [T, w]
     float* Dq = nullptr;                // [batch, heads, seq]
     void* dqkv = nullptr;               // [T, 3w]
+    bool fp16 = false;                  // IEEE half storage (else bfloat16)
 };
 
 // The backward is three launches: D = rowsum(dO * O) first, then the dK/dV
@@ -97,11 +102,11 @@ hipError_t attn_bwd_f32(const AttnDesc& a, int part, hipStream_t s);
 // out[c] = sum_r X[r*ld + c] over rows, fp32, into up to 3 column segments of length seg.
 // Deterministic two-pass reduction; `work` holds colsum_work_floats(cols) floats.
 int64_t colsum_work_floats(int64_t cols);
-hipError_t colsum(bool bf16, const void* X, int64_t rows, int64_t cols, int64_t ld,
+hipError_t colsum(int fmt, const void* X, int64_t rows, int64_t cols, int64_t ld,
                   float* const out[3], int seg, float* work, hipStream_t s);
 
 // out = sum_p parts[p] + bias (fp32 out).
-hipError_t sum_partials(bool bf16, int64_t rows, int64_t cols, const void* const* parts,
+hipError_t sum_partials(int fmt, int64_t rows, int64_t cols, const void* const* parts,
                         int nparts, const void* bias, float* out, hipStream_t s);
 
 // ---- pre-LN residual stream (layernorm.hip) ----
@@ -113,7 +118,7 @@ constexpr int LN_MAXP = 16;  // partials per call
 struct LnFwdDesc {
     int64_t rows = 0;
     int cols = 0;
-    bool bf16 = false;               // dtype of parts, bias and y
+    int fmt = FMT_F32;               // format of parts, bias and y
     const void* parts[LN_MAXP] = {};
     int nparts = 0;
     const void* bias = nullptr;
@@ -136,7 +141,7 @@ hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s);
 struct LnBwdDesc {
     int64_t rows = 0;
     int cols = 0;
-    bool bf16 = false;               // dtype of dparts and dx_act
+    int fmt = FMT_F32;               // format of dparts and dx_act
     const float* x = nullptr;
     const float* gamma = nullptr;
     const float* mean = nullptr;

@@ -7,8 +7,8 @@ oracle take their inputs from here.
 Recipe: a torch CPU ``Generator`` seeded with ``1000 * cid + k``, where k is
 the tensor's index in TENSOR_ORDER; values are drawn as float32 ``randn`` and
 scaled (activations and the upstream gradient N(0, 1), weights N(0, 0.02),
-biases 0 unless ``bias_std`` is given), then rounded to bfloat16 with
-round-to-nearest-even for bf16 workloads.  The oracle receives the same
+biases 0 unless ``bias_std`` is given), then rounded to the storage
+format (bfloat16 or IEEE half) with round-to-nearest-even for 16-bit workloads.  The oracle receives the same
 (rounded) values widened to float64.
 """
 from __future__ import annotations
@@ -34,7 +34,7 @@ def tensor_shapes(cfg: LayerConfig) -> dict:
 
 
 def storage_dtype(cfg: LayerConfig) -> torch.dtype:
-    return torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[cfg.dtype]
 
 
 def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,

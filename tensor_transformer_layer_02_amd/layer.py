@@ -18,6 +18,7 @@ import torch
 
 from . import tpshard as tp
 from .configs import LayerConfig
+from .inputs import storage_dtype
 
 EPS = 1e-5
 
@@ -27,7 +28,7 @@ class PreLNLayer:
         self.cfg, self.t = cfg, cfg.degree
         self.dims = tp.dims_of(cfg)
         self.act = self.dims.act
-        self.dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+        self.dt = storage_dtype(cfg)
         dev = self.dev = torch.device(device)
         self.x = {k: v.to(dev).contiguous() for k, v in inputs.items()}
         T, h, F = cfg.tokens, cfg.hidden, cfg.ffn
@@ -134,7 +135,7 @@ class PreLNLayer:
         """Algorithmic HBM bytes of each LayerNorm / residual phase (every tensor read or
         written once; the backward's band partials counted)."""
         T, h, t = self.cfg.tokens, self.cfg.hidden, self.t
-        e = 2 if self.dt == torch.bfloat16 else 4
+        e = self.dt.itemsize
         nb = min(T, 768)
         # band partials: written, read, and their 32 group sums written and read
         part = lambda q: q * 2 * (nb + 32) * h * 4

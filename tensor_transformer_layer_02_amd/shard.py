@@ -11,6 +11,7 @@ import torch
 
 from . import tpshard as tp
 from .configs import LayerConfig
+from .inputs import storage_dtype
 
 
 class ShardRun:
@@ -19,7 +20,7 @@ class ShardRun:
         self.cfg = cfg
         self.degree = cfg.degree if degree is None else degree
         self.dims = tp.dims_of(cfg)
-        self.dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+        self.dt = storage_dtype(cfg)
         self.dev = torch.device(device)
         self.x = {k: v.to(self.dev).contiguous() for k, v in inputs.items()}
         T, h, F = cfg.tokens, cfg.hidden, cfg.ffn

@@ -15,7 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtpshard.so")
 
-TP_FP32, TP_BF16 = 0, 1
+TP_FP32, TP_BF16, TP_FP16 = 0, 1, 2
 TP_GELU_ERF, TP_GELU_TANH = 0, 1
 STATUS = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_EDIVIDE", 3: "TP_ESHARD", 4: "TP_EALIGN", 5: "TP_EDTYPE",
           6: "TP_EUNSUPPORTED", 7: "TP_EHIP", 8: "TP_ESIZE"}
@@ -95,7 +95,7 @@ def make_dims(batch, seq, hidden, heads, ffn, causal=True, act=TP_BF16, gelu=TP_
 
 def dims_of(cfg, act=None) -> tp_dims:
     if act is None:
-        act = TP_FP32 if cfg.dtype == "fp32" else TP_BF16
+        act = {"fp32": TP_FP32, "bf16": TP_BF16, "fp16": TP_FP16}[cfg.dtype]
     gelu = TP_GELU_TANH if getattr(cfg, "gelu", "erf") == "tanh" else TP_GELU_ERF
     return make_dims(cfg.batch, cfg.seq, cfg.hidden, cfg.heads, cfg.ffn, cfg.causal, act, gelu)
 
@@ -213,7 +213,7 @@ def saved_layout(dims, shard, degree):
     Hs = dims.heads // degree
     d = dims.hidden // dims.heads
     w = Hs * d
-    e = 2 if dims.act == TP_BF16 else 4
+    e = 4 if dims.act == TP_FP32 else 2
     a = lambda x: (x + 255) // 256 * 256
     mlp = {"U": (0, (T, Fs)), "Y": (a(T * Fs * e), (T, Fs))}
     attn = {"QKV": (0, (T, 3 * w)), "O": (a(T * 3 * w * e), (T, w)),

@@ -59,6 +59,10 @@ def d(batch=2, seq=64, hidden=128, heads=4, ffn=512, causal=1, act=tp.TP_BF16):
     (d(batch=0), 0, 1, 1),
     (d(causal=2), 0, 1, 1),
     (d(act=7), 0, 1, 5),
+    (d(act=3), 0, 1, 5),
+    (d(act=tp.TP_FP16), 0, 2, 0),
+    (d(hidden=120, heads=4, act=tp.TP_FP16), 0, 1, 6),  # fp16 head dims are those of bf16
+    (d(hidden=96, heads=3, ffn=384, act=tp.TP_FP16), 0, 3, 6),
     (d(hidden=120, heads=4), 0, 1, 6),   # d = 30: bf16 head dims are 32/64/96/128
     (d(hidden=128, heads=2), 0, 2, 0),   # d = 64, w = 64
     (d(hidden=96, heads=3, ffn=384), 0, 3, 6),  # w = 32 is not a multiple of 64 (bf16)

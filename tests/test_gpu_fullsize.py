@@ -35,22 +35,24 @@ def _cpu(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-@pytest.mark.parametrize("name,nrows,seq_idx,head_idx", [
-    ("gpt8b", 24, 5, 3),
-    ("bert4b", 24, 11, 4),
-    ("g30b_t4", 8, 2, 13),
-    ("g30b_t1", 6, 1, 40),
+@pytest.mark.parametrize("name,nrows,seq_idx,head_idx,dtype", [
+    ("gpt8b", 24, 5, 3, "bf16"),
+    ("bert4b", 24, 11, 4, "bf16"),
+    ("g30b_t4", 8, 2, 13, "bf16"),
+    ("g30b_t1", 6, 1, 40, "bf16"),
+    ("gpt8b", 16, 7, 6, "fp16"),
 ])
-def test_full_size_sampled(name, nrows, seq_idx, head_idx):
+def test_full_size_sampled(name, nrows, seq_idx, head_idx, dtype):
     from tensor_transformer_layer_02_amd.shard import ShardRun
-    cfg = CONFIGS[name].with_(backward=True)
-    _say(f"[{name}] full size: T={cfg.tokens} h={cfg.hidden} F={cfg.ffn} H={cfg.heads} t={cfg.degree} shard 0")
+    cfg = CONFIGS[name].with_(backward=True, dtype=dtype)
+    _say(f"[{name}] full size: T={cfg.tokens} h={cfg.hidden} F={cfg.ffn} H={cfg.heads} t={cfg.degree} shard 0 "
+         f"{dtype}")
     inp = make_inputs(cfg)
     run = ShardRun(cfg, inp, shards=[0])
     run.step(0)
     torch.cuda.synchronize()
     sv = run.saved(0)
-    tol = TOL["bf16"]
+    tol = TOL[dtype]
     rep = []
     T, h, F, t, s = cfg.tokens, cfg.hidden, cfg.ffn, cfg.degree, cfg.seq
     p = {k: as_f64(v) for k, v in inp.items()}

@@ -1,12 +1,12 @@
 """The GeLU epilogues of the FFN GEMMs checked elementwise on a grid of 1600 inputs over [-8, 8],
-for both forms (exact erf and tanh approximation) and both dtypes.
+for both forms (exact erf and tanh approximation) and every dtype.
 
 The FFN shard is set up so that U = X A + b1 is the grid itself and dY = dZ B^T is one:
 X[r, 0] = 1, A[0, c] = u_c (all else 0), B[c, 0] = 1, dZ[r, 0] = 1.  Then the saved Y is
 GeLU(u_c) (fused bias+GeLU epilogue) and, over T = 8 rows, dA[0, c] = 8 * GeLU'(u_c) (fused
 GeLU' epilogue, summed exactly).  Tolerances: fp32 |err| <= 4e-6 (the epilogues' erf approximation and the
 hardware exp2 and reciprocal: a few fp32 ulps of values up to 1.13); bf16 that plus 2^-8
-relative (one rounding of the output)."""
+relative (one rounding of the output), fp16 that plus 2^-11 relative."""
 from __future__ import annotations
 
 import numpy as np
@@ -20,14 +20,14 @@ from tensor_transformer_layer_02_amd.inputs import as_f64
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("form", ["erf", "tanh"])
 def test_gelu_epilogues_on_a_grid(dtype, form):
     from tensor_transformer_layer_02_amd.shard import ShardRun
     T, h, F = 8, 64, 1600
     cfg = LayerConfig(160, f"gelu_grid_{form}_{dtype}", 1, T, h, 1, F, 1, True, dtype, True, gelu=form)
     print(f"[gelu grid] {form} {dtype}", flush=True)
-    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
     grid = torch.linspace(-8.0, 8.0, F, dtype=torch.float32).to(dt)
     z = lambda *s: torch.zeros(s, dtype=dt)
     X, A, B, dZ = z(T, h), z(h, F), z(F, h), z(T, h)
@@ -51,8 +51,9 @@ def test_gelu_epilogues_on_a_grid(dtype, form):
     if dtype == "fp32":
         tol_y = tol_g = np.full(F, 4e-6)
     else:
-        tol_y = np.abs(ref_y) * 2.0 ** -8 + 4e-6
-        tol_g = np.abs(ref_g) * 2.0 ** -8 + 4e-6
+        rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+        tol_y = np.abs(ref_y) * rel + 4e-6
+        tol_g = np.abs(ref_g) * rel + 4e-6
     for r in range(T):
         bad = np.abs(y[r] - ref_y) > tol_y
         assert not bad.any(), (r, u[bad][:4], y[r][bad][:4], ref_y[bad][:4])

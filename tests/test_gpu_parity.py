@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on the same seeded inputs.
 
 Tolerance (max |gpu - oracle| / max |oracle| per output tensor): 1e-4 for fp32 workloads,
-2e-2 for bf16 workloads with fp32 accumulation.
+2e-2 for bf16 and 3e-3 for fp16 (IEEE half) workloads with fp32 accumulation.
 """
 from __future__ import annotations
 
@@ -91,10 +91,22 @@ def test_small_bf16_all_shards(case):
     _say(f"[{name}] " + "; ".join(f"{n}={e:.1e}" for n, e in report))
 
 
+@pytest.mark.parametrize("case", SMALL_BF16, ids=[c[0].replace("bf16", "") + "_fp16" for c in SMALL_BF16])
+def test_small_fp16_all_shards(case):
+    """The IEEE-half storage variant (tp_dims.act = TP_FP16) on the same shapes as the bf16
+    cases: fp16 MFMAs with fp32 accumulation, every output against the oracle to 3e-3."""
+    name, b, s, h, H, F, t, causal = case
+    cfg = LayerConfig(170 + SMALL_BF16.index(case), name + "_fp16", b, s, h, H, F, t, causal, "fp16", True)
+    report = []
+    run_all_shards(cfg, 0.02, report)
+    _say(f"[{cfg.name}] " + "; ".join(f"{n}={e:.1e}" for n, e in report))
+
+
 @pytest.mark.parametrize("cfg", [
     CONFIGS["tiny"].with_(cid=130, name="tiny_tanh", gelu="tanh", backward=True),
     LayerConfig(131, "bf16_d96_tanh", 2, 130, 384, 4, 1536, 2, True, "bf16", True, gelu="tanh"),
-], ids=["tiny_fp32_tanh", "bf16_d96_tanh"])
+    LayerConfig(134, "fp16_d64_tanh", 3, 100, 256, 4, 1024, 2, False, "fp16", True, gelu="tanh"),
+], ids=["tiny_fp32_tanh", "bf16_d96_tanh", "fp16_d64_tanh"])
 def test_tanh_gelu_variant_all_shards(cfg):
     """The tanh-form GeLU variant (tp_dims.gelu = TP_GELU_TANH) against the oracle's tanh form."""
     report = []
