@@ -143,6 +143,10 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="time the whole pre-LN layer instead (all t shards of both sublayers plus the "
                          "residual / LayerNorm kernels, on one GPU) and print its own JSON line")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor library (hipBLASLt through torch.matmul, plain GEMMs with "
+                         "contiguous operands, 16-bit outputs, no epilogues) on the GEMM shapes of the "
+                         "step, for context, and print one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -180,6 +184,8 @@ def main():
     if cfg.dtype != args.dtype and cfg.dtype != "fp32":
         cfg = cfg.with_(dtype=args.dtype)
     K, W = args.steps, args.warmup
+    if args.vendor_gemm:
+        return vendor_gemm(cfg, K, W)
     if args.layer:
         return bench_layer(cfg, K, W)
     log(f"[bench] {cfg.note}: T={cfg.tokens} h={cfg.hidden} F/t={cfg.ffn_per_shard} H/t={cfg.heads_per_shard} "
@@ -295,6 +301,43 @@ def main():
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
+
+
+def vendor_gemm(cfg, K, W):
+    """The vendor GEMM (hipBLASLt via torch.matmul) on the shapes of each GEMM step of the shard,
+    [M, K] x [K, N] with both operands contiguous and a 16-bit output (no bias, GeLU or fp32
+    output): a context figure for the library's kernels, not part of the path."""
+    import torch
+
+    T, h, Fs, w = cfg.tokens, cfg.hidden, cfg.ffn_per_shard, cfg.attn_width
+    dt = torch.float16 if cfg.dtype == "fp16" else torch.bfloat16
+    steps = {  # step: list of (M, K, N)
+        "MLP_UP": [(T, h, Fs)], "MLP_DOWN": [(T, Fs, h)], "QKV": [(T, h, 3 * w)], "ATTN_OUT": [(T, w, h)],
+        "MLP_DU": [(T, h, Fs)], "MLP_DW": [(Fs, T, h), (h, T, Fs)], "MLP_DX": [(T, Fs, h)],
+        "ATTN_DO": [(T, h, w)], "ATTN_DW": [(h, T, 3 * w)], "ATTN_DWO": [(w, T, h)], "ATTN_DX": [(T, 3 * w, h)],
+    }
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for name, gemms in steps.items():
+        ops = [(torch.randn((m, k), generator=gen, device="cuda", dtype=dt),
+                torch.randn((k, n), generator=gen, device="cuda", dtype=dt)) for m, k, n in gemms]
+        for _ in range(W):
+            for a, b in ops:
+                torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            for a, b in ops:
+                torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K * 1e3
+        fl = sum(2 * m * k * n for m, k, n in gemms)
+        rows.append({"step": name, "avg_us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 1)})
+        log(f"  {name:<10} {us:9.2f} us  {rows[-1]['tflops']:8.1f} TF/s")
+    print(json.dumps({"vendor_gemm": "hipBLASLt via torch.matmul", "dtype": cfg.dtype, "steps": K,
+                      "warmup": W, "workload": cfg.name, "gemms": rows}), flush=True)
 
 
 def bench_layer(cfg, K, W):
