@@ -14,6 +14,8 @@ Prints ONE JSON line on stdout:
                    dense MFMA peak, timed live with HIP events on its stream
   cpu_baseline     the float64 CPU oracle timed on this host on a bounded sample
                    of the same workload (a baseline, not a target)
+  step_spread      median / min of single steps (an event pair around each), warm and
+                   with a 512 MiB write before each step (cold Infinity Cache)
   kernels          per-step breakdown (average duration, TFLOP/s or GB/s)
 """
 from __future__ import annotations
@@ -66,6 +68,16 @@ def step_costs(cfg):
         "ATTN_DBIAS": (0, 3 * T * w * e + 3 * w * 4),
         "ATTN_DX": (g(T, h, 3 * w), (3 * T * w + 3 * w * h + T * h) * e),
     }
+
+
+def peak_clock_mhz():
+    """hipDeviceAttributeClockRate of device 0 (kHz in HIP) in MHz, from the runtime torch loaded."""
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    v = ctypes.c_int(0)
+    HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5
+    if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE, 0) != 0:
+        return None
+    return v.value // 1000
 
 
 class HipEvents:
@@ -129,7 +141,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first: after idle the GPU needs ~25 steps (~25 ms of load) to reach "
+                         "its steady clock; per-step times fall from ~1.1 ms to ~0.925 ms over them")
     ap.add_argument("--config", default="gpt8b")
     ap.add_argument("--shard", type=int, default=0)
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
@@ -195,7 +209,9 @@ def main():
     step = lambda: run.step(args.shard, recompute=args.recompute)
     flops = shard_flops(cfg, backward=True)["total"]
     prop = torch.cuda.get_device_properties(0)
-    log(f"[bench] device {prop.name} CUs={prop.multi_processor_count} peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
+    clock_mhz = peak_clock_mhz()
+    log(f"[bench] device {prop.name} ({prop.gcnArchName}) CUs={prop.multi_processor_count} peak clock "
+        f"{clock_mhz} MHz, peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
 
     for _ in range(W):
         step()
@@ -215,6 +231,34 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.4f} ms/step  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)"
         f"  wall {wall:.3f}s")
+
+    # ---- spread over single steps (an event pair around each), then a cold-cache figure:
+    # a 512 MiB write (twice the 256 MB Infinity Cache) before each step evicts weights and inputs
+    def single_steps(n, before=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            if before is not None:
+                before()
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    def median(v):
+        n = len(v)
+        return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+    warm = single_steps(K)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = single_steps(min(K, 10), before=lambda: scratch.fill_(1))
+    del scratch
+    spread = {"warm_median_ms": round(median(warm), 5), "warm_min_ms": round(warm[0], 5),
+              "cold_median_ms": round(median(cold), 5), "cold_min_ms": round(cold[0], 5),
+              "cold_tflops": round(flops / (median(cold) * 1e-3) / 1e12, 2), "cold_steps": len(cold),
+              "note": "event pair around each single step; cold: 512 MiB written before each step"}
+    log(f"[bench] single steps: warm median {spread['warm_median_ms']:.4f} ms (min {spread['warm_min_ms']:.4f}), "
+        f"cold-cache median {spread['cold_median_ms']:.4f} ms ({spread['cold_tflops']} TFLOP/s)")
 
     # ---- per-kernel timing: HIP event pairs around each step's launch, same stream ----
     kernels, roof = [], None
@@ -294,10 +338,15 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.note}", "batch": cfg.batch, "seq": cfg.seq,
                    "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads, "ffn": cfg.ffn,
                    "degree": cfg.degree, "shard": args.shard, "causal": cfg.causal,
-                   "flops_per_step": flops, "parallelism": "one tp shard on one GPU (no collectives)",
+                   "flops_per_step": flops,
+                   "flops_per_step_dense_attention": shard_flops(cfg.with_(causal=False), backward=True)["total"],
+                   "parallelism": "one tp shard on one GPU (no collectives)",
                    "activations": "recomputed in the backward" if args.recompute else "saved"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_spread": spread,
+        "gpu": {"name": prop.name, "arch": prop.gcnArchName, "cus": prop.multi_processor_count,
+                "peak_clock_mhz": clock_mhz},
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
