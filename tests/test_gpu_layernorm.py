@@ -202,5 +202,8 @@ def test_preln_layer_matches_oracle(case):
               "ln2_db", "dWk"):
         check(k, layer.grads[k], bwd[k], tol, rep)
     # dbk is zero in exact arithmetic (a key bias shifts a query's scores by one constant)
-    assert float(layer.grads["dbk"].abs().max()) <= tol * float(layer.grads["dbq"].abs().max() + 1e-30)
+    # against the scale of the attention's bias gradients (with one key per query dQ and dK are
+    # exactly zero too, so dbq alone is no scale for the rounding noise)
+    scale = max(float(layer.grads["dbq"].abs().max()), float(layer.grads["dbv"].abs().max()))
+    assert float(layer.grads["dbk"].abs().max()) <= tol * scale
     _say(f"[{name}] " + "; ".join(f"{n}={e:.1e}" for n, e in rep))
