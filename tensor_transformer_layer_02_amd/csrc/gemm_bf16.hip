@@ -27,7 +27,12 @@
 //    GemmCore.  Operands travel global -> registers -> LDS: buffer loads are
 //    issued one or two steps before their data is stored, and every LDS read,
 //    LDS write and global load is paired with an MFMA by scheduling hints, in
-//    a branch-free steady state.
+//    a branch-free steady state.  The K-group tile instead loads straight into
+//    LDS (buffer loads with the LDS flag) through three slots, two steps
+//    ahead: no registers hold operands in transit and no LDS stores are
+//    issued, which is what bounds the register-staged loop (timing copies
+//    without the MFMAs run the MLP weight-gradient pair in 109 of its 150 us,
+//    without the LDS stores in 83).
 //  * Workgroup ids are remapped so that each XCD (ids are dealt round-robin
 //    over the 8 XCDs) owns a compact block of tiles that share A rows and B
 //    columns in its L2.
@@ -153,6 +158,16 @@ struct KOperand {
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + NWV * i) * 1024 + lane * 16) = v[i];
     }
+    // The same chunks straight into the LDS stage `dst` (buffer loads with the
+    // LDS flag: lane l's 16 bytes land at the instruction's base + 16 l, the
+    // bytes store() would write), no registers involved.
+    __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int krem, char* dst, int wave) const {
+        const bool kin = krem >= BK || koff < krem;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave + NWV * i) * 1024), 16,
+                                                     kin ? off[i] : OOB, 0, 0, 0);
+    }
 };
 
 // One stage of an M/N-contiguous operand, [64][COLS] (k rows), loaded by NWV waves.
@@ -186,6 +201,13 @@ struct MNOperand {
     __device__ __forceinline__ void store(char* dst, int wave, int lane, const u32x4 (&v)[NI]) const {
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(dst + (wave + NWV * i) * 1024 + lane * 16) = v[i];
+    }
+    __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int krem, char* dst, int wave) const {
+        const int klim = krem >= BK ? BK : krem;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave + NWV * i) * 1024), 16,
+                                                     (o0 + 1024 * NWV * i) / ROWB < klim ? off[i] : OOB, 0, 0, 0);
     }
 };
 
@@ -336,6 +358,10 @@ struct GemmCore {
     // global loads run two steps ahead; the 256 x 256 tile has no room for
     // the second set (except with two plain K-contiguous operands) and loads
     // one step ahead.
+    // LDS slots: two for the register-staged pipeline; the K-group tiles load
+    // straight into LDS through three, two steps ahead.
+    static constexpr int RINGS = KG == 2 ? 3 : STAGES;
+    static constexpr int NLD = LA::NI + LB::NI;  // direct loads per thread and step
     static constexpr int NSET = (KG == 2 || (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG)))) ? 1 : 2;
 
     char* smem;
@@ -407,14 +433,34 @@ struct GemmCore {
     // K range every lane takes the out-of-range offset; the base then stays
     // at k = 0 (no branch: a conditional 64-bit multiply would become one and
     // split the scheduling region).
-    __device__ __forceinline__ void load_a(int kt, u32x4 (&v)[LA::NI]) const {
-        const int k0 = (kbase + kt) * BK, krem = kend - k0;
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_a(int kt, int& krem) const {
+        const int k0 = (kbase + kt) * BK;
+        krem = kend - k0;
         const int kc = krem > 0 ? k0 : 0;
         const int64_t e = kadv(AK, kc, lda);
-        la.load(make_rsrc(abase + e, abytes - (uint32_t)(e * 2)), krem, v);
+        return make_rsrc(abase + e, abytes - (uint32_t)(e * 2));
+    }
+    __device__ __forceinline__ void load_a(int kt, u32x4 (&v)[LA::NI]) const {
+        int krem;
+        const __amdgpu_buffer_rsrc_t rs = rsrc_a(kt, krem);
+        la.load(rs, krem, v);
     }
     __device__ __forceinline__ void load_b(int kt, u32x4 (&v)[LB::NI]) const {
-        const int k0 = (kbase + kt) * BK, krem = kend - k0;
+        int krem;
+        const __amdgpu_buffer_rsrc_t rs = rsrc_b(kt, krem);
+        lb.load(rs, krem, v);
+    }
+    // Direct global -> LDS loads of step kt into the stage at `dst` (the K-group tiles).
+    __device__ __forceinline__ void load_lds(int kt, char* dst) const {
+        int krem;
+        const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(kt, krem);
+        la.load_lds(ra_, krem, dst, wave);
+        const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(kt, krem);
+        lb.load_lds(rb_, krem, dst + A_BYTES, wave);
+    }
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(int kt, int& krem) const {
+        const int k0 = (kbase + kt) * BK;
+        krem = kend - k0;
         const int kc = krem > 0 ? k0 : 0;
         int sg = 0, kl = kc;
         if constexpr (BKSEG) {
@@ -427,7 +473,7 @@ struct GemmCore {
         const uint64_t s1 = sg == 1, s2 = sg == 2;
         const bf16_t* b = reinterpret_cast<const bf16_t*>(bsel[0] + s1 * bsel[1] + s2 * bsel[2]);
         const uint32_t nb = bbsel[0] + (uint32_t)s1 * bbsel[1] + (uint32_t)s2 * bbsel[2];
-        lb.load(make_rsrc(b + e, nb - (uint32_t)(e * 2)), krem, v);
+        return make_rsrc(b + e, nb - (uint32_t)(e * 2));
     }
 
     // Registers -> LDS slot (swizzled layouts).
@@ -438,8 +484,8 @@ struct GemmCore {
         lb.store(smem + slot * STAGE + A_BYTES, wave, lane, v);
     }
 
-    __device__ __forceinline__ void read_sub(int slot, int kk, HF& F) const {
-        const char* as = smem + slot * STAGE;
+    __device__ __forceinline__ void read_sub(int slot, int kk, HF& F) const { read_at(smem + slot * STAGE, kk, F); }
+    __device__ __forceinline__ void read_at(const char* as, int kk, HF& F) const {
         const char* bs = as + A_BYTES;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -479,42 +525,48 @@ struct GemmCore {
         interleave<NM - PRE, NRD, 0, 0>();
     }
 
-    // KG == 2: the group's two sub-steps kk0, kk0+1 of step kt; on entry Fa holds kk0.
-    template <int P>
-    __device__ __forceinline__ void step2(int kt, HF& Fa, HF& Fb) {
-        constexpr int R = 0;
+    // KG == 2: the group's two sub-steps kk0, kk0+1 of step kt, whose stage is
+    // `cur`; on entry Fa holds kk0.  The direct loads of step kt+2 go to `dst`,
+    // the slot last read in step kt-1 (before the previous barrier).  Before
+    // this step's barrier each thread waits for its loads of step kt+1 (all but
+    // the NLD just issued), so the barrier publishes `nxt`.  The three slots
+    // come in as distinct restrict pointers: the compiler then knows that the
+    // reads of `nxt` after the barrier do not touch the slot still being
+    // loaded, and does not wait for those loads (without that it waits for
+    // every load in flight before the first LDS read after each barrier).
+    __device__ __forceinline__ void step2(int kt, HF& Fa, HF& Fb, const char* __restrict__ cur,
+                                          const char* __restrict__ nxt, char* __restrict__ dst) {
         run_mfmas<ST, 0, NM>(acc, Fa);
-        read_sub(P, kk0 + 1, Fb);
-        store_a(P ^ 1, ra[R]);
-        load_a(kt + 2, ra[R]);
-        store_b(P ^ 1, rb[R]);
-        load_b(kt + 2, rb[R]);
-        interleave<NM, NRD, LA::NI + LB::NI, LA::NI + LB::NI>();
+        read_at(cur, kk0 + 1, Fb);
+        load_lds(kt + 2, dst);
+        interleave<NM, NRD, 0, NLD>();
         __builtin_amdgcn_sched_barrier(0);
-        wait_lgkm();
+        wait_vm_lgkm<NLD>();
         run_mfmas<ST, 0, PRE>(acc, Fb);
         stage_barrier();
         run_mfmas<ST, PRE, NM>(acc, Fb);
-        read_sub(P ^ 1, kk0, Fa);
+        read_at(nxt, kk0, Fa);
         interleave<NM - PRE, NRD, 0, 0>();
     }
 
     __device__ __forceinline__ void run() {
         if (nk <= 0) return;
         if constexpr (KG == 2) {
-            load_a(0, ra[0]);
-            load_b(0, rb[0]);
-            store_a(0, ra[0]);
-            store_b(0, rb[0]);
-            load_a(1, ra[0]);
-            load_b(1, rb[0]);
-            wait_lgkm();
+            char* const s0 = smem;
+            char* const s1 = smem + STAGE;
+            char* const s2 = smem + 2 * STAGE;
+            load_lds(0, s0);
+            load_lds(1, s1);
+            wait_vm_lgkm<NLD>();
             stage_barrier();
             HF Fa, Fb;
-            read_sub(0, kk0, Fa);
-            for (int kt = 0; kt < nk; kt += 2) {
-                step2<0>(kt, Fa, Fb);
-                step2<1>(kt + 1, Fa, Fb);
+            read_at(s0, kk0, Fa);
+            // Up to two more steps than the K range: their loads are out of
+            // range, so they read zeros and add nothing.
+            for (int kt = 0; kt < nk; kt += 3) {
+                step2(kt, Fa, Fb, s0, s1, s2);
+                step2(kt + 1, Fa, Fb, s1, s2, s0);
+                step2(kt + 2, Fa, Fb, s2, s0, s1);
             }
             wait_vm_lgkm<0>();
             return;
@@ -607,7 +659,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV, KG, ST>;
     constexpr int NT = 64 * NWV / KG;  // epilogue threads (the first K group)
     constexpr int HR = NWV / KG / 4;   // wave rows per half tile
-    constexpr int RING = STAGES * Core::STAGE;
+    constexpr int RING = Core::RINGS * Core::STAGE;
     // fp32 epilogues (weight gradients, GeLU') stage half a tile at a time as
     // fp32; the bf16 ones stage the whole tile as bf16.
     constexpr bool F32STAGE = OUTF32 || EPI == EPI_GELU_BWD;
