@@ -361,6 +361,11 @@ struct GemmCore {
     // LDS slots: two for the register-staged pipeline; the K-group tiles load
     // straight into LDS through three, two steps ahead.
     static constexpr int RINGS = KG == 2 ? 3 : STAGES;
+    // The 8-wave 256 x 192 tile: A goes straight into LDS through three slots
+    // (two steps ahead), B through registers into two slots (three A slots
+    // plus two B slots = 144 KB; three whole stages would not fit).
+    static constexpr bool ADIRECT = KG == 1 && BM == 256 && BN == 192 && NWV == 8;
+    static constexpr int LDS_BYTES = ADIRECT ? 3 * A_BYTES + 2 * B_BYTES : RINGS * STAGE;
     static constexpr int NLD = LA::NI + LB::NI;  // direct loads per thread and step
     static constexpr int NSET = (KG == 2 || (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG)))) ? 1 : 2;
 
@@ -458,6 +463,11 @@ struct GemmCore {
         const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(kt, krem);
         lb.load_lds(rb_, krem, dst + A_BYTES, wave);
     }
+    __device__ __forceinline__ void load_lds_a(int kt, char* dst) const {
+        int krem;
+        const __amdgpu_buffer_rsrc_t rs = rsrc_a(kt, krem);
+        la.load_lds(rs, krem, dst, wave);
+    }
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(int kt, int& krem) const {
         const int k0 = (kbase + kt) * BK;
         krem = kend - k0;
@@ -485,8 +495,8 @@ struct GemmCore {
     }
 
     __device__ __forceinline__ void read_sub(int slot, int kk, HF& F) const { read_at(smem + slot * STAGE, kk, F); }
-    __device__ __forceinline__ void read_at(const char* as, int kk, HF& F) const {
-        const char* bs = as + A_BYTES;
+    __device__ __forceinline__ void read_at(const char* as, int kk, HF& F) const { read_ab(as, as + A_BYTES, kk, F); }
+    __device__ __forceinline__ void read_ab(const char* as, const char* bs, int kk, HF& F) const {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             if constexpr (AK) F.a[i] = frag_k(as, wm * WTM + i * 32, kk, lane);
@@ -549,8 +559,92 @@ struct GemmCore {
         interleave<NM - PRE, NRD, 0, 0>();
     }
 
+    // ADIRECT step kt: A stages at ca (this step), na (next), da (free: the
+    // loads of A for step kt+2 go there, in sub-step 0); B stages at cb, nb.
+    // Sub-step 1 stores B of step kt+1 (registers `rbv`, loaded two steps
+    // earlier) to nb and loads B of step kt+3 into the same registers.  Loads
+    // are issued in the order A(kt+2), B(kt+3) per step, so before the barrier
+    // vmcnt(LA::NI + 2 LB::NI) leaves only B(kt+2), A(kt+2), B(kt+3) in flight:
+    // A(kt+1) has landed, and with this thread's LDS stores done the barrier
+    // publishes na and nb.  The slots are restrict pointers so that the
+    // compiler does not wait for the loads into da before reading na.
+    __device__ __forceinline__ void stepa(int kt, HF& Fa, HF& Fb, const char* __restrict__ ca,
+                                          const char* __restrict__ na, char* __restrict__ da,
+                                          const char* __restrict__ cb, char* __restrict__ nb,
+                                          u32x4 (&rbv)[LB::NI]) {
+        run_mfmas<ST, 0, NM>(acc, Fa);
+        read_ab(ca, cb, 1, Fb);
+        load_lds_a(kt + 2, da);
+        interleave<NM, NRD, 0, LA::NI>();
+        run_mfmas<ST, 0, NM>(acc, Fb);
+        read_ab(ca, cb, 2, Fa);
+        lb.store(nb, wave, lane, rbv);
+        load_b(kt + 3, rbv);
+        interleave<NM, NRD, LB::NI, LB::NI>();
+        run_mfmas<ST, 0, NM>(acc, Fa);
+        read_ab(ca, cb, 3, Fb);
+        interleave<NM, NRD, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm<LA::NI + 2 * LB::NI>();
+        run_mfmas<ST, 0, PRE>(acc, Fb);
+        stage_barrier();
+        run_mfmas<ST, PRE, NM>(acc, Fb);
+        read_ab(na, nb, 0, Fa);
+        interleave<NM - PRE, NRD, 0, 0>();
+    }
+
     __device__ __forceinline__ void run() {
         if (nk <= 0) return;
+        if constexpr (ADIRECT) {
+            char* const a0 = smem;
+            char* const a1 = smem + A_BYTES;
+            char* const a2 = smem + 2 * A_BYTES;
+            char* const b0 = smem + 3 * A_BYTES;
+            char* const b1 = b0 + B_BYTES;
+            // B of step j travels in register set j % 2
+            load_lds_a(0, a0);
+            load_b(0, rb[0]);
+            lb.store(b0, wave, lane, rb[0]);
+            load_b(1, rb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_lds_a(1, a1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(2, rb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lgkm<LA::NI + 2 * LB::NI>();
+            stage_barrier();
+            HF Fa, Fb;
+            read_ab(a0, b0, 0, Fa);
+            // Whole rounds of six steps (the slot pattern repeats every six),
+            // then the remaining 0..5 steps.  No exit from inside the loop: an
+            // early exit makes the compiler wait for every load in flight at
+            // the top of each round.
+            int kt = 0;
+            for (; kt + 6 <= nk; kt += 6) {
+                stepa(kt, Fa, Fb, a0, a1, a2, b0, b1, rb[1]);
+                stepa(kt + 1, Fa, Fb, a1, a2, a0, b1, b0, rb[0]);
+                stepa(kt + 2, Fa, Fb, a2, a0, a1, b0, b1, rb[1]);
+                stepa(kt + 3, Fa, Fb, a0, a1, a2, b1, b0, rb[0]);
+                stepa(kt + 4, Fa, Fb, a1, a2, a0, b0, b1, rb[1]);
+                stepa(kt + 5, Fa, Fb, a2, a0, a1, b1, b0, rb[0]);
+            }
+            const int rem = nk - kt;
+            if (rem > 0) {
+                stepa(kt, Fa, Fb, a0, a1, a2, b0, b1, rb[1]);
+                if (rem > 1) {
+                    stepa(kt + 1, Fa, Fb, a1, a2, a0, b1, b0, rb[0]);
+                    if (rem > 2) {
+                        stepa(kt + 2, Fa, Fb, a2, a0, a1, b0, b1, rb[1]);
+                        if (rem > 3) {
+                            stepa(kt + 3, Fa, Fb, a0, a1, a2, b1, b0, rb[0]);
+                            if (rem > 4) stepa(kt + 4, Fa, Fb, a1, a2, a0, b0, b1, rb[1]);
+                        }
+                    }
+                }
+            }
+            wait_vm_lgkm<0>();
+            return;
+        }
         if constexpr (KG == 2) {
             char* const s0 = smem;
             char* const s1 = smem + STAGE;
@@ -659,7 +753,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     using Core = GemmCore<BM, BN, AK, BKC, BKSEG, NWV, KG, ST>;
     constexpr int NT = 64 * NWV / KG;  // epilogue threads (the first K group)
     constexpr int HR = NWV / KG / 4;   // wave rows per half tile
-    constexpr int RING = Core::RINGS * Core::STAGE;
+    constexpr int RING = Core::LDS_BYTES;
     // fp32 epilogues (weight gradients, GeLU') stage half a tile at a time as
     // fp32; the bf16 ones stage the whole tile as bf16.
     constexpr bool F32STAGE = OUTF32 || EPI == EPI_GELU_BWD;
