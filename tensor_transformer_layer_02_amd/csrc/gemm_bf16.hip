@@ -317,6 +317,12 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
+// Workgroups per CU a tile shape is built for (registers: 512 / occupancy per lane).
+template <int BM, int BN, int NWV>
+constexpr int tile_occupancy() {
+    return NWV == 8 ? 1 : BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
+}
+
 // Main loop of one workgroup tile: operand loaders, the LDS ring and the
 // accumulators.  (Written as a struct rather than lambdas inside the kernel:
 // closure types in a kernel template defeat the host-side stub emission of
@@ -361,13 +367,15 @@ struct GemmCore {
     // LDS slots: two for the register-staged pipeline; the K-group tiles load
     // straight into LDS through three, two steps ahead.
     static constexpr int RINGS = KG == 2 ? 3 : STAGES;
-    // The 8-wave 256 x 192 tile: A goes straight into LDS through three slots
-    // (two steps ahead), B through registers into two slots (three A slots
-    // plus two B slots = 144 KB; three whole stages would not fit).
-    static constexpr bool ADIRECT = KG == 1 && BM == 256 && BN == 192 && NWV == 8;
-    static constexpr int LDS_BYTES = ADIRECT ? 3 * A_BYTES + 2 * B_BYTES : RINGS * STAGE;
     static constexpr int NLD = LA::NI + LB::NI;  // direct loads per thread and step
     static constexpr int NSET = (KG == 2 || (BM == 256 && BN == 256 && (NWV == 8 || !(AK && BKC && !BKSEG)))) ? 1 : 2;
+    // The 8-wave 256 x 192 tile: A goes straight into LDS through three slots
+    // (two steps ahead), B through two register sets into two slots (three A
+    // slots plus two B slots = 144 KB; three whole stages would not fit).
+    // Only this one-per-CU tile: the same pipeline on the 4-wave tiles that
+    // run two or four per CU gave intermittently wrong blocks on the GPU.
+    static constexpr bool ADIRECT = KG == 1 && NSET == 2 && NWV == 8 && BM == 256 && BN == 192;
+    static constexpr int LDS_BYTES = ADIRECT ? 3 * A_BYTES + 2 * B_BYTES : RINGS * STAGE;
 
     char* smem;
     int lane, wave, wm, wn, nk, kk0;
@@ -688,12 +696,6 @@ struct GemmCore {
         wait_vm_lgkm<0>();
     }
 };
-
-// Workgroups per CU a tile shape is built for (registers: 512 / occupancy per lane).
-template <int BM, int BN, int NWV>
-constexpr int tile_occupancy() {
-    return NWV == 8 ? 1 : BM * BN <= 64 * 64 ? 4 : BM * BN <= 128 * 192 ? 2 : 1;
-}
 
 // bf16 epilogue, first half: the tile's values (plus bias, through GeLU when
 // GELU) as bf16 into a [BM][SP bytes] LDS image.  Each lane writes 8 bytes (4
