@@ -397,28 +397,43 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     }
 }
 
-// D[b, g, j] = dO_j . O_j per head (fp32).
+// D[b, g, j] = dO_j . O_j per head (fp32).  RD_LANES lanes per (token, head):
+// lane part p reads chunks p, p + RD_LANES, ... of the head's row segment, so
+// one load instruction covers 64-byte runs; the partial sums meet by two xor
+// shuffles in a fixed order (deterministic).
+constexpr int RD_LANES = 4;
 template <int D, typename ST>
 __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;  // (token, head)
+    constexpr int CPL = D / 8 / RD_LANES;  // 16-byte chunks per lane
+    static_assert((D / 8) % RD_LANES == 0, "head dim must hold a multiple of 4 chunks");
+    const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
+    const int64_t idx = gid / RD_LANES;  // (token, head)
+    const int p = (int)(gid % RD_LANES);
     const int64_t T = (int64_t)a.batch * a.seq;
-    if (idx >= T * a.heads) return;
-    const int64_t r = idx / a.heads;
-    const int g = (int)(idx % a.heads);
-    const bf16_t* o = a.O + r * a.ld_o + g * D;
-    const bf16_t* d = a.dO + r * a.ld_o + g * D;
+    const bool valid = idx < T * a.heads;
+    const int64_t r = valid ? idx / a.heads : 0;
+    const int g = valid ? (int)(idx % a.heads) : 0;
     float acc = 0.f;
+    if (valid) {
+        const bf16_t* o = a.O + r * a.ld_o + g * D;
+        const bf16_t* d = a.dO + r * a.ld_o + g * D;
 #pragma unroll
-    for (int c = 0; c < D; c += 8) {
-        const u32x4 ov = ld16(o + c), dv = ld16(d + c);
+        for (int k = 0; k < CPL; ++k) {
+            const int c = 8 * (p + RD_LANES * k);
+            const u32x4 ov = ld16(o + c), dv = ld16(d + c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc += Store16<ST>::lo(ov[i]) * Store16<ST>::lo(dv[i]);
-            acc += Store16<ST>::hi(ov[i]) * Store16<ST>::hi(dv[i]);
+            for (int i = 0; i < 4; ++i) {
+                acc += Store16<ST>::lo(ov[i]) * Store16<ST>::lo(dv[i]);
+                acc += Store16<ST>::hi(ov[i]) * Store16<ST>::hi(dv[i]);
+            }
         }
     }
-    const int b = (int)(r / a.seq), j = (int)(r % a.seq);
-    a.Dq[((int64_t)b * a.heads + g) * a.seq + j] = acc;
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (valid && p == 0) {
+        const int b = (int)(r / a.seq), j = (int)(r % a.seq);
+        a.Dq[((int64_t)b * a.heads + g) * a.seq + j] = acc;
+    }
 }
 
 // Sum of the two query halves' partial dK (or dV) of a key group: the half-1
@@ -737,7 +752,7 @@ hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
     const int64_t T = (int64_t)a.batch * a.seq;
     dim3 grid_pair(((a.seq + BKV - 1) / BKV + 1) / 2, a.batch * a.heads);
     if (part == ATTN_BWD_ROWDOT)
-        hipLaunchKernelGGL((attn_rowdot_kernel<D, ST>), dim3((unsigned)((T * a.heads + NT - 1) / NT)), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((attn_rowdot_kernel<D, ST>), dim3((unsigned)((T * a.heads * RD_LANES + NT - 1) / NT)), dim3(NT), 0, s, a);
     else if (part == ATTN_BWD_DKDV)
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
     else if (part == ATTN_BWD_DQ)
