@@ -18,6 +18,7 @@ traffic of its dominant kernel only while that hash still matches.
 Usage:
   python -m tensor_transformer_layer_02_amd.profiling traffic FETCH_DIR WRITE_DIR CFETCH_DIR CWRITE_DIR OUT
   python -m tensor_transformer_layer_02_amd.profiling durations TRACE_DIR OUT
+  python -m tensor_transformer_layer_02_amd.profiling counters OUT PMC_DIR [PMC_DIR ...]
 """
 from __future__ import annotations
 
@@ -247,10 +248,52 @@ def read_traffic(path):
     return tab, h
 
 
+def counters(out, *dirs):
+    """Per-step averages of every counter of one or more --pmc runs (one run per counter
+    group), with the kernel time of the step in that run and, where a run holds
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_BUSY_CU_CYCLES, the matrix-core utilisation
+    MFMA-busy / (4 SIMDs x CU-busy cycles) and the clock CU-busy / (256 CUs x time)."""
+    lines = ["# hardware counters per step launch, layer shard gpt8b (8.3B shape, t = 8, shard 0), bf16 fwd+bwd",
+             "# commands (from the repository root, on the GPU host), one per counter group:"]
+    body = []
+    for d in dirs:
+        rows = _read(_one(d, "_counter_collection.csv"))
+        per = {}
+        for r in rows:
+            e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "us": (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        names = sorted({k for e in per.values() for k in e if k not in ("name", "us")})
+        lines.append(f"#   rocprofv3 --pmc {' '.join(names)} --kernel-trace -d DIR -o c --output-format csv "
+                     "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-kernel-timing")
+        steps = split_steps([(e["name"], e) for k, e in sorted(per.items()) if _ours(e["name"])])
+        mf, cu = "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES"
+        derived = mf in names and cu in names
+        body.append("# step  kernel_us  " + ("mfma_util  clock_GHz  " if derived else "") + "  ".join(names))
+        for step, _ in STEP_ORDER:
+            launches = [st[step] for st in steps if step in st]
+            if not launches:
+                continue
+            avg = lambda f: sum(sum(f(r) for r in recs) for recs in launches) / len(launches)
+            us = avg(lambda r: r["us"])
+            vals = {n: avg(lambda r, n=n: r.get(n, 0.0)) for n in names}
+            txt = f"{step:<14} {us:9.2f}  "
+            if derived:
+                txt += f"{vals[mf] / (4 * vals[cu]) if vals[cu] else 0.0:9.3f}  {vals[cu] / 256 / us / 1e3:9.2f}  "
+            body.append(txt + "  ".join(f"{vals[n]:.4g}" for n in names))
+        body.append("")
+    lines.append("#   python -m tensor_transformer_layer_02_amd.profiling counters <this file> DIR [DIR ...]")
+    lines.append(f"source_sha256_16 {source_hash()}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines + body))
+
+
 if __name__ == "__main__":
     if len(sys.argv) == 7 and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
     elif len(sys.argv) == 4 and sys.argv[1] == "durations":
         durations(*sys.argv[2:4])
+    elif len(sys.argv) >= 4 and sys.argv[1] == "counters":
+        counters(sys.argv[2], *sys.argv[3:])
     else:
         raise SystemExit(__doc__)
