@@ -54,6 +54,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 
 typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct AttnArgs {
     int batch, seq, heads, causal;
@@ -457,27 +458,120 @@ __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DB], float* mg, int q
     __syncthreads();
 }
 
-// dK, dV for the 64-key blocks x and nb-1-x (key groups of 32 as the row
-// groups of PairRows, so the two waves sharing a SIMD hold keys of different
-// blocks and every workgroup carries about the same work under the causal
-// mask).  Query blocks of 64 (Q and dO rows plus their log2-scaled LSE and D)
-// stream through LDS; the two waves of a key group take the two 32-query
-// halves of each block, and their dK, dV partial sums add through LDS at the
-// end (in a fixed order: deterministic).
+// One 16-byte-per-lane buffer load into LDS (lane l writes dst + 16 l).  A
+// plain function: with the builtin written inside the templates below, the
+// compiler's host pass emitted launch stubs only for the first storage type.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
+// Direct global -> LDS loads of ROWS rows x D (row-major, stride ld) into a
+// swizzled [ROWS][D] tile: instruction i of wave w fills tile bytes
+// [(w + 8i) * 1024, +1024), lane l the 16 bytes at +16 l, so the lane holding
+// row r, physical chunk pc fetches logical chunk pc ^ swz(r) of that row (the
+// byte image toff() gives).  Rows at or past `nvalid` read as zeros.
+template <int D, int ROWS>
+struct TileDMA {
+    static constexpr int BYTES = ROWS * D * 2;
+    static constexpr int NI = BYTES / (8 * 1024);
+    static_assert(BYTES % (8 * 1024) == 0, "the tile must split into 1 KB pieces over 8 waves");
+    int row[NI];
+    uint32_t off[NI];
+    __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int q = (wave + 8 * i) * 1024 + 16 * lane;
+            const int r = q / (2 * D), pc = (q % (2 * D)) / 16;
+            row[i] = r;
+            off[i] = (uint32_t)(r * ld * 2 + ((pc ^ swz<D>(r)) << 4));
+        }
+    }
+    __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int nvalid, char* tile,
+                                         int wave) const {
+        const int rem = nvalid - row0;
+        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * ld * 2 + D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)(rem > 0 ? row0 : 0) * ld, bytes);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            load16_lds(rs, tile + (wave + 8 * i) * 1024, row[i] < rem ? off[i] : OOB);
+    }
+};
+
+// One wave's share of one streamed pair of 64-query blocks in the dK/dV pass:
+// keys kw0 .. kw0+31 (K^T, V^T in kf, vf), queries 32 (half) of block j of
+// the pair in LDS stage `cur` (Q and dO [128][D], then the log2-scaled LSE and
+// D of the 128 queries).  The stage is a restrict pointer so that the
+// compiler does not wait for the loads in flight into the other stage.
+template <int D, typename ST>
+__device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>& fa, const char* __restrict__ cur,
+                                           const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16],
+                                           f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int q0, int j, int half,
+                                           int kw0, int kw, int lane) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    const int s = a.seq;
+    const char* Qt = cur;
+    const char* dOt = cur + 2 * TILE;
+    const float* lse2 = reinterpret_cast<const float*>(cur + 4 * TILE) + BKV * j;
+    const float* Dl = lse2 + 2 * BKV;
+    const int rb = BKV * j;           // first row of block j in the tiles
+    const int qh0 = q0 + 32 * half;   // this wave's 32 queries
+    f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        sacc = Store16<ST>::mfma(fa.frag_rows(Qt, rb + 32 * half, c), kf[c], sacc);
+        pacc = Store16<ST>::mfma(fa.frag_rows(dOt, rb + 32 * half, c), vf[c], pacc);
+    }
+    // rows = queries qh0 + res_row(r), column = this lane's key
+    const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const int ql = 32 * half + 8 * r4 + 4 * (lane >> 5);
+        const f32x4 L = *reinterpret_cast<const f32x4*>(lse2 + ql);
+        const f32x4 Dd = *reinterpret_cast<const f32x4*>(Dl + ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e, q = q0 + ql + e;
+            float pv = ex2(fmaf(sacc[r], a.scale_log2, -L[e]));
+            if (edge && !(q < s && kw < s && (!a.causal || kw <= q))) pv = 0.f;
+            sacc[r] = pv;
+            pacc[r] = pv * (pacc[r] - Dd[e]);
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const u32x4 pf = pack_chunk<ST>(sacc, hh), sf = pack_chunk<ST>(pacc, hh);
+        const int kc = 2 * half + hh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            dv[db] = Store16<ST>::mfma(pf, fa.frag_tr(dOt, rb, db, kc), dv[db]);
+            dk[db] = Store16<ST>::mfma(sf, fa.frag_tr(Qt, rb, db, kc), dk[db]);
+        }
+    }
+}
+
+// dK, dV for the 64-key blocks x and nb-1-x, one after the other, each with
+// all 8 waves: wave = (32-key group kg2 = wave & 1) x (query quarter qq =
+// wave >> 1: block qq / 2 of each streamed pair of 64-query blocks, 32-query
+// half qq % 2).  Under the causal mask block x sees nb - x query blocks and
+// block nb-1-x sees x + 1, so every workgroup streams about (nb + 1) / 2
+// pairs whatever x is (a workgroup that ran both key blocks side by side
+// over one query stream would take nb - x steps while the waves of the later
+// block wait).  Q and dO pairs go straight into LDS (two stages), the LSE and
+// D of their queries through registers.  The four quarters' dK, dV add
+// through LDS in a fixed order, (q0 + q1) + (q2 + q3): deterministic.
 template <int D, typename ST>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
-    constexpr int SLOT = 2 * TILE + 2 * BKV * 4;  // Q, dO, LSE, D
-    constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for the 4 key groups
+    constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
+    constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for four groups
     constexpr int SMEM = 2 * SLOT > MERGE ? 2 * SLOT : MERGE;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const PairRows pr((int)blockIdx.x, s, wave, a.causal);  // rows = keys here
-    const int kg = pr.qg, qh = pr.kp, kw0 = pr.qw0;
+    const int nb = (s + BKV - 1) / BKV, x = (int)blockIdx.x, xl = nb - 1 - x;
+    const int kg2 = wave & 1, qq = wave >> 1, jb = qq >> 1, half = qq & 1;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int kw = kw0 + (lane & 31);  // this lane's key
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
@@ -486,128 +580,97 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     const float* lseg = a.lse + ((int64_t)b * a.heads + g) * s;
     const float* Dg = a.Dq + ((int64_t)b * a.heads + g) * s;
 
-    u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-        const bool ok = kw < s;
-        const int64_t o = (int64_t)kw * a.ld_qkv + 16 * c + 8 * (lane >> 5);
-        kf[c] = ok ? ld16(Kg + o) : u32x4{0u, 0u, 0u, 0u};
-        vf[c] = ok ? ld16(Vg + o) : u32x4{0u, 0u, 0u, 0u};
-    }
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
-
     FragAddr<D> fa;
     fa.init(lane);
-    RowGeom<D, BKV, NT8> gq, go;  // Q rows (stride ld_qkv) and dO rows (stride ld_o)
-    gq.init(a.ld_qkv, tid);
-    go.init(a.ld_o, tid);
-    u32x4 qv[RowGeom<D, BKV, NT8>::NI], ov[RowGeom<D, BKV, NT8>::NI];
-    float lsev = 0.f, dval = 0.f;  // threads < 64: one query's log2-scaled LSE and D
+    TileDMA<D, 2 * BKV> gq, go;  // Q rows (stride ld_qkv), dO rows (stride ld_o)
+    gq.init(a.ld_qkv, wave, lane);
+    go.init(a.ld_o, wave, lane);
+    char* const st0 = smem;
+    char* const st1 = smem + SLOT;
 
-    const int nqb = (s + BKV - 1) / BKV;
-    const int qb0 = a.causal ? (int)blockIdx.x : 0;  // the first query that sees the lowest key
-    if (qb0 < nqb) {
-        const int q0 = qb0 * BKV;
-        gq.load(Qg, a.ld_qkv, q0, s, qv);
-        go.load(dOg, a.ld_o, q0, s, ov);
-        if (tid < BKV) {
-            lsev = q0 + tid < s ? lseg[q0 + tid] * LOG2E : 0.f;
-            dval = q0 + tid < s ? Dg[q0 + tid] : 0.f;
+    const int nphase = xl != x ? 2 : 1;
+    for (int ph = 0; ph < nphase; ++ph) {
+        const int kb = ph == 0 ? x : xl;
+        const int kw0 = min(s, kb * BKV + 32 * kg2);  // first key of this wave's group (s: none)
+        const int kw = kw0 + (lane & 31);              // this lane's key
+        u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const bool ok = kw < s;
+            const int64_t o = (int64_t)kw * a.ld_qkv + 16 * c + 8 * (lane >> 5);
+            kf[c] = ok ? ld16(Kg + o) : u32x4{0u, 0u, 0u, 0u};
+            vf[c] = ok ? ld16(Vg + o) : u32x4{0u, 0u, 0u, 0u};
         }
-        gq.store(smem, qv);
-        go.store(smem + TILE, ov);
-        if (tid < BKV) {
-            reinterpret_cast<float*>(smem + 2 * TILE)[tid] = lsev;
-            reinterpret_cast<float*>(smem + 2 * TILE + BKV * 4)[tid] = dval;
-        }
-    }
-    __syncthreads();
+        f32x16 dk[DB], dv[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
 
-    for (int qb = qb0; qb < nqb; ++qb) {
-        const int q0 = qb * BKV;
-        const bool more = qb + 1 < nqb;
-        if (more) {
-            const int q1 = q0 + BKV;
-            gq.load(Qg, a.ld_qkv, q1, s, qv);
-            go.load(dOg, a.ld_o, q1, s, ov);
-            if (tid < BKV) {
-                lsev = q1 + tid < s ? lseg[q1 + tid] * LOG2E : 0.f;
-                dval = q1 + tid < s ? Dg[q1 + tid] : 0.f;
+        const int qs = a.causal ? kb : 0;     // the first query block that sees the key block
+        const int npair = (nb - qs + 1) / 2;  // streamed pairs of query blocks
+        float lsev = 0.f, dval = 0.f;         // threads < 128: one query's log2-scaled LSE and D
+        if (npair > 0) {
+            const int row0 = qs * BKV;
+            gq.load(Qg, a.ld_qkv, row0, s, st0, wave);
+            go.load(dOg, a.ld_o, row0, s, st0 + 2 * TILE, wave);
+            if (tid < 2 * BKV) {
+                const int q = row0 + tid;
+                reinterpret_cast<float*>(st0 + 4 * TILE)[tid] = q < s ? lseg[q] * LOG2E : 0.f;
+                reinterpret_cast<float*>(st0 + 4 * TILE + 2 * BKV * 4)[tid] = q < s ? Dg[q] : 0.f;
             }
         }
-        const char* slot = smem + ((qb - qb0) & 1) * SLOT;
-        const char* Qt = slot;
-        const char* dOt = slot + TILE;
-        const float* lse2 = reinterpret_cast<const float*>(slot + 2 * TILE);
-        const float* Dl = lse2 + BKV;
-        const int qh0 = q0 + 32 * qh;  // this wave's 32 queries
-        // skip when the key group is empty or every query precedes every key
-        if (kw0 < s && !(a.causal && qh0 + 31 < kw0)) {
-            f32x16 sacc = zero16(), pacc = zero16();
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                sacc = Store16<ST>::mfma(fa.frag_rows(Qt, 32 * qh, c), kf[c], sacc);
-                pacc = Store16<ST>::mfma(fa.frag_rows(dOt, 32 * qh, c), vf[c], pacc);
-            }
-            // rows = queries qh0 + res_row(r), column = this lane's key
-            const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int ql = 32 * qh + 8 * r4 + 4 * (lane >> 5);
-                const f32x4 L = *reinterpret_cast<const f32x4*>(lse2 + ql);
-                const f32x4 Dd = *reinterpret_cast<const f32x4*>(Dl + ql);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e, q = q0 + ql + e;
-                    float pv = ex2(fmaf(sacc[r], a.scale_log2, -L[e]));
-                    if (edge && !(q < s && kw < s && (!a.causal || kw <= q))) pv = 0.f;
-                    sacc[r] = pv;
-                    pacc[r] = pv * (pacc[r] - Dd[e]);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads and LDS stores are done
+        __syncthreads();
+        for (int it = 0; it < npair; ++it) {
+            char* const cur = (it & 1) ? st1 : st0;
+            char* const nxt = (it & 1) ? st0 : st1;
+            const bool more = it + 1 < npair;
+            if (more) {  // the other stage was last read in iteration it-1, before its closing barrier
+                const int row1 = (qs + 2 * (it + 1)) * BKV;
+                gq.load(Qg, a.ld_qkv, row1, s, nxt, wave);
+                go.load(dOg, a.ld_o, row1, s, nxt + 2 * TILE, wave);
+                if (tid < 2 * BKV) {
+                    const int q = row1 + tid;
+                    lsev = q < s ? lseg[q] * LOG2E : 0.f;
+                    dval = q < s ? Dg[q] : 0.f;
                 }
             }
+            const int q0 = (qs + 2 * it + jb) * BKV;  // this wave's query block
+            // skip when the key group or the query block is empty, or every query precedes every key
+            if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0))
+                dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
+            if (more && tid < 2 * BKV) {
+                reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev;
+                reinterpret_cast<float*>(nxt + 4 * TILE + 2 * BKV * 4)[tid] = dval;
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+
+        // (q0 + q1) + (q2 + q3): round 1 adds odd quarters into even ones, round 2 quarter 2 into 0
+        float* mg = reinterpret_cast<float*>(smem);
+        merge_halves<DB>(dk, mg, half, 2 * kg2 + jb, lane);
+        merge_halves<DB>(dv, mg, half, 2 * kg2 + jb, lane);
+        const int role2 = qq == 0 ? 0 : (qq == 2 ? 1 : 2);
+        merge_halves<DB>(dk, mg, role2, kg2, lane);
+        merge_halves<DB>(dv, mg, role2, kg2, lane);
+
+        // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
+        if (qq == 0 && kw0 < s) {
+            bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
+            bf16_t* dVg = dKg + a.w;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const u32x4 pf = pack_chunk<ST>(sacc, half), sf = pack_chunk<ST>(pacc, half);
-                const int kc = 2 * qh + half;
+            for (int r = 0; r < 16; ++r) {
+                const int key = kw0 + res_row(r, lane);
+                if (key >= s) continue;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dv[db] = Store16<ST>::mfma(pf, fa.frag_tr(dOt, 0, db, kc), dv[db]);
-                    dk[db] = Store16<ST>::mfma(sf, fa.frag_tr(Qt, 0, db, kc), dk[db]);
+                    const int c = 32 * db + (lane & 31);
+                    dKg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dk[db][r] * a.scale);
+                    dVg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dv[db][r]);
                 }
             }
         }
-        if (more) {  // slot of block qb+1 was last read in iteration qb-1, before its closing barrier
-            char* nxt = smem + ((qb + 1 - qb0) & 1) * SLOT;
-            gq.store(nxt, qv);
-            go.store(nxt + TILE, ov);
-            if (tid < BKV) {
-                reinterpret_cast<float*>(nxt + 2 * TILE)[tid] = lsev;
-                reinterpret_cast<float*>(nxt + 2 * TILE + BKV * 4)[tid] = dval;
-            }
-        }
-        __syncthreads();
-    }
-
-    merge_halves<DB>(dk, reinterpret_cast<float*>(smem), qh, kg, lane);
-    merge_halves<DB>(dv, reinterpret_cast<float*>(smem), qh, kg, lane);
-
-    // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
-    if (qh == 0 && kw0 < s) {
-        bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
-        bf16_t* dVg = dKg + a.w;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kw0 + res_row(r, lane);
-            if (key >= s) continue;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int c = 32 * db + (lane & 31);
-                dKg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dk[db][r] * a.scale);
-                dVg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dv[db][r]);
-            }
-        }
+        __syncthreads();  // the merge area is the stages of the next phase
     }
 }
 
