@@ -549,17 +549,21 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
     }
 }
 
-// dK, dV for the 64-key blocks x and nb-1-x, one after the other, each with
-// all 8 waves: wave = (32-key group kg2 = wave & 1) x (query quarter qq =
-// wave >> 1: block qq / 2 of each streamed pair of 64-query blocks, 32-query
-// half qq % 2).  Under the causal mask block x sees nb - x query blocks and
-// block nb-1-x sees x + 1, so every workgroup streams about (nb + 1) / 2
-// pairs whatever x is (a workgroup that ran both key blocks side by side
-// over one query stream would take nb - x steps while the waves of the later
-// block wait).  Q and dO pairs go straight into LDS (two stages), the LSE and
-// D of their queries through registers.  The four quarters' dK, dV add
-// through LDS in a fixed order, (q0 + q1) + (q2 + q3): deterministic.
-template <int D, typename ST>
+// dK, dV for the 64-key blocks x and nb-1-x.  Causal: one block after the
+// other, each with all 8 waves: wave = (32-key group kg2 = wave & 1) x (query
+// quarter qq = wave >> 1: block qq / 2 of each streamed pair of 64-query
+// blocks, 32-query half qq % 2).  Block x sees nb - x query blocks and block
+// nb-1-x sees x + 1, so every workgroup streams about (nb + 1) / 2 pairs
+// whatever x is (a workgroup that ran both key blocks side by side over one
+// query stream would take nb - x steps while the waves of the later block
+// wait); the four quarters' dK, dV add through LDS in a fixed order,
+// (q0 + q1) + (q2 + q3).  No mask (NOMASK, used up to d = 64): both key blocks
+// see every query, so they run side by side over one stream (wave = 32-key
+// group wave & 3 of the two blocks x 32-query half wave >> 2, both blocks of
+// each pair), halves added q0 + q1; larger heads without a mask take the
+// one-block-at-a-time form, whose registers fit.  Q and dO pairs go straight into LDS (two stages), the LSE and D
+// of their queries through registers.  Deterministic either way.
+template <int D, typename ST, bool NOMASK>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
     constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
@@ -570,7 +574,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
     const int nb = (s + BKV - 1) / BKV, x = (int)blockIdx.x, xl = nb - 1 - x;
-    const int kg2 = wave & 1, qq = wave >> 1, jb = qq >> 1, half = qq & 1;
+    const bool side = NOMASK && xl != x;  // both key blocks over one query stream
+    const int kg2 = wave & 1, qq = side ? 2 * (wave >> 2) : wave >> 1;
+    const int jb = qq >> 1, half = side ? wave >> 2 : qq & 1;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -588,9 +594,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     char* const st0 = smem;
     char* const st1 = smem + SLOT;
 
-    const int nphase = xl != x ? 2 : 1;
+    const int nphase = (xl != x && !side) ? 2 : 1;
     for (int ph = 0; ph < nphase; ++ph) {
-        const int kb = ph == 0 ? x : xl;
+        const int kb = side ? ((wave & 2) ? xl : x) : (ph == 0 ? x : xl);
         const int kw0 = min(s, kb * BKV + 32 * kg2);  // first key of this wave's group (s: none)
         const int kw = kw0 + (lane & 31);              // this lane's key
         u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
@@ -634,10 +640,18 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
                     dval = q < s ? Dg[q] : 0.f;
                 }
             }
-            const int q0 = (qs + 2 * it + jb) * BKV;  // this wave's query block
-            // skip when the key group or the query block is empty, or every query precedes every key
-            if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0))
-                dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
+            if (NOMASK && side) {  // both query blocks of the pair, this wave's half of each
+#pragma unroll 1
+                for (int j = 0; j < 2; ++j) {  // rolled: two copies of the block would spill
+                    const int q0 = (qs + 2 * it + j) * BKV;
+                    if (kw0 < s && q0 < s) dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, j, half, kw0, kw, lane);
+                }
+            } else {
+                const int q0 = (qs + 2 * it + jb) * BKV;  // this wave's query block
+                // skip when the key group or the query block is empty, or every query precedes every key
+                if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0))
+                    dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
+            }
             if (more && tid < 2 * BKV) {
                 reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev;
                 reinterpret_cast<float*>(nxt + 4 * TILE + 2 * BKV * 4)[tid] = dval;
@@ -646,16 +660,20 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
             __syncthreads();
         }
 
-        // (q0 + q1) + (q2 + q3): round 1 adds odd quarters into even ones, round 2 quarter 2 into 0
         float* mg = reinterpret_cast<float*>(smem);
-        merge_halves<DB>(dk, mg, half, 2 * kg2 + jb, lane);
-        merge_halves<DB>(dv, mg, half, 2 * kg2 + jb, lane);
-        const int role2 = qq == 0 ? 0 : (qq == 2 ? 1 : 2);
-        merge_halves<DB>(dk, mg, role2, kg2, lane);
-        merge_halves<DB>(dv, mg, role2, kg2, lane);
+        if (NOMASK && side) {  // q0 + q1 per key group
+            merge_halves<DB>(dk, mg, half, wave & 3, lane);
+            merge_halves<DB>(dv, mg, half, wave & 3, lane);
+        } else {  // (q0 + q1) + (q2 + q3): odd quarters into even ones, then quarter 2 into 0
+            merge_halves<DB>(dk, mg, half, 2 * kg2 + jb, lane);
+            merge_halves<DB>(dv, mg, half, 2 * kg2 + jb, lane);
+            const int role2 = qq == 0 ? 0 : (qq == 2 ? 1 : 2);
+            merge_halves<DB>(dk, mg, role2, kg2, lane);
+            merge_halves<DB>(dv, mg, role2, kg2, lane);
+        }
 
         // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
-        if (qq == 0 && kw0 < s) {
+        if ((side ? half == 0 : qq == 0) && kw0 < s) {
             bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
             bf16_t* dVg = dKg + a.w;
 #pragma unroll
@@ -817,7 +835,18 @@ hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
     if (part == ATTN_BWD_ROWDOT)
         hipLaunchKernelGGL((attn_rowdot_kernel<D, ST>), dim3((unsigned)((T * a.heads * RD_LANES + NT - 1) / NT)), dim3(NT), 0, s, a);
     else if (part == ATTN_BWD_DKDV)
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
+    {
+        // The side-by-side form for the unmasked case fits the registers only up to d = 64
+        // (beyond, two query blocks per step spill); larger heads take the one-block-at-a-time form.
+        if constexpr (D <= 64) {
+            if (!a.causal) {
+                hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST, true>), grid_pair, dim3(NT8), 0, s, a);
+                count_launch();
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST, false>), grid_pair, dim3(NT8), 0, s, a);
+    }
     else if (part == ATTN_BWD_DQ)
         hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
     else
