@@ -692,10 +692,49 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     }
 }
 
-// dQ for two 64-query blocks (rows as in the forward).  The two waves of a
-// row group take alternate 64-key blocks of each streamed pair; their dQ^T
-// sums add through LDS at the end (in a fixed order: deterministic).
+// One wave's dQ^T update from 32 keys k0 .. k0+31 of a streamed K/V pair in LDS
+// (rows rb .. rb+31 of the pair tiles) for its 32 queries (Q^T, dO^T in qf, of).
 template <int D, typename ST>
+__device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa, const char* Kt, const char* Vt,
+                                        const u32x4 (&qf)[D / 16], const u32x4 (&of)[D / 16],
+                                        f32x16 (&dq)[D / 32], int rb, int k0, int qw0, int qw, float lse2,
+                                        float Dv, int lane) {
+    constexpr int KC = D / 16, DB = D / 32;
+    const int s = a.seq;
+    f32x16 sacc = zero16(), pacc = zero16();  // S^T and dP^T: rows = keys, column = this lane's query
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        sacc = Store16<ST>::mfma(fa.frag_rows(Kt, rb, c), qf[c], sacc);
+        pacc = Store16<ST>::mfma(fa.frag_rows(Vt, rb, c), of[c], pacc);
+    }
+    const bool edge = (a.causal && k0 + 31 > qw0) || k0 + 32 > s || qw0 + 32 > s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int key = k0 + res_row(r, lane);
+        float pv = ex2(fmaf(sacc[r], a.scale_log2, -lse2));
+        if (edge && !(qw < s && key < s && (!a.causal || key <= qw))) pv = 0.f;
+        pacc[r] = pv * (pacc[r] - Dv);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        const u32x4 sf = pack_chunk<ST>(pacc, kc);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dq[db] = Store16<ST>::mfma(fa.frag_tr(Kt, rb, db, kc), sf, dq[db]);
+    }
+}
+
+// dQ for the 64-query blocks x and nb-1-x.  Causal (MASKED): one block after the
+// other, each with all 8 waves: wave = (32-query row group rg = wave & 1) x
+// (key part kq = wave >> 1: 32-key half kq % 2 of key block kq / 2 of each
+// streamed K/V pair).  Block x sees x + 1 key blocks and block nb-1-x sees
+// nb - x, so every workgroup streams about (nb + 2) / 2 pairs of half the
+// per-wave work whatever x is (side by side over one key stream it would take
+// (nb - x) / 2 full steps while the waves of block x wait); the four parts'
+// dQ^T add through LDS as (k0 + k1) + (k2 + k3).  No mask: both query blocks
+// see every key, so they run side by side over one stream (the forward's
+// layout: the two waves of a row group take alternate 64-key blocks of each
+// pair), halves added k0 + k1.  Deterministic either way.
+template <int D, typename ST, bool MASKED>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
     constexpr int SLOT = 2 * PT;  // K pair, V pair
@@ -704,26 +743,16 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const PairRows pr((int)blockIdx.x, s, wave, a.causal);
-    const int qg = pr.qg, kp = pr.kp, qw0 = pr.qw0;
+    const int nb = (s + BKV - 1) / BKV, x = (int)blockIdx.x, xl = nb - 1 - x;
     const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
-    const int qw = qw0 + (lane & 31);  // this lane's query
+    const PairRows pr(x, s, wave, a.causal);  // the side-by-side layout (no mask)
+    const int rg = wave & 1, kq = wave >> 1;  // the one-after-the-other layout (causal)
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
     const bf16_t* Vg = Qg + 2 * a.w;
     const bf16_t* dOg = a.dO + (int64_t)b * s * a.ld_o + g * D;
-
-    u32x4 qf[KC], of[KC];  // Q^T, dO^T operands: column = query, k = d
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-        const bool ok = qw < s;
-        qf[c] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
-        of[c] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
-    }
     const int64_t hrow = ((int64_t)b * a.heads + g) * s;
-    const float lse2 = qw < s ? a.lse[hrow + qw] * LOG2E : 0.f;
-    const float Dv = qw < s ? a.Dq[hrow + qw] : 0.f;
 
     FragAddr<D> fa;
     fa.init(lane);
@@ -731,77 +760,71 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     geo.init(a.ld_qkv, tid);
     u32x4 kv[PairGeom<D>::NI], vv[PairGeom<D>::NI];
 
-    f32x16 dq[DB];
+    const int nphase = (MASKED && xl != x) ? 2 : 1;
+    for (int ph = 0; ph < nphase; ++ph) {
+        const int qb = ph == 0 ? x : xl;
+        const int qw0 = MASKED ? min(s, qb * BKV + 32 * rg) : pr.qw0;  // first query of the wave (s: none)
+        const int qw = qw0 + (lane & 31);                               // this lane's query
+        u32x4 qf[KC], of[KC];  // Q^T, dO^T operands: column = query, k = d
 #pragma unroll
-    for (int i = 0; i < DB; ++i) dq[i] = zero16();
+        for (int c = 0; c < KC; ++c) {
+            const bool ok = qw < s;
+            qf[c] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+            of[c] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const float lse2 = qw < s ? a.lse[hrow + qw] * LOG2E : 0.f;
+        const float Dv = qw < s ? a.Dq[hrow + qw] : 0.f;
+        f32x16 dq[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) dq[i] = zero16();
 
-    const int nkb = pr.nkb;
-    const int npair = (nkb + 1) / 2;
-    geo.load(Kg, a.ld_qkv, 0, s, kv);
-    geo.load(Vg, a.ld_qkv, 0, s, vv);
-    geo.store(smem, kv);
-    geo.store(smem + PT, vv);
-    __syncthreads();
-
-    for (int it = 0; it < npair; ++it) {
-        const bool more = it + 1 < npair;
-        if (more) {
-            geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
-            geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
-        }
-        const char* Kt = smem + (it & 1) * SLOT;
-        const char* Vt = Kt + PT;
-        const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
-        if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {
-            f32x16 sacc[2], pacc[2];  // S^T and dP^T: rows = keys, column = this lane's query
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                sacc[h] = pacc[h] = zero16();
-#pragma unroll
-                for (int c = 0; c < KC; ++c) {
-                    sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
-                    pacc[h] = Store16<ST>::mfma(fa.frag_rows(Vt, rb + 32 * h, c), of[c], pacc[h]);
-                }
-            }
-            const bool edge = (a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s || qw0 + 32 > s;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * h + res_row(r, lane);
-                    float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -lse2));
-                    if (edge && !(qw < s && key < s && (!a.causal || key <= qw))) pv = 0.f;
-                    pacc[h][r] = pv * (pacc[h][r] - Dv);
-                }
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const u32x4 sf = pack_chunk<ST>(pacc[kc >> 1], kc & 1);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) dq[db] = Store16<ST>::mfma(fa.frag_tr(Kt, rb, db, kc), sf, dq[db]);
-            }
-        }
-        if (more) {
-            char* nxt = smem + ((it + 1) & 1) * SLOT;
-            geo.store(nxt, kv);
-            geo.store(nxt + PT, vv);
-        }
+        const int nkb = MASKED ? (a.causal ? qb + 1 : nb) : pr.nkb;  // key blocks the phase streams
+        const int npair = (nkb + 1) / 2;
+        geo.load(Kg, a.ld_qkv, 0, s, kv);
+        geo.load(Vg, a.ld_qkv, 0, s, vv);
+        geo.store(smem, kv);
+        geo.store(smem + PT, vv);
         __syncthreads();
-    }
 
-    float* mg = reinterpret_cast<float*>(smem);
-    if (kp == 1) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mg[((16 * db + r) * 4 + qg) * 64 + lane] = dq[db][r];
-    }
-    __syncthreads();
-    if (kp == 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dq[db][r] += mg[((16 * db + r) * 4 + qg) * 64 + lane];
-        if (qw < s) store_rowT<D, ST>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
+        for (int it = 0; it < npair; ++it) {
+            const bool more = it + 1 < npair;
+            if (more) {
+                geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
+                geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
+            }
+            const char* Kt = smem + (it & 1) * SLOT;
+            const char* Vt = Kt + PT;
+            if constexpr (MASKED) {  // 32 keys: half kq % 2 of block 2 it + kq / 2
+                const int kb = 2 * it + (kq >> 1), rb = BKV * (kq >> 1) + 32 * (kq & 1), k0 = 2 * it * BKV + rb;
+                if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31))
+                    dq_keys<D, ST>(a, fa, Kt, Vt, qf, of, dq, rb, k0, qw0, qw, lse2, Dv, lane);
+            } else {  // 64 keys: block 2 it + kp, both halves in order
+                const int kb = 2 * it + pr.kp, k0 = kb * BKV, rb = BKV * pr.kp;
+                if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {
+                    dq_keys<D, ST>(a, fa, Kt, Vt, qf, of, dq, rb, k0, qw0, qw, lse2, Dv, lane);
+                    dq_keys<D, ST>(a, fa, Kt, Vt, qf, of, dq, rb + 32, k0 + 32, qw0, qw, lse2, Dv, lane);
+                }
+            }
+            if (more) {
+                char* nxt = smem + ((it + 1) & 1) * SLOT;
+                geo.store(nxt, kv);
+                geo.store(nxt + PT, vv);
+            }
+            __syncthreads();
+        }
+
+        float* mg = reinterpret_cast<float*>(smem);
+        bool writer;
+        if constexpr (MASKED) {  // (k0 + k1) + (k2 + k3) per row group
+            merge_halves<DB>(dq, mg, kq & 1, 2 * rg + (kq >> 1), lane);
+            merge_halves<DB>(dq, mg, kq == 0 ? 0 : (kq == 2 ? 1 : 2), rg, lane);
+            writer = kq == 0;
+        } else {  // k0 + k1 per row group
+            merge_halves<DB>(dq, mg, pr.kp, pr.qg, lane);
+            writer = pr.kp == 0;
+        }
+        if (writer && qw < s) store_rowT<D, ST>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
+        __syncthreads();  // the merge area is the first stage of the next phase
     }
 }
 
@@ -847,8 +870,12 @@ hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
         }
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, ST, false>), grid_pair, dim3(NT8), 0, s, a);
     }
-    else if (part == ATTN_BWD_DQ)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST>), grid_pair, dim3(NT8), 0, s, a);
+    else if (part == ATTN_BWD_DQ) {
+        if (a.causal)
+            hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST, true>), grid_pair, dim3(NT8), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST, false>), grid_pair, dim3(NT8), 0, s, a);
+    }
     else
         return hipErrorInvalidValue;
     count_launch();
