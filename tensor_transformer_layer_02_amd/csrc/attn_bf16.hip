@@ -516,10 +516,20 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
     const int rb = BKV * j;           // first row of block j in the tiles
     const int qh0 = q0 + 32 * half;   // this wave's 32 queries
     f32x16 sacc = zero16(), pacc = zero16();
+    // The fragments of chunk c + 1 are read before the MFMAs of chunk c, so that an
+    // LDS read is in flight behind every MFMA (same MFMA order per accumulator).
+    u32x4 fq = fa.frag_rows(Qt, rb + 32 * half, 0), fo = fa.frag_rows(dOt, rb + 32 * half, 0);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-        sacc = Store16<ST>::mfma(fa.frag_rows(Qt, rb + 32 * half, c), kf[c], sacc);
-        pacc = Store16<ST>::mfma(fa.frag_rows(dOt, rb + 32 * half, c), vf[c], pacc);
+        u32x4 nq = fq, no = fo;
+        if (c + 1 < KC) {
+            nq = fa.frag_rows(Qt, rb + 32 * half, c + 1);
+            no = fa.frag_rows(dOt, rb + 32 * half, c + 1);
+        }
+        sacc = Store16<ST>::mfma(fq, kf[c], sacc);
+        pacc = Store16<ST>::mfma(fo, vf[c], pacc);
+        fq = nq;
+        fo = no;
     }
     // rows = queries qh0 + res_row(r), column = this lane's key
     const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
@@ -537,14 +547,22 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
             pacc[r] = pv * (pacc[r] - Dd[e]);
         }
     }
+    u32x4 to = fa.frag_tr(dOt, rb, 0, 2 * half), tq = fa.frag_tr(Qt, rb, 0, 2 * half);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const u32x4 pf = pack_chunk<ST>(sacc, hh), sf = pack_chunk<ST>(pacc, hh);
-        const int kc = 2 * half + hh;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            dv[db] = Store16<ST>::mfma(pf, fa.frag_tr(dOt, rb, db, kc), dv[db]);
-            dk[db] = Store16<ST>::mfma(sf, fa.frag_tr(Qt, rb, db, kc), dk[db]);
+            u32x4 no = to, nq = tq;  // the next (chunk, d block) pair's fragments
+            const int nd = db + 1 < DB ? db + 1 : 0, nk = 2 * half + (db + 1 < DB ? hh : hh + 1);
+            if (db + 1 < DB || hh == 0) {
+                no = fa.frag_tr(dOt, rb, nd, nk);
+                nq = fa.frag_tr(Qt, rb, nd, nk);
+            }
+            dv[db] = Store16<ST>::mfma(pf, to, dv[db]);
+            dk[db] = Store16<ST>::mfma(sf, tq, dk[db]);
+            to = no;
+            tq = nq;
         }
     }
 }
