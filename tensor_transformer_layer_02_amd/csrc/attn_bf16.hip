@@ -309,13 +309,19 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
         const char* Vt = Kt + PT;
         const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
         if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
-            f32x16 sacc[2];
+            f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                sacc[h] = zero16();
+            for (int c = 0; c < KC; ++c)  // the two halves' chains interleaved
 #pragma unroll
-                for (int c = 0; c < KC; ++c) sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+                for (int h = 0; h < 2; ++h) sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+            // Keep two chunks' reads in flight: 4 LDS reads, then (2 MFMAs, 2 reads) per chunk.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int c = 0; c + 2 < KC; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             // Masks only where the block reaches past the diagonal or the
             // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
             // the max and the exponent.
@@ -724,6 +730,17 @@ __device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa
     for (int c = 0; c < KC; ++c) {
         sacc = Store16<ST>::mfma(fa.frag_rows(Kt, rb, c), qf[c], sacc);
         pacc = Store16<ST>::mfma(fa.frag_rows(Vt, rb, c), of[c], pacc);
+    }
+    // Keep two chunks' reads in flight: 4 LDS reads, then (2 MFMAs, 2 reads) per chunk
+    // (up to d = 96: at d = 128 the registers of the extra reads come from spills).
+    if constexpr (D <= 96) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int c = 0; c + 2 < KC; ++c) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     const bool edge = (a.causal && k0 + 31 > qw0) || k0 + 32 > s || qw0 + 32 > s;
 #pragma unroll
