@@ -738,14 +738,30 @@ __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ld
     constexpr int GPR = BN / 8;  // 8-column groups per row
     constexpr int ITEMS = BM * GPR / NTH;
     static_assert((BM * GPR) % NTH == 0, "epilogue split");
+    // Items go in groups of G: the group's LDS reads (always inside the image) are
+    // issued together, then the stores of its items inside the valid extent, so the
+    // reads do not wait for one another behind the bounds test of each item.
+    constexpr int G = ITEMS < 8 ? ITEMS : 8;
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int e = tid + it * NTH;
-        const int lr = e / GPR, cg = e % GPR;
-        if (lr >= rows || cg * 8 >= ncols) continue;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16 + 8);
-        *reinterpret_cast<u32x4*>(C + (int64_t)lr * ldc + cg * 8) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    for (int g0 = 0; g0 < ITEMS; g0 += G) {
+        u32x4 v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int e = tid + (g0 + k) * NTH;
+            const int lr = e / GPR, cg = e % GPR;
+            if (g0 + k < ITEMS) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(st + lr * SP + cg * 16 + 8);
+                v[k] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int e = tid + (g0 + k) * NTH;
+            const int lr = e / GPR, cg = e % GPR;
+            if (g0 + k < ITEMS && lr < rows && cg * 8 < ncols)
+                *reinterpret_cast<u32x4*>(C + (int64_t)lr * ldc + cg * 8) = v[k];
+        }
     }
 }
 
@@ -796,18 +812,27 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
 #pragma unroll
         for (int j = 0; j < Core::FN; ++j) {
             __syncthreads();
+            // value r of block i, lane l of wave wl at [((i * 4 + r / 4) * 4 + wl) * 256 + 4 l + r % 4]:
+            // 16 bytes per lane and access, all reads of a block issued before the adds
             if (g == 1) {
 #pragma unroll
                 for (int i = 0; i < Core::FM; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mg[((i * 16 + r) * 4 + wl) * 64 + lane] = acc[i][j][r];
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        *reinterpret_cast<f32x4*>(mg + ((i * 4 + r4) * 4 + wl) * 256 + 4 * lane) =
+                            f32x4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
             }
             __syncthreads();
             if (g == 0) {
 #pragma unroll
-                for (int i = 0; i < Core::FM; ++i)
+                for (int i = 0; i < Core::FM; ++i) {
+                    f32x4 t[4];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += mg[((i * 16 + r) * 4 + wl) * 64 + lane];
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        t[r4] = *reinterpret_cast<const f32x4*>(mg + ((i * 4 + r4) * 4 + wl) * 256 + 4 * lane);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += t[r / 4][r % 4];
+                }
             }
         }
     }
@@ -815,6 +840,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const int csg = n0 / p.cseg;
     const int cofs = csg * p.cseg;
     const int rows = p.M - m0, ncols = p.N - n0;  // valid extent of the tile
+    static_assert(F32STAGE || KG == 1, "bf16 epilogues assume every thread holds final sums");
     if constexpr (!F32STAGE) {
         // Bias (and GeLU) on the accumulators; the output image goes through
         // LDS once (twice with GeLU: U, then Y).
@@ -855,33 +881,58 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
             constexpr int GPR = BN / 8;                 // 8-column groups per row
             constexpr int ITEMS = EROWS * GPR / NT;
             static_assert(ITEMS >= 1 && (EROWS * GPR) % NT == 0, "epilogue split");
+            // Items in groups of G: the group's U loads (GeLU') and LDS reads are all
+            // issued before its first use, so their latencies overlap instead of
+            // adding up item by item.
+            constexpr int G = ITEMS < 4 ? ITEMS : 4;
+            if (epi_wave && (!OUTF32 || batch.ksplit == 1)) {
 #pragma unroll
-            for (int it = 0; it < ITEMS; ++it) {
-                const int e = tid + it * NT;
-                const int lr = e / GPR, cg = e % GPR;
-                const int m = m0 + half * EROWS + lr, n = n0 + cg * 8;
-                if (!epi_wave || m >= p.M || n >= p.N) continue;
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8 + 4);
-                const int nl = n - cofs;
-                if constexpr (OUTF32) {
-                    if (batch.ksplit == 1) {
-                        float* c = reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + nl;
-                        *reinterpret_cast<f32x4*>(c) = lo;
-                        *reinterpret_cast<f32x4*>(c + 4) = hi;
+                for (int g0 = 0; g0 < ITEMS; g0 += G) {
+                    f32x4 lo[G], hi[G];
+                    u32x4 uw[G];
+                    bool ok[G];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        const int e = tid + (g0 + k) * NT;
+                        const int lr = e / GPR, cg = e % GPR;
+                        const int m = m0 + half * EROWS + lr, n = n0 + cg * 8;
+                        ok[k] = g0 + k < ITEMS && m < p.M && n < p.N;
+                        if constexpr (!OUTF32)
+                            uw[k] = ok[k] ? *reinterpret_cast<const u32x4*>(p.aux + (int64_t)m * p.ldaux + (n - cofs))
+                                          : u32x4{0u, 0u, 0u, 0u};
                     }
-                } else {  // EPI_GELU_BWD: dU = dY * GeLU'(U)
-                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    const u32x4 uw = *reinterpret_cast<const u32x4*>(p.aux + (int64_t)m * p.ldaux + nl);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[2 * q] *= gelu_prime_sel(Store16<ST>::lo(uw[q]), p.gelu_tanh != 0);
-                        v[2 * q + 1] *= gelu_prime_sel(Store16<ST>::hi(uw[q]), p.gelu_tanh != 0);
+                    for (int k = 0; k < G; ++k) {
+                        const int e = tid + (g0 + k) * NT;
+                        const int lr = e / GPR, cg = e % GPR;
+                        if (g0 + k < ITEMS) {
+                            lo[k] = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8);
+                            hi[k] = *reinterpret_cast<const f32x4*>(stage + lr * ELD + cg * 8 + 4);
+                        }
                     }
-                    u32x4 o;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o[q] = Store16<ST>::pack2(v[2 * q], v[2 * q + 1]);
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
+                    for (int k = 0; k < G; ++k) {
+                        if (!ok[k]) continue;
+                        const int e = tid + (g0 + k) * NT;
+                        const int lr = e / GPR, cg = e % GPR;
+                        const int m = m0 + half * EROWS + lr, nl = n0 + cg * 8 - cofs;
+                        if constexpr (OUTF32) {
+                            float* c = reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + nl;
+                            *reinterpret_cast<f32x4*>(c) = lo[k];
+                            *reinterpret_cast<f32x4*>(c + 4) = hi[k];
+                        } else {  // EPI_GELU_BWD: dU = dY * GeLU'(U)
+                            float v[8] = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                v[2 * q] *= gelu_prime_sel(Store16<ST>::lo(uw[k][q]), p.gelu_tanh != 0);
+                                v[2 * q + 1] *= gelu_prime_sel(Store16<ST>::hi(uw[k][q]), p.gelu_tanh != 0);
+                            }
+                            u32x4 o;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) o[q] = Store16<ST>::pack2(v[2 * q], v[2 * q + 1]);
+                            *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
+                        }
+                    }
                 }
             }
             if constexpr (OUTF32) {
