@@ -704,19 +704,31 @@ struct GemmCore {
 template <typename ST, int FM, int FN, int WTM, int WTN, int SP, bool GELU>
 __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN], const bf16_t* bias, int ncols,
                                            int wm, int wn, int lane, bool tanh_form = false) {
+    // The wave's bias words, all loaded before the first is used (a lane past the valid
+    // columns reads the first word instead and takes zeros).
+    u32x2 bws[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bws[j][q] = u32x2{0u, 0u};
+    if (bias) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+                const u32x2 w = *reinterpret_cast<const u32x2*>(bias + (nl < ncols ? nl : 0));
+                bws[j][q] = nl < ncols ? w : u32x2{0u, 0u};
+            }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int nl = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);  // first of the 4 columns
-            float b4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias && nl < ncols) {
-                const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + nl);
-                b4[0] = Store16<ST>::lo(bw[0]);
-                b4[1] = Store16<ST>::hi(bw[0]);
-                b4[2] = Store16<ST>::lo(bw[1]);
-                b4[3] = Store16<ST>::hi(bw[1]);
-            }
+            const u32x2 bw = bws[j][q];
+            const float b4[4] = {Store16<ST>::lo(bw[0]), Store16<ST>::hi(bw[0]), Store16<ST>::lo(bw[1]),
+                                 Store16<ST>::hi(bw[1])};
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 float v[4];
