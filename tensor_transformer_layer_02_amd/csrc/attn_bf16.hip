@@ -443,23 +443,50 @@ __global__ void __launch_bounds__(NT) attn_rowdot_kernel(const AttnArgs a) {
     }
 }
 
-// Sum of the two query halves' partial dK (or dV) of a key group: the half-1
-// wave writes value r of d block db for lane l at [((db*16 + r)*4 + kg)*64 + l]
-// and the half-0 wave adds it.  Every wave of the workgroup calls it.
+// Sum of two partial dK, dV or dQ^T of the same rows through LDS: the wave with
+// qh = 1 writes its values to slot kg and the wave with qh = 0 adds them (other
+// values of qh only keep the barriers).  Every wave of the workgroup calls it.
+// Up to d = 96 value r of d block db, lane l sits at
+// [(((db*4 + r/4)*4 + kg)*64 + l)*4 + r%4] (16 bytes per lane and access, all
+// reads of a block issued before its adds); at d = 128, where the registers
+// for those reads would come from spills, at [((db*16 + r)*4 + kg)*64 + l].
 template <int DB>
 __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DB], float* mg, int qh, int kg, int lane) {
-    if (qh == 1) {
+    if constexpr (DB <= 3) {
+        if (qh == 1) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mg[((16 * db + r) * 4 + kg) * 64 + lane] = acc[db][r];
-    }
-    __syncthreads();
-    if (qh == 0) {
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4*>(mg + (((db * 4 + r4) * 4 + kg) * 64 + lane) * 4) =
+                        f32x4{acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
+        }
+        __syncthreads();
+        if (qh == 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db) {
+                f32x4 t[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[db][r] += mg[((16 * db + r) * 4 + kg) * 64 + lane];
+                for (int r4 = 0; r4 < 4; ++r4)
+                    t[r4] = *reinterpret_cast<const f32x4*>(mg + (((db * 4 + r4) * 4 + kg) * 64 + lane) * 4);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] += t[r / 4][r % 4];
+            }
+        }
+    } else {
+        if (qh == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mg[((16 * db + r) * 4 + kg) * 64 + lane] = acc[db][r];
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] += mg[((16 * db + r) * 4 + kg) * 64 + lane];
+        }
     }
     __syncthreads();
 }
