@@ -148,6 +148,45 @@ struct RowGeom {
 template <int D>
 using PairGeom = RowGeom<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
 
+// One 16-byte-per-lane buffer load into LDS (lane l writes dst + 16 l).  A
+// plain function: with the builtin written inside the templates below, the
+// compiler's host pass emitted launch stubs only for the first storage type.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
+// Direct global -> LDS loads of ROWS rows x D (row-major, stride ld) into a
+// swizzled [ROWS][D] tile: instruction i of wave w fills tile bytes
+// [(w + 8i) * 1024, +1024), lane l the 16 bytes at +16 l, so the lane holding
+// row r, physical chunk pc fetches logical chunk pc ^ swz(r) of that row (the
+// byte image toff() gives).  Rows at or past `nvalid` read as zeros.
+template <int D, int ROWS>
+struct TileDMA {
+    static constexpr int BYTES = ROWS * D * 2;
+    static constexpr int NI = BYTES / (8 * 1024);
+    static_assert(BYTES % (8 * 1024) == 0, "the tile must split into 1 KB pieces over 8 waves");
+    int row[NI];
+    uint32_t off[NI];
+    __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int q = (wave + 8 * i) * 1024 + 16 * lane;
+            const int r = q / (2 * D), pc = (q % (2 * D)) / 16;
+            row[i] = r;
+            off[i] = (uint32_t)(r * ld * 2 + ((pc ^ swz<D>(r)) << 4));
+        }
+    }
+    __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int nvalid, char* tile,
+                                         int wave) const {
+        const int rem = nvalid - row0;
+        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * ld * 2 + D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)(rem > 0 ? row0 : 0) * ld, bytes);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            load16_lds(rs, tile + (wave + 8 * i) * 1024, row[i] < rem ? off[i] : OOB);
+    }
+};
+
 // Per-lane LDS byte offsets of the fragment reads of a [rows][D] tile.  The
 // chunk swizzle depends only on the row modulo 16, so a row base that is a
 // multiple of 16 (and the tile base) is a uniform addend.
@@ -249,6 +288,76 @@ struct PairRows {
     }
 };
 
+// One pair step of the forward for one wave: the online-softmax update of its 32
+// queries (Q^T in qf) from the 64-key block at rows rb .. rb+63 of the pair tiles
+// Kt, Vt (keys k0 ..).  The tiles are restrict pointers so that the compiler does
+// not wait for the loads in flight into the other stage.
+template <int D, typename ST>
+__device__ __forceinline__ void fwd_pair(const AttnArgs& a, const FragAddr<D>& fa, const char* __restrict__ Kt,
+                                         const char* __restrict__ Vt, const u32x4 (&qf)[D / 16],
+                                         f32x16 (&oacc)[D / 32], float& mref, float& lsum, int rb, int k0,
+                                         int qw0, int qw, int lane) {
+    constexpr int KC = D / 16, DB = D / 32;
+    constexpr float LAZY = 8.f;
+    const int s = a.seq;
+    f32x16 sacc[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int c = 0; c < KC; ++c)  // the two halves' chains interleaved
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
+    // Keep two chunks' reads in flight: 4 LDS reads, then (2 MFMAs, 2 reads) per chunk.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int c = 0; c + 2 < KC; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // Masks only where the block reaches past the diagonal or the
+    // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
+    // the max and the exponent.
+    if ((a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 32 * h + res_row(r, lane);
+                if (key >= s || (a.causal && key > qw)) sacc[h][r] = -INFINITY;
+            }
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[h][r]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * a.scale_log2;
+    if (any_lane(bmax > mref + LAZY)) {  // move the reference (to the block max where it grew)
+        const float mnew = fmaxf(mref, bmax);
+        const float alpha = ex2(mref - ((mnew == -INFINITY) ? 0.f : mnew));
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        mref = mnew;
+    }
+    const float msub = (mref == -INFINITY) ? 0.f : mref;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -msub));
+            sacc[h][r] = pv;
+            lsum += pv;
+        }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 pf = pack_chunk<ST>(sacc[kc >> 1], kc & 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = Store16<ST>::mfma(fa.frag_tr(Vt, rb, db, kc), pf, oacc[db]);
+    }
+}
+
 // Forward.  The two waves of a row group (32 queries) take alternate 64-key
 // blocks of each streamed pair; their online-softmax
 // states (m, l, O^T) merge through LDS at the end.  The running max is a
@@ -261,8 +370,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     constexpr int SLOT = 2 * PT;                                   // K pair, V pair
     constexpr int NMERGE = DB * 16 + 2;                            // m, l, O^T per lane
     constexpr int SMEM = 2 * SLOT > NMERGE * 4 * 64 * 4 ? 2 * SLOT : NMERGE * 4 * 64 * 4;
-    constexpr float LAZY = 8.f;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
@@ -282,9 +390,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
 
     FragAddr<D> fa;
     fa.init(lane);
-    PairGeom<D> geo;
-    geo.init(a.ld_qkv, tid);
-    u32x4 kv[PairGeom<D>::NI], vv[PairGeom<D>::NI];
+    TileDMA<D, 2 * BKV> gkv;  // K and V pair rows (both stride ld_qkv) straight into LDS
+    gkv.init(a.ld_qkv, wave, lane);
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -293,84 +400,22 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
 
     const int nkb = pr.nkb;
     const int npair = (nkb + 1) / 2;
-    geo.load(Kg, a.ld_qkv, 0, s, kv);
-    geo.load(Vg, a.ld_qkv, 0, s, vv);
-    geo.store(smem, kv);
-    geo.store(smem + PT, vv);
+    gkv.load(Kg, a.ld_qkv, 0, s, smem, wave);
+    gkv.load(Vg, a.ld_qkv, 0, s, smem + PT, wave);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into LDS are done
     __syncthreads();
 
     for (int it = 0; it < npair; ++it) {
-        const bool more = it + 1 < npair;
-        if (more) {
-            geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
-            geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
+        char* const cur = smem + (it & 1) * SLOT;
+        char* const nxt = smem + ((it + 1) & 1) * SLOT;
+        if (it + 1 < npair) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
+            gkv.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt, wave);
+            gkv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt + PT, wave);
         }
-        const char* Kt = smem + (it & 1) * SLOT;
-        const char* Vt = Kt + PT;
         const int kb = 2 * it + kp, k0 = kb * BKV, rb = BKV * kp;
-        if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31)) {  // some key of the block is visible to this wave
-            f32x16 sacc[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int c = 0; c < KC; ++c)  // the two halves' chains interleaved
-#pragma unroll
-                for (int h = 0; h < 2; ++h) sacc[h] = Store16<ST>::mfma(fa.frag_rows(Kt, rb + 32 * h, c), qf[c], sacc[h]);
-            // Keep two chunks' reads in flight: 4 LDS reads, then (2 MFMAs, 2 reads) per chunk.
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int c = 0; c + 2 < KC; ++c) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            // Masks only where the block reaches past the diagonal or the
-            // sequence end; the scale 1/sqrt(d) (and log2 e) is folded into
-            // the max and the exponent.
-            if ((a.causal && k0 + BKV - 1 > qw0) || k0 + BKV > s) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * h + res_row(r, lane);
-                        if (key >= s || (a.causal && key > qw)) sacc[h][r] = -INFINITY;
-                    }
-            }
-            float bmax = -INFINITY;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, sacc[h][r]);
-            bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * a.scale_log2;
-            if (any_lane(bmax > mref + LAZY)) {  // move the reference (to the block max where it grew)
-                const float mnew = fmaxf(mref, bmax);
-                const float alpha = ex2(mref - ((mnew == -INFINITY) ? 0.f : mnew));
-                lsum *= alpha;
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-                mref = mnew;
-            }
-            const float msub = (mref == -INFINITY) ? 0.f : mref;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pv = ex2(fmaf(sacc[h][r], a.scale_log2, -msub));
-                    sacc[h][r] = pv;
-                    lsum += pv;
-                }
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const u32x4 pf = pack_chunk<ST>(sacc[kc >> 1], kc & 1);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] = Store16<ST>::mfma(fa.frag_tr(Vt, rb, db, kc), pf, oacc[db]);
-            }
-        }
-        if (more) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
-            char* nxt = smem + ((it + 1) & 1) * SLOT;
-            geo.store(nxt, kv);
-            geo.store(nxt + PT, vv);
-        }
+        if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31))  // some key of the block is visible to this wave
+            fwd_pair<D, ST>(a, fa, cur, cur + PT, qf, oacc, mref, lsum, rb, k0, qw0, qw, lane);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -490,45 +535,6 @@ __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DB], float* mg, int q
     }
     __syncthreads();
 }
-
-// One 16-byte-per-lane buffer load into LDS (lane l writes dst + 16 l).  A
-// plain function: with the builtin written inside the templates below, the
-// compiler's host pass emitted launch stubs only for the first storage type.
-__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, off, 0, 0, 0);
-}
-
-// Direct global -> LDS loads of ROWS rows x D (row-major, stride ld) into a
-// swizzled [ROWS][D] tile: instruction i of wave w fills tile bytes
-// [(w + 8i) * 1024, +1024), lane l the 16 bytes at +16 l, so the lane holding
-// row r, physical chunk pc fetches logical chunk pc ^ swz(r) of that row (the
-// byte image toff() gives).  Rows at or past `nvalid` read as zeros.
-template <int D, int ROWS>
-struct TileDMA {
-    static constexpr int BYTES = ROWS * D * 2;
-    static constexpr int NI = BYTES / (8 * 1024);
-    static_assert(BYTES % (8 * 1024) == 0, "the tile must split into 1 KB pieces over 8 waves");
-    int row[NI];
-    uint32_t off[NI];
-    __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int q = (wave + 8 * i) * 1024 + 16 * lane;
-            const int r = q / (2 * D), pc = (q % (2 * D)) / 16;
-            row[i] = r;
-            off[i] = (uint32_t)(r * ld * 2 + ((pc ^ swz<D>(r)) << 4));
-        }
-    }
-    __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int nvalid, char* tile,
-                                         int wave) const {
-        const int rem = nvalid - row0;
-        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * ld * 2 + D * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)(rem > 0 ? row0 : 0) * ld, bytes);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            load16_lds(rs, tile + (wave + 8 * i) * 1024, row[i] < rem ? off[i] : OOB);
-    }
-};
 
 // One wave's share of one streamed pair of 64-query blocks in the dK/dV pass:
 // keys kw0 .. kw0+31 (K^T, V^T in kf, vf), queries 32 (half) of block j of
