@@ -102,51 +102,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Thread geometry of moving ROWS rows x D columns (16-byte chunks t + THREADS i
-// for thread t) from a row-major bf16 matrix with row stride ld into a
-// swizzled LDS tile; computed once per kernel, shared by every matrix of the
-// same shape.  When the chunks do not split evenly, the threads past the last
-// chunk of the final round load nothing and store nothing.
-template <int D, int ROWS, int THREADS>
-struct RowGeom {
-    static constexpr int CH = D / 8;                           // chunks per row
-    static constexpr int TOTAL = ROWS * CH;
-    static constexpr int NI = (TOTAL + THREADS - 1) / THREADS;  // chunks per thread
-    static constexpr bool EXACT = TOTAL % THREADS == 0;
-    uint32_t off[NI];  // byte offset of the chunk from the block's first row
-    int row[NI];       // its row within the block (1 << 30: no chunk)
-    int dst[NI];       // its byte offset in the LDS tile (-1: no chunk)
-    __device__ __forceinline__ void init(int64_t ld, int tid) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int u = tid + THREADS * i, r = u / CH, c = u % CH;
-            const bool has = EXACT || u < TOTAL;
-            row[i] = has ? r : (1 << 30);
-            off[i] = has ? (uint32_t)(r * ld * 2 + c * 16) : OOB;
-            dst[i] = has ? toff<D>(r, c * 8) : -1;
-        }
-    }
-    // Buffer loads of rows row0 .. row0+ROWS-1 (rows >= nvalid read as zeros):
-    // the buffer base moves to row0, so no lane branches.
-    __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int nvalid,
-                                         u32x4 (&v)[NI]) const {
-        const int rem = nvalid - row0;
-        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * ld * 2 + D * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)(rem > 0 ? row0 : 0) * ld, bytes);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t o = row[i] < rem ? off[i] : OOB;
-            v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
-        }
-    }
-    __device__ __forceinline__ void store(char* tile, const u32x4 (&v)[NI]) const {
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if (EXACT || i + 1 < NI || dst[i] >= 0) *reinterpret_cast<u32x4*>(tile + dst[i]) = v[i];
-    }
-};
-template <int D>
-using PairGeom = RowGeom<D, 2 * BKV, NT8>;  // two consecutive 64-row blocks, 8 waves
 
 // One 16-byte-per-lane buffer load into LDS (lane l writes dst + 16 l).  A
 // plain function: with the builtin written inside the templates below, the
@@ -752,7 +707,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
 // One wave's dQ^T update from 32 keys k0 .. k0+31 of a streamed K/V pair in LDS
 // (rows rb .. rb+31 of the pair tiles) for its 32 queries (Q^T, dO^T in qf, of).
 template <int D, typename ST>
-__device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa, const char* Kt, const char* Vt,
+__device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa, const char* __restrict__ Kt,
+                                        const char* __restrict__ Vt,
                                         const u32x4 (&qf)[D / 16], const u32x4 (&of)[D / 16],
                                         f32x16 (&dq)[D / 32], int rb, int k0, int qw0, int qw, float lse2,
                                         float Dv, int lane) {
@@ -807,7 +763,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
     constexpr int SLOT = 2 * PT;  // K pair, V pair
     constexpr int SMEM = 2 * SLOT > DB * 16 * 4 * 64 * 4 ? 2 * SLOT : DB * 16 * 4 * 64 * 4;
-    __shared__ __attribute__((aligned(16))) char smem[SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
@@ -824,9 +780,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
 
     FragAddr<D> fa;
     fa.init(lane);
-    PairGeom<D> geo;
-    geo.init(a.ld_qkv, tid);
-    u32x4 kv[PairGeom<D>::NI], vv[PairGeom<D>::NI];
+    TileDMA<D, 2 * BKV> gkv;  // K and V pair rows (both stride ld_qkv) straight into LDS
+    gkv.init(a.ld_qkv, wave, lane);
 
     const int nphase = (MASKED && xl != x) ? 2 : 1;
     for (int ph = 0; ph < nphase; ++ph) {
@@ -848,20 +803,19 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
 
         const int nkb = MASKED ? (a.causal ? qb + 1 : nb) : pr.nkb;  // key blocks the phase streams
         const int npair = (nkb + 1) / 2;
-        geo.load(Kg, a.ld_qkv, 0, s, kv);
-        geo.load(Vg, a.ld_qkv, 0, s, vv);
-        geo.store(smem, kv);
-        geo.store(smem + PT, vv);
+        gkv.load(Kg, a.ld_qkv, 0, s, smem, wave);
+        gkv.load(Vg, a.ld_qkv, 0, s, smem + PT, wave);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into LDS are done
         __syncthreads();
 
         for (int it = 0; it < npair; ++it) {
-            const bool more = it + 1 < npair;
-            if (more) {
-                geo.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, kv);
-                geo.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, vv);
+            char* const Kt = smem + (it & 1) * SLOT;
+            char* const Vt = Kt + PT;
+            if (it + 1 < npair) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
+                char* const nxt = smem + ((it + 1) & 1) * SLOT;
+                gkv.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt, wave);
+                gkv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt + PT, wave);
             }
-            const char* Kt = smem + (it & 1) * SLOT;
-            const char* Vt = Kt + PT;
             if constexpr (MASKED) {  // 32 keys: half kq % 2 of block 2 it + kq / 2
                 const int kb = 2 * it + (kq >> 1), rb = BKV * (kq >> 1) + 32 * (kq & 1), k0 = 2 * it * BKV + rb;
                 if (qw0 < s && kb < nkb && !(a.causal && k0 > qw0 + 31))
@@ -873,11 +827,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
                     dq_keys<D, ST>(a, fa, Kt, Vt, qf, of, dq, rb + 32, k0 + 32, qw0, qw, lse2, Dv, lane);
                 }
             }
-            if (more) {
-                char* nxt = smem + ((it + 1) & 1) * SLOT;
-                geo.store(nxt, kv);
-                geo.store(nxt + PT, vv);
-            }
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
 
