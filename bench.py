@@ -17,6 +17,9 @@ Prints ONE JSON line on stdout:
   step_spread      median / min of single steps (an event pair around each), warm and
                    with a 512 MiB write before each step (cold Infinity Cache)
   kernels          per-step breakdown (average duration, TFLOP/s or GB/s)
+  other_workloads  the other per-shard shapes of the pages' models (BERT 3.9B t=8, 30B
+                   t=4 and t=1), each timed in the same run before the headline
+                   workload (its own warm-up and timed steps), ms/step and TFLOP/s
 """
 from __future__ import annotations
 
@@ -130,11 +133,47 @@ def cpu_baseline(cfg, inp, nseq):
     oracle.attn_shard_bwd(d, 0, cfg.degree, *args, p["dZ"])
     dt = time.perf_counter() - t0
     fl = shard_flops(sub, backward=True)["total"]
+    what = (f"the whole workload ({cfg.batch} sequences, {rows} tokens" if nseq == cfg.batch else
+            f"the first {nseq} of {cfg.batch} sequences ({rows} of {cfg.tokens} tokens")
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"shard 0 fwd+bwd on the first {nseq} of {cfg.batch} sequences "
-                      f"({rows} of {cfg.tokens} tokens; {fl / 1e9:.1f} GFLOP algorithmic), float64 C loops "
+            "sample": f"shard 0 fwd+bwd on {what}; {fl / 1e9:.1f} GFLOP algorithmic), float64 C loops "
                       f"with OpenMP"}
+
+
+# Other per-shard shapes of the pages' models, timed in the same run as the headline:
+# (config, warm-up steps, timed steps), each about 0.05-0.3 s of GPU time.
+OTHER_WORKLOADS = [("bert4b", 30, 20), ("g30b_t4", 5, 10), ("g30b_t1", 3, 5)]
+
+
+def time_workload(name, dtype, W, K):
+    """ms per shard fwd+bwd step (HIP events around K steps after W warm-up steps, inputs resident)
+    and algorithmic TFLOP/s of one other workload, shard 0."""
+    import torch
+
+    from tensor_transformer_layer_02_amd.configs import CONFIGS, shard_flops
+    from tensor_transformer_layer_02_amd.inputs import make_inputs
+    from tensor_transformer_layer_02_amd.shard import ShardRun
+    cfg = CONFIGS[name].with_(backward=True, dtype=dtype)
+    run = ShardRun(cfg, make_inputs(cfg), shards=[0])
+    for _ in range(W):
+        run.step(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        run.step(0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    fl = shard_flops(cfg, backward=True)["total"]
+    del run
+    torch.cuda.empty_cache()
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": f"{cfg.name}: {cfg.note}", "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads,
+            "ffn": cfg.ffn, "degree": cfg.degree, "causal": cfg.causal, "steps": K, "warmup": W,
+            "ms_per_step": round(ms, 4), "flops_per_step": fl, "tflops": round(tf, 1),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
 def main():
@@ -148,7 +187,11 @@ def main():
     ap.add_argument("--shard", type=int, default=0)
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
                     help="16-bit storage format (fp16: IEEE half with fp16 MFMAs; same dense peak)")
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=None,
+                    help="sequences in the CPU-oracle sample (default: all of the workload's sequences)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other model shapes (BERT 3.9B t=8, 30B t=4 and t=1 shards), which are "
+                         "otherwise timed first, in the same run, and reported under other_workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--recompute", action="store_true",
@@ -212,6 +255,18 @@ def main():
     clock_mhz = peak_clock_mhz()
     log(f"[bench] device {prop.name} ({prop.gcnArchName}) CUs={prop.multi_processor_count} peak clock "
         f"{clock_mhz} MHz, peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
+
+    # ---- the other model shapes first (same run; the headline below keeps its own W and K)
+    others = []
+    if not args.no_others and args.config == "gpt8b" and not args.recompute:
+        del run
+        torch.cuda.empty_cache()
+        for name, ow, ok in OTHER_WORKLOADS:
+            r = time_workload(name, cfg.dtype, ow, ok)
+            others.append(r)
+            log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step  {r['tflops']} TFLOP/s  "
+                f"({r['pct_of_bf16_peak']}% of bf16 peak)")
+        run = ShardRun(cfg, inp, shards=[args.shard], recompute=args.recompute)
 
     for _ in range(W):
         step()
@@ -317,8 +372,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline on {args.cpu_seqs} sequence(s) ...")
-        cpu = cpu_baseline(cfg, inp, args.cpu_seqs)
+        nseq = cfg.batch if args.cpu_seqs is None else max(1, min(args.cpu_seqs, cfg.batch))
+        log(f"[bench] CPU oracle baseline on {nseq} of {cfg.batch} sequence(s) ...")
+        cpu = cpu_baseline(cfg, inp, nseq)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['seconds']} s)")
 
     out = {
@@ -348,6 +404,7 @@ def main():
         "gpu": {"name": prop.name, "arch": prop.gcnArchName, "cus": prop.multi_processor_count,
                 "peak_clock_mhz": clock_mhz},
         "kernels": kernels,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 

@@ -55,9 +55,10 @@
  *     backward entry points run independent launches (a weight gradient, a
  *     bias column sum) on the device's auxiliary stream (created on first
  *     use, default priority), forked from and joined back to `stream` with
- *     events, so everything a call enqueues precedes later work on `stream`;
- *     host threads that call them concurrently are serialised while they
- *     enqueue.
+ *     events, so everything a call enqueues precedes later work on `stream`,
+ *     also when a launch fails part-way (the auxiliary stream is joined back
+ *     on every return); host threads that call them concurrently are
+ *     serialised while they enqueue.
  *   - Errors: every argument is validated on the host BEFORE any HIP call
  *     or enqueue; on failure nothing is written and a tp_status is
  *     returned.  A failed launch returns TP_EHIP.  No C++ exception
@@ -65,6 +66,11 @@
  *   - Alignment: every device pointer must be 16-byte aligned; hidden,
  *     F/t and (H/t)*d must be multiples of 8.  Supported head dims:
  *     32, 64, 96, 128 (bf16, fp16) and 8..128 in steps of 8 (fp32).
+ *   - Size limit: the kernels address operands through 32-bit byte ranges, so
+ *     every matrix a shard call touches must be smaller than 2 GiB: [T, h],
+ *     [T, F/t] and [T, 3w] in dims.act, and the fp32 gradients [h, F] and
+ *     [h, h].  Larger dims are refused with TP_EUNSUPPORTED before any HIP
+ *     call (tp_check_dims reports it too).
  *   - Calls on different streams may run concurrently if their output
  *     buffers do not overlap.
  */
@@ -85,7 +91,7 @@ typedef enum {
     TP_ESHARD = 3,        /* shard index outside [0, t) or t < 1                      */
     TP_EALIGN = 4,        /* pointer not 16-byte aligned or size not a multiple of 8  */
     TP_EDTYPE = 5,        /* dims.act is not one of TP_FP32, TP_BF16, TP_FP16         */
-    TP_EUNSUPPORTED = 6,  /* head dimension not supported                             */
+    TP_EUNSUPPORTED = 6,  /* head dimension not supported, or a matrix of 2 GiB or more */
     TP_EHIP = 7,          /* a kernel launch failed                                   */
     TP_ESIZE = 8          /* work buffer smaller than tp_*_work_bytes                 */
 } tp_status;
@@ -258,6 +264,20 @@ int tp_attn_shard_bwd_recompute(const tp_dims* dims, int shard, int degree,
 int tp_profile_enable(void* const* events, int npairs);
 int tp_profile_count(int step);
 int tp_profile_kernels(int step);
+
+/*
+ * Test hook (coverage of every GEMM tile shape against the oracle; no effect on
+ * what is computed, only on how it is tiled).  The 16-bit GEMMs pick one of
+ * tp_test_gemm_tile_count() tile shapes (and, for the fp32 weight gradients, a
+ * K split of 1 or 2) by a cost model.  tp_test_force_gemm_tile(tile, ksplit)
+ * makes every later GEMM for which tile `tile` is valid use it (a tile must
+ * not straddle a Q|K|V segment; two tiles serve only the fp32 weight
+ * gradients), with a K split of 2 where allowed if ksplit == 2; tile == -1
+ * restores the cost model.  TP_EINVAL for tile outside [-1, count) or ksplit
+ * outside [0, 2].  Process-wide and not thread-safe: for tests only.
+ */
+int tp_test_force_gemm_tile(int tile, int ksplit);
+int tp_test_gemm_tile_count(void);
 
 /*
  * Verification-only local sum that stands in for the all-reduce on one GPU

@@ -71,6 +71,15 @@ int derive(const tp_dims* dims, int shard, int degree, Shape* o) {
     // Launch-grid limits (grid y <= 65535 with 64-row tiles; int indices).
     if (s.T > (int64_t)65535 * 64 || s.b * s.Hs > 65535) return TP_EUNSUPPORTED;
     if (s.h > INT_MAX / 4 || s.F > INT_MAX / 4) return TP_EUNSUPPORTED;
+    // The kernels address their operands through buffer descriptors with 32-bit
+    // byte ranges and offsets, so every matrix the shard reads or writes must stay
+    // below 2 GiB: activations and partials [T, h], [T, F/t], [T, 3w], the weights
+    // [h, F] and [h, h], and their fp32 gradients.
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t ext[] = {s.T * s.h * s.e, s.T * s.Fs * s.e, s.T * 3 * s.w * s.e,
+                           s.h * s.F * 4, s.h * s.h * 4};
+    for (int64_t x : ext)
+        if (x >= lim) return TP_EUNSUPPORTED;
     if (o) *o = s;
     return TP_OK;
 }
@@ -198,6 +207,8 @@ struct AuxScope {
     Aux* a = nullptr;
     std::unique_lock<std::mutex> lock;
     hipError_t err = hipSuccess;
+    hipStream_t main_st = nullptr;
+    bool forked = false;  // work is on the auxiliary stream that `main_st` does not yet wait for
     AuxScope() {
         int dev = 0;
         if ((err = hipGetDevice(&dev)) != hipSuccess) return;
@@ -225,12 +236,25 @@ struct AuxScope {
         a = &x;
     }
     hipError_t to_aux(hipStream_t main, int k) {
+        main_st = main;
+        forked = true;  // from here on the destructor joins, whatever the outcome
         hipError_t e = hipEventRecord(a->ev[k], main);
         return e != hipSuccess ? e : hipStreamWaitEvent(a->st, a->ev[k], 0);
     }
     hipError_t to_main(hipStream_t main, int k) {
         hipError_t e = hipEventRecord(a->ev[k], a->st);
-        return e != hipSuccess ? e : hipStreamWaitEvent(main, a->ev[k], 0);
+        if (e == hipSuccess) e = hipStreamWaitEvent(main, a->ev[k], 0);
+        if (e == hipSuccess) forked = false;
+        return e;
+    }
+    // An early (error) return after a fork still orders the caller's stream after
+    // everything enqueued on the auxiliary stream, which may read or write the
+    // caller's buffers.  Best effort: there is no status left to report.
+    ~AuxScope() {
+        if (a && forked) {
+            if (hipEventRecord(a->ev[AUX_EVENTS - 1], a->st) == hipSuccess)
+                (void)hipStreamWaitEvent(main_st, a->ev[AUX_EVENTS - 1], 0);
+        }
     }
 };
 
@@ -333,6 +357,14 @@ int tp_profile_enable(void* const* events, int npairs) {
     for (int i = 0; i < TP_NUM_STEPS; ++i) g_prof.count[i] = g_prof.kernels[i] = 0;
     return TP_OK;
 }
+
+int tp_test_force_gemm_tile(int tile, int ksplit) {
+    if (tile < -1 || tile >= tp::gemm_tile_count() || ksplit < 0 || ksplit > 2) return TP_EINVAL;
+    tp::gemm_force_tile(tile, ksplit);
+    return TP_OK;
+}
+
+int tp_test_gemm_tile_count(void) { return tp::gemm_tile_count(); }
 
 int tp_profile_count(int step) { return (step >= 0 && step < TP_NUM_STEPS) ? g_prof.count[step] : -1; }
 

@@ -1080,7 +1080,19 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
     }
 }
 
+// Test hook (gemm_force_tile): a tile index of kCands and a K split that replace
+// the cost model's choice for every GEMM they are valid for; -1 / 0: the model.
+int g_force_tile = -1;
+int g_force_split = 0;
+
 }  // namespace
+
+void gemm_force_tile(int tile, int ksplit) {
+    g_force_tile = tile;
+    g_force_split = ksplit;
+}
+
+int gemm_tile_count() { return (int)(sizeof(kCands) / sizeof(kCands[0])); }
 
 // Tile shape (and K split) with the least estimated time on 256 CUs.  A CU
 // gets ceil(items / 256) tiles and runs o = min(occupancy, that) of them at
@@ -1103,12 +1115,14 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     int kmax = 0;
     for (int i = 0; i < n; ++i) kmax = d[i].K > kmax ? d[i].K : kmax;
     const double kov = (d[0].epi == EPI_BIAS_GELU || d[0].epi == EPI_GELU_BWD) ? K_OVERHEAD_GELU : K_OVERHEAD;
-    for (int c = 0; c < (int)(sizeof(kCands) / sizeof(kCands[0])); ++c) {
+    const int ncand = (int)(sizeof(kCands) / sizeof(kCands[0]));
+    const bool forced = g_force_tile >= 0 && g_force_tile < ncand;
+    for (int c = 0; c < ncand; ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
         // The 8-wave tiles take a whole CU's registers; beside another launch the
         // co-resident 4-wave tiles do better (attention dX beside dWqkv: +1% per step).
-        if ((c == 8 || c == 9) && d[0].concurrent) continue;
+        if ((c == 8 || c == 9) && d[0].concurrent && !forced) continue;
         bool ok = true;
         int64_t t = 0;
         for (int i = 0; i < n; ++i) {
@@ -1118,6 +1132,12 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
             t += (int64_t)((g.M + k.bm - 1) / k.bm) * ((g.N + k.bn - 1) / k.bn);
         }
         if (!ok) continue;
+        if (forced && c == g_force_tile) {  // test hook: this tile wherever it is valid
+            best = c;
+            best_split = (g_force_split == 2 && allow_split && tn32) ? 2 : 1;
+            best_cost = -1.0;
+            break;
+        }
         for (int split = 1; split <= ((allow_split && tn32) ? 2 : 1); ++split) {
             const int64_t tpc = (t * split + 255) / 256;  // tiles per CU
             const int64_t o = tpc < k.occ ? tpc : k.occ;

@@ -59,6 +59,11 @@ hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s);
 // split in two along K (*ksplit_out reports it); the output blocks are then
 // zeroed first by a kernel on the same stream and the halves added atomically.
 hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s);
+// Test hook: every later 16-bit GEMM for which tile `tile` (0 .. gemm_tile_count()-1)
+// is valid uses it, with a K split of `ksplit` (2: fp32-output GEMMs split in two;
+// else no split); tile < 0 restores the cost model.  Process-wide, not thread-safe.
+void gemm_force_tile(int tile, int ksplit);
+int gemm_tile_count();
 
 // Zero a [rows, cols] fp32 block with row stride ld (a kernel, so it can be captured).
 // Zero n (<= ZMAX) row-major fp32 blocks (p[k]: rows[k] x cols[k], row stride

@@ -38,8 +38,14 @@ def storage_dtype(cfg: LayerConfig) -> torch.dtype:
 
 
 def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,
-                seed_base: int | None = None) -> dict:
-    """Return {name: CPU tensor in the storage dtype} for the requested tensors."""
+                seed_base: int | None = None, qk_std: float | None = None,
+                x_ramp: float = 0.0) -> dict:
+    """Return {name: CPU tensor in the storage dtype} for the requested tensors.
+
+    Large-logit variant (tests of the softmax at large score magnitudes): ``qk_std``
+    replaces the standard deviation of Wq and Wk, and ``x_ramp`` scales row j of each
+    sequence of X by 1 + x_ramp * j / (seq - 1), so that later keys carry larger scores
+    than earlier ones.  Both default to the plain recipe."""
     shapes = tensor_shapes(cfg)
     base = 1000 * cfg.cid if seed_base is None else seed_base
     dt = storage_dtype(cfg)
@@ -52,6 +58,8 @@ def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,
             std = 1.0
         elif name.startswith("b"):
             std = bias_std
+        elif name in ("Wq", "Wk") and qk_std is not None:
+            std = qk_std
         else:
             std = WEIGHT_STD
         if std == 0.0:
@@ -60,6 +68,9 @@ def make_inputs(cfg: LayerConfig, bias_std: float = 0.0, names=None,
             g = torch.Generator().manual_seed(base + k)
             t = torch.randn(shape, generator=g, dtype=torch.float32)
             t.mul_(std)
+            if name == "X" and x_ramp:
+                pos = torch.arange(cfg.seq, dtype=torch.float32) / max(1, cfg.seq - 1)
+                t.view(cfg.batch, cfg.seq, -1).mul_((1.0 + x_ramp * pos)[None, :, None])
         out[name] = t.to(dt)
     return out
 

@@ -50,6 +50,17 @@ class ShardRun:
                 "dX_attn": torch.empty((T, h), dtype=self.dt, device=self.dev),
             }
 
+    def poison(self, i=None, grads=False):
+        """Fill the outputs, saved and work buffers of shard i (all shards if None), and the
+        gradient buffers if asked, with all-ones bytes: a NaN in bfloat16, IEEE half and
+        float32 alike, so anything a kernel leaves unwritten shows up as non-finite."""
+        for k in (self.shards if i is None else [i]):
+            for v in self.buf[k].values():
+                v.view(torch.uint8).fill_(255)
+        if grads:
+            for v in self.grads.values():
+                v.view(torch.uint8).fill_(255)
+
     # ------------------------------------------------------------- passes
     def mlp_fwd(self, i, stream=None):
         x, b = self.x, self.buf[i]

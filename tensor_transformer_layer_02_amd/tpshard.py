@@ -25,7 +25,8 @@ EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_byte
            "tp_attn_shard_fwd", "tp_attn_shard_bwd", "tp_sum_partials", "tp_profile_enable",
            "tp_profile_count", "tp_profile_kernels", "tp_residual_layernorm", "tp_layernorm_bwd_work_bytes",
            "tp_layernorm_bwd", "tp_mlp_recompute_work_bytes", "tp_attn_recompute_work_bytes",
-           "tp_mlp_shard_bwd_recompute", "tp_attn_shard_bwd_recompute"]
+           "tp_mlp_shard_bwd_recompute", "tp_attn_shard_bwd_recompute", "tp_test_force_gemm_tile",
+           "tp_test_gemm_tile_count"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
@@ -264,3 +265,12 @@ def tp_layernorm_bwd(dtype, rows, cols, x, gamma, mean, rstd, dparts, dres, dx, 
                  _ptr(rstd), _parr(dparts), len(dparts), _ptr(dres), _ptr(dx), _ptr(dx_act), _ptr(dgamma),
                  _ptr(dbeta), _ptr(dres_sum), _ptr(dx_sum), _ptr(work), work.numel() * work.element_size(),
                  _stream(stream))
+
+
+def tp_test_force_gemm_tile(tile: int, ksplit: int = 0) -> int:
+    """Test hook: force GEMM tile `tile` (-1: the cost model) and K split `ksplit`."""
+    return _call("tp_test_force_gemm_tile", int(tile), int(ksplit))
+
+
+def tp_test_gemm_tile_count() -> int:
+    return lib().tp_test_gemm_tile_count()

@@ -131,3 +131,39 @@ def test_entry_points_reject_before_any_launch(L):
 def test_null_dims_pointer(L):
     assert L.tp_check_dims(None, 0, 1) == 1
     assert L.tp_mlp_saved_bytes(None, 0, 1) == 0
+
+
+@pytest.mark.parametrize("kw,degree,code", [
+    # [T, h] activations at 2 GiB: T = 2^17 tokens of h = 8192 bf16 (2^31 bytes)
+    (dict(batch=128, seq=1024, hidden=8192, heads=64, ffn=32768), 8, 6),
+    # one token fewer per sequence keeps [T, h] just under 2 GiB, but [T, F/t] = [T, 4096] is fine
+    # too and the fp32 gradient [h, F] = 8192 x 32768 x 4 = 1 GiB: accepted
+    (dict(batch=128, seq=1023, hidden=8192, heads=64, ffn=32768), 8, 0),
+    # [T, F/t] at 2 GiB with [T, h] below it: t = 1 shard of an F = 4h FFN
+    (dict(batch=64, seq=1024, hidden=4096, heads=32, ffn=16384), 1, 6),
+    # fp32 weight gradient [h, F] at 2 GiB (h = 16384, F = 32768), few tokens
+    (dict(batch=1, seq=64, hidden=16384, heads=128, ffn=32768), 8, 6),
+    # fp32 activations: [T, h] = 2^14 x 2^15 x 4 bytes = 2 GiB
+    (dict(batch=16, seq=1024, hidden=32768, heads=256, ffn=32768, act=tp.TP_FP32), 256, 6),
+])
+def test_matrices_of_2gib_or_more_are_refused(L, kw, degree, code):
+    """The kernels address operands through 32-bit byte ranges: a shard whose activations,
+    FFN activations or fp32 weight gradients reach 2 GiB is refused before any HIP call."""
+    dims = d(**kw)
+    assert tp.tp_check_dims(dims, 0, degree) == code
+    if code:
+        P = _fake()
+        with pytest.raises(tp.TpError) as e:
+            tp.tp_mlp_shard_fwd(dims, 0, degree, P, P, None, P, P, P, stream=0)
+        assert e.value.code == code
+        assert tp.tp_mlp_saved_bytes(dims, 0, degree) == 0
+
+
+def test_force_tile_hook_rejects_bad_arguments(L):
+    n = tp.tp_test_gemm_tile_count()
+    assert n == 10
+    for bad in ((-2, 0), (n, 0), (0, 3), (0, -1)):
+        with pytest.raises(tp.TpError) as e:
+            tp.tp_test_force_gemm_tile(*bad)
+        assert e.value.code == 1
+    assert tp.tp_test_force_gemm_tile(-1, 0) == 0

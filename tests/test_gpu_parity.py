@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, check, oracle_inputs, oracle_shard, relerr
+from gpu_helpers import TOL, check, check_lse, oracle_inputs, oracle_shard, relerr, run_all_shards
 from tensor_transformer_layer_02_amd.configs import CONFIGS, LayerConfig
 from tensor_transformer_layer_02_amd.inputs import make_inputs
 
@@ -21,50 +21,6 @@ pytestmark = pytest.mark.gpu
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def run_all_shards(cfg: LayerConfig, bias_std: float, report):
-    from tensor_transformer_layer_02_amd.shard import ShardRun
-    inp = make_inputs(cfg, bias_std=bias_std)
-    p = oracle_inputs(inp)
-    run = ShardRun(cfg, inp)
-    tol = TOL[cfg.dtype]
-    grads = {}
-    oz = {}
-    for i in range(cfg.degree):
-        _say(f"[{cfg.name}] shard {i}/{cfg.degree} T={cfg.tokens} h={cfg.hidden} d={cfg.head_dim}")
-        run.step(i, backward=True)
-        torch.cuda.synchronize()
-        o = oracle_shard(cfg.with_(backward=True), p, i, grads=grads)
-        sv = run.saved(i)
-        for k in ("U", "Y", "QKV", "O", "LSE"):
-            check(f"shard{i}.{k}", sv[k], o[k], tol, report)
-        for k in ("Z_mlp", "Z_attn", "dX_mlp", "dX_attn"):
-            check(f"shard{i}.{k}", run.buf[i][k], o[k], tol, report)
-        oz[i] = o
-    for k in ("dA", "db1", "dB", "dWq", "dWv", "dWo", "dbq", "dbv"):
-        check(k, run.grads[k], grads[k], tol, report)
-    # the key-bias gradient is zero in exact arithmetic (softmax ignores a per-row shift)
-    # against the scale of the attention's bias gradients (with one key per query dQ and dK are
-    # exactly zero too, so dbq alone is no scale for the rounding noise)
-    scale = max(float(run.grads["dbq"].abs().max()), float(run.grads["dbv"].abs().max()))
-    assert float(run.grads["dbk"].abs().max()) <= tol * scale
-    # sum of partials + row-parallel bias == unsharded sublayer
-    import oracle
-    d = cfg.dims()
-    Zm = run.sum_partials("Z_mlp", "b2")
-    Za = run.sum_partials("Z_attn", "bo")
-    full_m = oracle.mlp_full_fwd(d, p["X"], p["A"], p["b1"], p["B"], p["b2"])
-    full_a = oracle.attn_full_fwd(d, *[p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")], p["bo"])
-    check("sum(Z_mlp)+b2 vs unsharded", Zm, full_m, tol, report)
-    check("sum(Z_attn)+bo vs unsharded", Za, full_a, tol, report)
-    dXm = run.sum_partials("dX_mlp")
-    dXa = run.sum_partials("dX_attn")
-    fb_m = oracle.mlp_full_bwd(d, p["X"], p["A"], p["b1"], p["B"], p["dZ"])
-    fb_a = oracle.attn_full_bwd(d, *[p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")], p["dZ"])
-    check("sum(dX_mlp) vs unsharded", dXm, fb_m["dX"], tol, report)
-    check("sum(dX_attn) vs unsharded", dXa, fb_a["dX"], tol, report)
-    return run
 
 
 @pytest.mark.parametrize("bias_std", [0.0, 0.02])
@@ -219,3 +175,44 @@ def test_concurrent_calls_on_two_streams_match_serial():
             assert torch.equal(ref.buf[i][k], run.buf[i][k]), (i, k)
     for k, v in ref.grads.items():
         assert torch.equal(v, run.grads[k]), k
+
+
+LARGE_LOGITS = [
+    # name, batch, seq, hidden, heads, ffn, t, causal, std of Wq and Wk
+    ("logits_d64_causal", 2, 200, 256, 4, 1024, 2, True, 0.07),
+    ("logits_d64_noncausal", 2, 160, 256, 4, 1024, 2, False, 0.07),
+    ("logits_d96_causal", 2, 190, 384, 4, 1536, 2, True, 0.06),
+    ("logits_d96_noncausal", 2, 190, 384, 4, 1536, 2, False, 0.06),
+    ("logits_d128_causal", 1, 300, 512, 4, 2048, 2, True, 0.045),
+    ("logits_d128_noncausal", 2, 257, 512, 4, 2048, 2, False, 0.045),
+]
+LAZY_LOG2 = 8.0   # the forward moves its softmax reference when a block max exceeds it by 2^8
+
+
+@pytest.mark.parametrize("case", LARGE_LOGITS, ids=[c[0] for c in LARGE_LOGITS])
+def test_large_logit_softmax(case):
+    """Scores that span tens (per-head softmax, page "Megatron-LM: what the tensor parallelism
+    paper actually says", section "The attention heads split"): Wq and Wk scaled up and X
+    ramped along each sequence, so that later keys score far above earlier ones.  The forward
+    then has to move its running softmax reference (and rescale O) as keys stream in, and the
+    two halves of a row group, which take alternate key blocks, merge states whose maxima
+    differ widely.  Every output of every shard against the oracle at the usual bar."""
+    name, b, s, h, H, F, t, causal, qk = case
+    cfg = LayerConfig(200 + LARGE_LOGITS.index(case), name, b, s, h, H, F, t, causal, "bf16", True)
+    # the inputs must exercise the rescale: in some row a later 64-key block's max score
+    # exceeds the first block's by more than the lazy threshold (base-2 units)
+    import oracle
+    p = oracle_inputs(make_inputs(cfg, bias_std=0.02, qk_std=qk, x_ramp=1.0))
+    af = oracle.attn_shard_fwd(cfg.dims(), 0, t, *[p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")])
+    d = cfg.head_dim
+    Q, K = af["Q"][:s, :d], af["K"][:s, :d]
+    S = Q @ K.T / np.sqrt(d) * 1.4426950408889634
+    if causal:
+        S = np.where(np.tril(np.ones((s, s), bool)), S, -np.inf)
+    first = S[:, :64].max(axis=1)
+    later = S[:, 64:].max(axis=1)
+    assert np.nanmax(later - first) > LAZY_LOG2, "inputs do not reach the rescale"
+    assert np.ptp(S[np.isfinite(S)]) > 30.0
+    report = []
+    run_all_shards(cfg, 0.02, report, qk_std=qk, x_ramp=1.0)
+    _say(f"[{name}] " + "; ".join(f"{n}={e:.1e}" for n, e in report))
