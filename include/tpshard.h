@@ -93,7 +93,8 @@ typedef enum {
     TP_EDTYPE = 5,        /* dims.act is not one of TP_FP32, TP_BF16, TP_FP16         */
     TP_EUNSUPPORTED = 6,  /* head dimension not supported, or a matrix of 2 GiB or more */
     TP_EHIP = 7,          /* a kernel launch failed                                   */
-    TP_ESIZE = 8          /* work buffer smaller than tp_*_work_bytes                 */
+    TP_ESIZE = 8,         /* work buffer smaller than tp_*_work_bytes                 */
+    TP_ESCRATCH = 9       /* needs more than the no-allocation entry point's scratch  */
 } tp_status;
 
 typedef enum { TP_FP32 = 0, TP_BF16 = 1, TP_FP16 = 2 } tp_dtype;
@@ -166,6 +167,28 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree,
                      const void* saved, const void* dZ,
                      void* dX_part, float* dA, float* db1, float* dB,
                      void* work, size_t work_bytes, void* stream);
+
+/*
+ * FFN shard backward that allocates nothing, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, kernels and results (bitwise) as
+ * tp_mlp_shard_bwd, with no `work` argument.  Its scratch (dU and the column-sum
+ * partials, tp_mlp_work_bytes of them) is a static device array of
+ * TP_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on until
+ * the process ends; dims whose tp_mlp_work_bytes exceed it return TP_ESCRATCH
+ * before any HIP call (the 8.3B-shape t = 8 shard needs 25.4 MB).  Every launch
+ * runs on `stream` (no auxiliary stream, no events); no device or host memory is
+ * allocated and no allocating library routine is called (the first call on a
+ * device looks up the array's device address once).  All calls on one device
+ * share that device's array and each call overwrites it before reading it (no
+ * part of it needs to start at zero): calls that overlap in time on one device
+ * (two streams, two threads) race on it and must be serialised by the caller.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int tp_mlp_shard_bwd_noalloc(const tp_dims* dims, int shard, int degree,
+                             const void* X, const void* A, const void* B,
+                             const void* saved, const void* dZ,
+                             void* dX_part, float* dA, float* db1, float* dB, void* stream);
 
 /*
  * Attention shard forward ("The attention heads split"), for every batch

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["gemm_bf16.hip", "attn_bf16.hip", "fp32_path.hip", "misc.hip", "layernorm.hip", "api.cpp"]
+SOURCES = ["gemm_bf16.hip", "attn_bf16.hip", "fp32_path.hip", "misc.hip", "layernorm.hip", "noalloc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -317,6 +317,72 @@ hipError_t attn_fwd_saved(const Shape& s, const void* X, const void* Wq, const v
     return s.h16 ? tp::attn_fwd_bf16(ad, st) : tp::attn_fwd_f32(ad, st);
 }
 
+// Pointer checks of the FFN backward (everything but the work buffer).
+int mlp_bwd_check(const void* X, const void* A, const void* B, const void* saved, const void* dZ,
+                  const void* dX_part, const float* dA, const float* db1, const float* dB) {
+    if (!X || !A || !B || !saved || !dZ || !dX_part || !dA || !dB) return TP_EINVAL;
+    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(saved) || !aligned16(dZ) ||
+        !aligned16(dX_part) || !aligned16(dA) || !aligned16(dB) || (db1 && !aligned16(db1)))
+        return TP_EALIGN;
+    return TP_OK;
+}
+
+// The FFN backward's launches: dU (GEMM with the GeLU' epilogue), db1 (column
+// sums of dU), dB and dA (one GEMM launch), dX_part.  dU and the column-sum
+// partials go to `dU` and `cs` (scratch the caller or the library provides).
+// With `aux`, the column sum runs on the auxiliary stream beside the GEMMs;
+// without, every launch runs on `st` (same kernels, same results).
+int mlp_bwd_run(const Shape& s, const void* X, const void* A, const void* B, const void* saved, const void* dZ,
+                void* dX_part, float* dA, float* db1, float* dB, void* dU, float* cs, hipStream_t st,
+                AuxScope* aux) {
+    const MlpSaved L = mlp_saved(s);
+    const void* U = at(saved, L.U, 1);
+    const void* Y = at(saved, L.Y, 1);
+    const int64_t c0 = s.i * s.Fs;
+
+    tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * GeLU'(U)
+    g.M = (int)s.T; g.N = (int)s.Fs; g.K = (int)s.h;
+    g.A = dZ; g.lda = s.h; g.a_kcontig = true;
+    g.B[0] = at(B, c0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
+    g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
+    g.epi = tp::EPI_GELU_BWD;
+    g.gelu_tanh = s.gelu_tanh;
+    if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
+
+    if (db1) {  // db1[C_i] = column sums of dU (beside the GEMMs below when there is an aux stream)
+        float* outs[3] = {db1 + c0, nullptr, nullptr};
+        hipStream_t cst = st;
+        if (aux) {
+            if (aux->to_aux(st, 0) != hipSuccess) return TP_EHIP;
+            cst = aux->a->st;
+        }
+        StepTimer t(TP_STEP_MLP_DB1, cst);
+        if (tp::colsum(fmt(s), dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, cst) != hipSuccess) return TP_EHIP;
+    }
+
+    tp::GemmDesc gw[2];  // one launch: dB[C_i, :] = Y^T dZ and dA[:, C_i] = X^T dU
+    tp::GemmDesc& gb = gw[0];
+    gb.M = (int)s.Fs; gb.N = (int)s.h; gb.K = (int)s.T;
+    gb.A = Y; gb.lda = s.Fs; gb.a_kcontig = false;
+    gb.B[0] = dZ; gb.ldb = s.h; gb.b_kcontig = false;
+    gb.C[0] = dB + c0 * s.h; gb.ldc = s.h; gb.out_f32 = true;
+    tp::GemmDesc& ga = gw[1];
+    ga.M = (int)s.h; ga.N = (int)s.Fs; ga.K = (int)s.T;
+    ga.A = X; ga.lda = s.h; ga.a_kcontig = false;
+    ga.B[0] = dU; ga.ldb = s.Fs; ga.b_kcontig = false;
+    ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
+    if (gemm2(s, gw, st, TP_STEP_MLP_DW) != hipSuccess) return TP_EHIP;
+
+    tp::GemmDesc gx;  // dX_part = dU A[:, C_i]^T
+    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)s.Fs;
+    gx.A = dU; gx.lda = s.Fs; gx.a_kcontig = true;
+    gx.B[0] = at(A, c0, s.e); gx.ldb = s.F; gx.b_kcontig = true;
+    gx.C[0] = dX_part; gx.ldc = s.h;
+    if (gemm(s, gx, st, TP_STEP_MLP_DX) != hipSuccess) return TP_EHIP;
+    if (aux && db1 && aux->to_main(st, 1) != hipSuccess) return TP_EHIP;
+    return TP_OK;
+}
+
 }  // namespace
 
 namespace tp {
@@ -338,6 +404,7 @@ const char* tp_status_string(int status) {
         case TP_EUNSUPPORTED: return "unsupported shape (head dimension or size limit)";
         case TP_EHIP: return "HIP kernel launch failed";
         case TP_ESIZE: return "work buffer smaller than required";
+        case TP_ESCRATCH: return "problem needs more scratch than the no-allocation entry point's static buffer";
         default: return "unknown status";
     }
 }
@@ -419,60 +486,30 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     Shape s;
     int rc = derive(dims, shard, degree, &s);
     if (rc) return rc;
-    if (!X || !A || !B || !saved || !dZ || !dX_part || !dA || !dB || !work) return TP_EINVAL;
-    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(saved) || !aligned16(dZ) ||
-        !aligned16(dX_part) || !aligned16(dA) || !aligned16(dB) || !aligned16(work) || (db1 && !aligned16(db1)))
-        return TP_EALIGN;
+    if (!work) return TP_EINVAL;
+    if ((rc = mlp_bwd_check(X, A, B, saved, dZ, dX_part, dA, db1, dB))) return rc;
+    if (!aligned16(work)) return TP_EALIGN;
     const MlpWork W = mlp_work(s);
     if (work_bytes < (size_t)W.total) return TP_ESIZE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const MlpSaved L = mlp_saved(s);
-    const void* U = at(saved, L.U, 1);
-    const void* Y = at(saved, L.Y, 1);
-    void* dU = at(work, W.dU, 1);
-    float* cs = static_cast<float*>(at(work, W.cs, 1));
-    const int64_t c0 = s.i * s.Fs;
-
     AuxScope aux;
     if (aux.err != hipSuccess) return TP_EHIP;
+    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, at(work, W.dU, 1),
+                       static_cast<float*>(at(work, W.cs, 1)), static_cast<hipStream_t>(stream), &aux);
+}
 
-    tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * GeLU'(U)
-    g.M = (int)s.T; g.N = (int)s.Fs; g.K = (int)s.h;
-    g.A = dZ; g.lda = s.h; g.a_kcontig = true;
-    g.B[0] = at(B, c0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
-    g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
-    g.epi = tp::EPI_GELU_BWD;
-    g.gelu_tanh = s.gelu_tanh;
-    if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;
-
-    if (db1) {  // db1[C_i] = column sums of dU, on the auxiliary stream beside the GEMMs below
-        float* outs[3] = {db1 + c0, nullptr, nullptr};
-        if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
-        StepTimer t(TP_STEP_MLP_DB1, aux.a->st);
-        if (tp::colsum(fmt(s), dU, s.T, s.Fs, s.Fs, outs, SEG_NONE, cs, aux.a->st) != hipSuccess) return TP_EHIP;
-    }
-
-    tp::GemmDesc gw[2];  // one launch: dB[C_i, :] = Y^T dZ and dA[:, C_i] = X^T dU
-    tp::GemmDesc& gb = gw[0];
-    gb.M = (int)s.Fs; gb.N = (int)s.h; gb.K = (int)s.T;
-    gb.A = Y; gb.lda = s.Fs; gb.a_kcontig = false;
-    gb.B[0] = dZ; gb.ldb = s.h; gb.b_kcontig = false;
-    gb.C[0] = dB + c0 * s.h; gb.ldc = s.h; gb.out_f32 = true;
-    tp::GemmDesc& ga = gw[1];
-    ga.M = (int)s.h; ga.N = (int)s.Fs; ga.K = (int)s.T;
-    ga.A = X; ga.lda = s.h; ga.a_kcontig = false;
-    ga.B[0] = dU; ga.ldb = s.Fs; ga.b_kcontig = false;
-    ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
-    if (gemm2(s, gw, st, TP_STEP_MLP_DW) != hipSuccess) return TP_EHIP;
-
-    tp::GemmDesc gx;  // dX_part = dU A[:, C_i]^T
-    gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)s.Fs;
-    gx.A = dU; gx.lda = s.Fs; gx.a_kcontig = true;
-    gx.B[0] = at(A, c0, s.e); gx.ldb = s.F; gx.b_kcontig = true;
-    gx.C[0] = dX_part; gx.ldc = s.h;
-    if (gemm(s, gx, st, TP_STEP_MLP_DX) != hipSuccess) return TP_EHIP;
-    if (db1 && aux.to_main(st, 1) != hipSuccess) return TP_EHIP;
-    return TP_OK;
+int tp_mlp_shard_bwd_noalloc(const tp_dims* dims, int shard, int degree, const void* X, const void* A,
+                             const void* B, const void* saved, const void* dZ, void* dX_part, float* dA, float* db1,
+                             float* dB, void* stream) {
+    Shape s;
+    int rc = derive(dims, shard, degree, &s);
+    if (rc) return rc;
+    if ((rc = mlp_bwd_check(X, A, B, saved, dZ, dX_part, dA, db1, dB))) return rc;
+    const MlpWork W = mlp_work(s);
+    if (W.total > tp::NOALLOC_SCRATCH_BYTES) return TP_ESCRATCH;
+    void* scratch = nullptr;  // the device address of this device's static array
+    if (tp::noalloc_scratch(&scratch) != hipSuccess) return TP_EHIP;
+    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, at(scratch, W.dU, 1),
+                       static_cast<float*>(at(scratch, W.cs, 1)), static_cast<hipStream_t>(stream), nullptr);
 }
 
 int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq, const void* Wk,

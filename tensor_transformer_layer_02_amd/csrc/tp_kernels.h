@@ -114,6 +114,11 @@ hipError_t colsum(int fmt, const void* X, int64_t rows, int64_t cols, int64_t ld
 hipError_t sum_partials(int fmt, int64_t rows, int64_t cols, const void* const* parts,
                         int nparts, const void* bias, float* out, hipStream_t s);
 
+// ---- static scratch of the no-allocation FFN backward (noalloc.hip) ----
+constexpr int64_t NOALLOC_SCRATCH_BYTES = (int64_t)64 << 20;
+// Device address of the current device's scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // ---- pre-LN residual stream (layernorm.hip) ----
 constexpr int LN_MAXP = 16;  // partials per call
 // h = residual + bias + sum_k parts[k] -> out (fp32, if non-null); then, if y is

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libtpshard.so")
 TP_FP32, TP_BF16, TP_FP16 = 0, 1, 2
 TP_GELU_ERF, TP_GELU_TANH = 0, 1
 STATUS = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_EDIVIDE", 3: "TP_ESHARD", 4: "TP_EALIGN", 5: "TP_EDTYPE",
-          6: "TP_EUNSUPPORTED", 7: "TP_EHIP", 8: "TP_ESIZE"}
+          6: "TP_EUNSUPPORTED", 7: "TP_EHIP", 8: "TP_ESIZE", 9: "TP_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TP_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_bytes", "tp_attn_saved_bytes",
            "tp_mlp_work_bytes", "tp_attn_work_bytes", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
@@ -26,7 +27,7 @@ EXPORTS = ["tp_version", "tp_status_string", "tp_check_dims", "tp_mlp_saved_byte
            "tp_profile_count", "tp_profile_kernels", "tp_residual_layernorm", "tp_layernorm_bwd_work_bytes",
            "tp_layernorm_bwd", "tp_mlp_recompute_work_bytes", "tp_attn_recompute_work_bytes",
            "tp_mlp_shard_bwd_recompute", "tp_attn_shard_bwd_recompute", "tp_test_force_gemm_tile",
-           "tp_test_gemm_tile_count"]
+           "tp_test_gemm_tile_count", "tp_mlp_shard_bwd_noalloc"]
 
 # step ids of the measurement hook (TP_STEP_* in tpshard.h), in launch order
 STEPS = ["MLP_UP", "MLP_DOWN", "QKV", "ATTN_CORE", "ATTN_OUT", "MLP_DU", "MLP_DW", "MLP_DB1", "MLP_DX",
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).argtypes = [D, i32, i32]
         L.tp_mlp_shard_fwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.tp_mlp_shard_bwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+        L.tp_mlp_shard_bwd_noalloc.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, fp, fp, fp, vp]
         L.tp_attn_shard_fwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.tp_attn_shard_bwd.argtypes = [D, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp,
                                         vp, sz, vp]
@@ -161,6 +163,11 @@ def tp_mlp_shard_bwd(dims, shard, degree, X, A, B, saved, dZ, dX_part, dA, db1, 
     nbytes = work.numel() * work.element_size() if hasattr(work, "numel") else 0
     return _call("tp_mlp_shard_bwd", ctypes.byref(dims), shard, degree, _ptr(X), _ptr(A), _ptr(B), _ptr(saved),
                  _ptr(dZ), _ptr(dX_part), _ptr(dA), _ptr(db1), _ptr(dB), _ptr(work), nbytes, _stream(stream))
+
+
+def tp_mlp_shard_bwd_noalloc(dims, shard, degree, X, A, B, saved, dZ, dX_part, dA, db1, dB, stream=None):
+    return _call("tp_mlp_shard_bwd_noalloc", ctypes.byref(dims), shard, degree, _ptr(X), _ptr(A), _ptr(B),
+                 _ptr(saved), _ptr(dZ), _ptr(dX_part), _ptr(dA), _ptr(db1), _ptr(dB), _stream(stream))
 
 
 def tp_attn_shard_fwd(dims, shard, degree, X, Wq, Wk, Wv, bq, bk, bv, Wo, Z_part, saved, stream=None):

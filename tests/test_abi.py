@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for code in range(9):
+    for code in range(10):
         assert tp.tp_status_string(code)
     assert tp.tp_status_string(99) == "unknown status"
 
@@ -167,3 +167,27 @@ def test_force_tile_hook_rejects_bad_arguments(L):
             tp.tp_test_force_gemm_tile(*bad)
         assert e.value.code == 1
     assert tp.tp_test_force_gemm_tile(-1, 0) == 0
+
+
+def test_noalloc_backward_refuses_work_beyond_its_scratch(L):
+    """tp_mlp_shard_bwd_noalloc keeps its scratch in a fixed static device array; a shard whose
+    backward needs more (the 30B t = 4 shard: dU alone is 8192 x 7168 x 2 bytes) is refused with
+    TP_ESCRATCH before any HIP call, and its argument checks come first."""
+    from tensor_transformer_layer_02_amd.configs import CONFIGS
+    P = _fake()
+    big = tp.dims_of(CONFIGS["g30b_t4"])
+    assert tp.tp_mlp_work_bytes(big, 0, 4) > tp.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_bwd_noalloc(big, 0, 4, P, P, P, P, P, P, P, P, P, stream=0)
+    assert e.value.code == 9
+    fits = tp.dims_of(CONFIGS["gpt8b"])
+    assert tp.tp_mlp_work_bytes(fits, 0, 8) <= tp.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(tp.TpError) as e:   # NULL X
+        tp.tp_mlp_shard_bwd_noalloc(fits, 0, 8, None, P, P, P, P, P, P, P, P, stream=0)
+    assert e.value.code == 1
+    with pytest.raises(tp.TpError) as e:   # misaligned dB
+        tp.tp_mlp_shard_bwd_noalloc(fits, 0, 8, P, P, P, P, P, P, P, P, P + 4, stream=0)
+    assert e.value.code == 4
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard_bwd_noalloc(fits, 9, 8, P, P, P, P, P, P, P, P, P, stream=0)
+    assert e.value.code == 3
