@@ -222,6 +222,20 @@ __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x1
         }
 }
 
+// Workgroup -> (block pair x, sequence-head index bh) for a grid of (pairs,
+// sequences x heads).  The hardware deals workgroups round-robin over the 8 XCDs
+// by linear id; this numbering gives each XCD a contiguous range of (bh, x), so the
+// pair workgroups of one (sequence, head) run on one XCD and share its L2 for that
+// head's Q, K, V and dO (dealt over all XCDs, every L2 would hold every head).
+__device__ __forceinline__ void xcd_map(int& x, int& bh) {
+    const int nx = (int)gridDim.x, n = (int)(gridDim.x * gridDim.y);
+    const int L = (int)(blockIdx.x + blockIdx.y * gridDim.x);
+    const int per = (n + 7) / 8, r = n % 8, xc = L % 8, q = L / 8;
+    const int id = (r == 0 || xc < r) ? xc * per + q : r * per + (xc - r) * (per - 1) + q;
+    x = id % nx;
+    bh = id / nx;
+}
+
 // Rows of a forward / dQ workgroup: the 64-row blocks x and nb-1-x of the
 // sequence (nb blocks of 64 rows), so that under the causal mask a short and a
 // long row range share every workgroup and all workgroups carry about the same
@@ -329,9 +343,11 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const PairRows pr((int)blockIdx.x, s, wave, a.causal);
+    int xb, bh;
+    xcd_map(xb, bh);
+    const PairRows pr(xb, s, wave, a.causal);
     const int qg = pr.qg, kp = pr.kp, qw0 = pr.qw0;
-    const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
+    const int b = bh / a.heads, g = bh % a.heads;
     const int qw = qw0 + (lane & 31);  // this lane's query
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
@@ -585,11 +601,13 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const int nb = (s + BKV - 1) / BKV, x = (int)blockIdx.x, xl = nb - 1 - x;
+    int x, bh;
+    xcd_map(x, bh);
+    const int nb = (s + BKV - 1) / BKV, xl = nb - 1 - x;
     const bool side = NOMASK && xl != x;  // both key blocks over one query stream
     const int kg2 = wave & 1, qq = side ? 2 * (wave >> 2) : wave >> 1;
     const int jb = qq >> 1, half = side ? wave >> 2 : qq & 1;
-    const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
+    const int b = bh / a.heads, g = bh % a.heads;
 
     const bf16_t* Qg = a.qkv + (int64_t)b * s * a.ld_qkv + g * D;
     const bf16_t* Kg = Qg + a.w;
@@ -767,8 +785,10 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = a.seq;
-    const int nb = (s + BKV - 1) / BKV, x = (int)blockIdx.x, xl = nb - 1 - x;
-    const int b = blockIdx.y / a.heads, g = blockIdx.y % a.heads;
+    int x, bh;
+    xcd_map(x, bh);
+    const int nb = (s + BKV - 1) / BKV, xl = nb - 1 - x;
+    const int b = bh / a.heads, g = bh % a.heads;
     const PairRows pr(x, s, wave, a.causal);  // the side-by-side layout (no mask)
     const int rg = wave & 1, kq = wave >> 1;  // the one-after-the-other layout (causal)
 
