@@ -341,7 +341,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     constexpr int SMEM = 2 * SLOT > NMERGE * 4 * 64 * 4 ? 2 * SLOT : NMERGE * 4 * 64 * 4;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: derived conditions are scalar branches
     const int s = a.seq;
     int xb, bh;
     xcd_map(xb, bh);
@@ -542,21 +543,25 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
         fo = no;
     }
     // rows = queries qh0 + res_row(r), column = this lane's key
-    const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;
+    const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;  // wave-uniform
+    f32x4 Dd[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
         const int ql = 32 * half + 8 * r4 + 4 * (lane >> 5);
         const f32x4 L = *reinterpret_cast<const f32x4*>(lse2 + ql);
-        const f32x4 Dd = *reinterpret_cast<const f32x4*>(Dl + ql);
+        Dd[r4] = *reinterpret_cast<const f32x4*>(Dl + ql);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e, q = q0 + ql + e;
-            float pv = ex2(fmaf(sacc[r], a.scale_log2, -L[e]));
-            if (edge && !(q < s && kw < s && (!a.causal || kw <= q))) pv = 0.f;
-            sacc[r] = pv;
-            pacc[r] = pv * (pacc[r] - Dd[e]);
+        for (int e = 0; e < 4; ++e) sacc[4 * r4 + e] = ex2(fmaf(sacc[4 * r4 + e], a.scale_log2, -L[e]));
+    }
+    if (edge) {  // blocks that cross the diagonal or an end of the sequence only
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 32 * half + res_row(r, lane);
+            if (!(q < s && kw < s && (!a.causal || kw <= q))) sacc[r] = 0.f;
         }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - Dd[r / 4][r % 4]);
     u32x4 to = fa.frag_tr(dOt, rb, 0, 2 * half), tq = fa.frag_tr(Qt, rb, 0, 2 * half);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -599,7 +604,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     constexpr int SMEM = 2 * SLOT > MERGE ? 2 * SLOT : MERGE;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: derived conditions are scalar branches
     const int s = a.seq;
     int x, bh;
     xcd_map(x, bh);
@@ -749,14 +755,18 @@ __device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    const bool edge = (a.causal && k0 + 31 > qw0) || k0 + 32 > s || qw0 + 32 > s;
+    const bool edge = (a.causal && k0 + 31 > qw0) || k0 + 32 > s || qw0 + 32 > s;  // wave-uniform
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = k0 + res_row(r, lane);
-        float pv = ex2(fmaf(sacc[r], a.scale_log2, -lse2));
-        if (edge && !(qw < s && key < s && (!a.causal || key <= qw))) pv = 0.f;
-        pacc[r] = pv * (pacc[r] - Dv);
+    for (int r = 0; r < 16; ++r) sacc[r] = ex2(fmaf(sacc[r], a.scale_log2, -lse2));
+    if (edge) {  // blocks that cross the diagonal or an end of the sequence only
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + res_row(r, lane);
+            if (!(qw < s && key < s && (!a.causal || key <= qw))) sacc[r] = 0.f;
+        }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - Dv);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
         const u32x4 sf = pack_chunk<ST>(pacc, kc);
@@ -783,7 +793,8 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     constexpr int SMEM = 2 * SLOT > DB * 16 * 4 * 64 * 4 ? 2 * SLOT : DB * 16 * 4 * 64 * 4;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: derived conditions are scalar branches
     const int s = a.seq;
     int x, bh;
     xcd_map(x, bh);
