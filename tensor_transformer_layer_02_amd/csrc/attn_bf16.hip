@@ -670,9 +670,9 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
                 const int row1 = (qs + 2 * (it + 1)) * BKV;
                 gq.load(Qg, a.ld_qkv, row1, s, nxt, wave);
                 go.load(dOg, a.ld_o, row1, s, nxt + 2 * TILE, wave);
-                if (tid < 2 * BKV) {
+                if (tid < 2 * BKV) {  // raw values: scaling them here would wait for every load in flight
                     const int q = row1 + tid;
-                    lsev = q < s ? lseg[q] * LOG2E : 0.f;
+                    lsev = q < s ? lseg[q] : 0.f;
                     dval = q < s ? Dg[q] : 0.f;
                 }
             }
@@ -689,7 +689,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
                     dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
             }
             if (more && tid < 2 * BKV) {
-                reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev;
+                reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev * LOG2E;
                 reinterpret_cast<float*>(nxt + 4 * TILE + 2 * BKV * 4)[tid] = dval;
             }
             __builtin_amdgcn_s_waitcnt(0);
