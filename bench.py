@@ -66,8 +66,8 @@ def step_costs(cfg):
         "MLP_DX": (g(T, h, Fs), (T * Fs + h * Fs + T * h) * e),
         "ATTN_DO": (g(T, w, h), (T * h + w * h + T * w) * e),
         "ATTN_CORE_BWD": (4 * 2 * d * pairs, 9 * T * w * e),
-        "ATTN_DW": (g(h, 3 * w, T), (T * h + 3 * T * w) * e + 3 * h * w * 4),
-        "ATTN_DWO": (g(w, h, T), (T * w + T * h) * e + w * h * 4),
+        # dW{q,k,v} and dWo share one launch
+        "ATTN_DW": (g(h, 3 * w, T) + g(w, h, T), (T * h + 3 * T * w + T * w + T * h) * e + 4 * h * w * 4),
         "ATTN_DBIAS": (0, 3 * T * w * e + 3 * w * 4),
         "ATTN_DX": (g(T, h, 3 * w), (3 * T * w + 3 * w * h + T * h) * e),
     }

@@ -236,10 +236,10 @@ enum {
     TP_STEP_MLP_DX = 8,      /* dX_part = dU A_i^T                                          */
     TP_STEP_ATTN_DO = 9,     /* dO = dZ Wo_i^T                                              */
     TP_STEP_ATTN_CORE_BWD = 10, /* softmax attention backward -> dQ, dK, dV                 */
-    TP_STEP_ATTN_DW = 11,    /* dW{q,k,v}_i = X^T d{Q,K,V}                                  */
+    TP_STEP_ATTN_DW = 11,    /* dW{q,k,v}_i = X^T d{Q,K,V} and dWo_i = O^T dZ (one launch)  */
     TP_STEP_ATTN_DBIAS = 12, /* db{q,k,v}_i = column sums                                   */
     TP_STEP_ATTN_DX = 13,    /* dX_part = d{Q,K,V} W{q,k,v}_i^T                             */
-    TP_STEP_ATTN_DWO = 14,   /* dWo_i = O^T dZ                                              */
+    TP_STEP_ATTN_DWO = 14,   /* (not recorded: dWo_i is part of the TP_STEP_ATTN_DW launch) */
     TP_NUM_STEPS = 15
 };
 

@@ -9,10 +9,10 @@
 //   tp_attn_shard_fwd: [X*[Wq|Wk|Wv]_i + b -> QKV]  [fused attention -> O, LSE]
 //                      [O*Wo_i -> Z_part]
 //   tp_attn_shard_bwd: [dZ*Wo_i^T -> dO]  [fused attention bwd -> dQKV]
-//                      [X^T dQKV -> dW{q,k,v}_i]  [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]
-//                      and, on the auxiliary stream: [O^T dZ -> dWo_i] (from the
-//                      start), [colsum -> db{q,k,v}_i] and the dX_part GEMM (after
-//                      the attention bwd, beside the dW{q,k,v} GEMM)
+//                      [X^T dQKV -> dW{q,k,v}_i, O^T dZ -> dWo_i] (one launch)
+//                      [dQKV*[Wq|Wk|Wv]_i^T -> dX_part]; the last, and
+//                      [colsum -> db{q,k,v}_i] before it, on the auxiliary stream
+//                      beside the weight-gradient launch
 // The MLP backward's column sum also runs on the auxiliary stream.
 // The shard slices follow page "Megatron-LM: what the tensor parallelism paper
 // actually says": FFN columns/rows C_i ("How transformer layers actually
@@ -567,13 +567,11 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     AuxScope aux;
     if (aux.err != hipSuccess) return TP_EHIP;
 
-    tp::GemmDesc go;  // dWo[rows of G_i, :] = O^T dZ: needs only forward outputs, so it runs on
-    go.M = (int)s.w; go.N = (int)s.h; go.K = (int)s.T;  // the auxiliary stream beside dO and the core
+    tp::GemmDesc go;  // dWo[rows of G_i, :] = O^T dZ: shares one launch with dW{q,k,v} (below)
+    go.M = (int)s.w; go.N = (int)s.h; go.K = (int)s.T;
     go.A = O; go.lda = s.w; go.a_kcontig = false;
     go.B[0] = dZ; go.ldb = s.h; go.b_kcontig = false;
     go.C[0] = dWo + col0 * s.h; go.ldc = s.h; go.out_f32 = true;
-    if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
-    if (gemm_w(s, go, aux.a->st, TP_STEP_ATTN_DWO) != hipSuccess) return TP_EHIP;
 
     tp::GemmDesc g;  // dO = dZ Wo[rows of G_i, :]^T
     g.M = (int)s.T; g.N = (int)s.w; g.K = (int)s.h;
@@ -602,7 +600,7 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     // On the auxiliary stream: db{q,k,v}[cols of G_i] = column sums of dQKV, then
     // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T, beside the weight-gradient GEMM
     // (whose tiles leave CUs idle).
-    if (aux.to_aux(st, 1) != hipSuccess) return TP_EHIP;
+    if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
     if (bias_grads) {
         float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
         StepTimer t(TP_STEP_ATTN_DBIAS, aux.a->st);
@@ -616,18 +614,22 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     for (int z = 0; z < 3; ++z) gx.B[z] = at(W3[z], col0, s.e);
     gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
     gx.C[0] = dX_part; gx.ldc = s.h;
-    gx.concurrent = true;
     if (gemm(s, gx, aux.a->st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
 
-    tp::GemmDesc gq;  // dW{q,k,v}[:, cols of G_i] = X^T dQKV
+    // One launch: dW{q,k,v}[:, cols of G_i] = X^T dQKV and dWo (same layout: transposed
+    // operands, fp32 output, K = T).  dWo needs only forward outputs, but running it beside the
+    // attention core took CUs from the core's one-workgroup-per-CU grid and slowed both.
+    tp::GemmDesc gw[2];
+    tp::GemmDesc& gq = gw[0];
     gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
     gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
     gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
     float* dW3[3] = {dWq, dWk, dWv};
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
-    if (gemm_w(s, gq, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
-    return aux.to_main(st, 2) != hipSuccess ? TP_EHIP : TP_OK;
+    gw[1] = go;
+    if (gemm2(s, gw, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
+    return aux.to_main(st, 1) != hipSuccess ? TP_EHIP : TP_OK;
 }
 
 int tp_sum_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int nparts, const void* bias,

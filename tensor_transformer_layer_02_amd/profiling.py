@@ -36,7 +36,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 STEP_ORDER = [
     ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gemm"]), ("ATTN_CORE", ["attn_fwd"]),
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
-    ("MLP_DW", ["zero*", "gemm"]), ("MLP_DX", ["gemm"]), ("ATTN_DWO", ["zero*", "gemm"]), ("ATTN_DO", ["gemm"]),
+    ("MLP_DW", ["zero*", "gemm"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
     ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
     ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["zero*", "gemm"]),
 ]
