@@ -142,6 +142,36 @@ struct TileDMA {
     }
 };
 
+// Direct global -> LDS loads of NTL (2 or 4) [64][D] tiles laid one after the
+// other at dst (the swizzled image toff() gives).  Tile t holds 64 rows of a
+// row-major source starting at row (t & (NTL/2) ? r1 : r0); with NTL = 4 odd
+// tiles come from B (row stride ldb), even ones from A (stride lda); with NTL = 2
+// both from A.  The tiles' 1 KB pieces are dealt over the 8 waves (piece q to
+// wave q % 8), so every wave issues the same number of loads.  Rows at or past
+// the sequence end read as zeros.
+template <int D, int NTL>
+__device__ __forceinline__ void load_tiles(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int r0,
+                                           int r1, int s, char* dst, int wave, int lane) {
+    constexpr int PPT = BKV * D * 2 / 1024;  // pieces per tile
+    static_assert(NTL == 2 || NTL == 4, "two or four tiles");
+    static_assert((NTL * PPT) % 8 == 0, "the tiles must split into 1 KB pieces over 8 waves");
+#pragma unroll
+    for (int i = 0; i < NTL * PPT / 8; ++i) {
+        const int q = wave + 8 * i;  // wave-uniform
+        const int t = q / PPT;
+        const bool fromb = NTL == 4 && (t & 1);
+        const bf16_t* sp = fromb ? B : A;
+        const int64_t sl = fromb ? ldb : lda;
+        const int rs0 = (t & (NTL / 2)) ? r1 : r0;
+        const int off = (q % PPT) * 1024 + 16 * lane;
+        const int r = off / (2 * D), pc = (off % (2 * D)) / 16;
+        const int rem = s - rs0;
+        const uint32_t bytes = rem > 0 ? (uint32_t)((rem - 1) * sl * 2 + D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sp + (int64_t)(rem > 0 ? rs0 : 0) * sl, bytes);
+        load16_lds(rs, dst + q * 1024, r < rem ? (uint32_t)(r * sl * 2 + ((pc ^ swz<D>(r)) << 4)) : OOB);
+    }
+}
+
 // Per-lane LDS byte offsets of the fragment reads of a [rows][D] tile.  The
 // chunk swizzle depends only on the row modulo 16, so a row base that is a
 // multiple of 16 (and the tile base) is a uniform addend.
@@ -336,9 +366,14 @@ __device__ __forceinline__ void fwd_pair(const AttnArgs& a, const FragAddr<D>& f
 template <int D, typename ST>
 __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;  // one [128][D] pair tile
+    constexpr int TILE = BKV * D * 2;                              // one [64][D] tile
     constexpr int SLOT = 2 * PT;                                   // K pair, V pair
     constexpr int NMERGE = DB * 16 + 2;                            // m, l, O^T per lane
-    constexpr int SMEM = 2 * SLOT > NMERGE * 4 * 64 * 4 ? 2 * SLOT : NMERGE * 4 * 64 * 4;
+    // The Q tiles of both query blocks come into LDS once (each is read by the two
+    // waves that share those queries) beside the two stages.
+    constexpr int REG = 2 * SLOT + 2 * TILE;
+    static_assert(REG <= 160 * 1024, "stages and Q tiles fit the LDS");
+    constexpr int SMEM = REG > NMERGE * 4 * 64 * 4 ? REG : NMERGE * 4 * 64 * 4;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -355,15 +390,13 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     const bf16_t* Kg = Qg + a.w;
     const bf16_t* Vg = Qg + 2 * a.w;
 
-    u32x4 qf[KC];  // Q^T operand: column = query, k = d
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-        qf[c] = (qw < s) ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
-
     FragAddr<D> fa;
     fa.init(lane);
     TileDMA<D, 2 * BKV> gkv;  // K and V pair rows (both stride ld_qkv) straight into LDS
     gkv.init(a.ld_qkv, wave, lane);
+    const int xq = xb, xlq = (s + BKV - 1) / BKV - 1 - xb;  // the workgroup's two query blocks
+    char* const qt = smem + 2 * SLOT;                       // their Q tiles
+    load_tiles<D, 2>(Qg, a.ld_qkv, Qg, a.ld_qkv, xq * BKV, xlq * BKV, s, qt, wave, lane);
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -376,6 +409,14 @@ __global__ void __launch_bounds__(NT8, 1) attn_fwd_kernel(const AttnArgs a) {
     gkv.load(Vg, a.ld_qkv, 0, s, smem + PT, wave);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into LDS are done
     __syncthreads();
+    u32x4 qf[KC];  // Q^T operand: column = query, k = d (rows past the sequence end are zeros)
+    {
+        const int blk = qg < 2 ? xq : xlq;
+        const char* Qt = qt + (qg < 2 ? 0 : TILE);
+        const int rb = (qw0 - blk * BKV) & 32;  // 0 or 32 (anything when the wave has no queries)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qf[c] = fa.frag_rows(Qt, rb, c);
+    }
 
     for (int it = 0; it < npair; ++it) {
         char* const cur = smem + (it & 1) * SLOT;
@@ -601,7 +642,15 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
     constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
     constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for four groups
-    constexpr int SMEM = 2 * SLOT > MERGE ? 2 * SLOT : MERGE;
+    // PRE: the K and V tiles of both key blocks come into LDS once, at the start
+    // (the fragments of a key group are then read from LDS by each of the four
+    // waves that use them, instead of four times from memory), where they fit
+    // beside the two stages (up to d = 96).
+    constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
+    constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
+    constexpr int SMEM = REG > MERGE ? REG : MERGE;
+    constexpr int PITCH = D * 2 + 16;  // row pitch of the bf16 dK / dV image (rows 4 apart on other banks)
+    static_assert(2 * BKV * PITCH <= SLOT && MERGE <= SLOT, "epilogue areas fit one stage");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -629,45 +678,68 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
     go.init(a.ld_o, wave, lane);
     char* const st0 = smem;
     char* const st1 = smem + SLOT;
+    char* const kvt = smem + 2 * SLOT;  // PRE: [K | V] of key block x, then of key block nb-1-x
+    if constexpr (PRE) load_tiles<D, 4>(Kg, a.ld_qkv, Vg, a.ld_qkv, x * BKV, xl * BKV, s, kvt, wave, lane);
 
     const int nphase = (xl != x && !side) ? 2 : 1;
+    int sbase = 0;        // slot of the phase's first stage
+    bool staged = false;  // that stage is already in LDS (loaded during the previous phase)
     for (int ph = 0; ph < nphase; ++ph) {
         const int kb = side ? ((wave & 2) ? xl : x) : (ph == 0 ? x : xl);
         const int kw0 = min(s, kb * BKV + 32 * kg2);  // first key of this wave's group (s: none)
         const int kw = kw0 + (lane & 31);              // this lane's key
-        u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const bool ok = kw < s;
-            const int64_t o = (int64_t)kw * a.ld_qkv + 16 * c + 8 * (lane >> 5);
-            kf[c] = ok ? ld16(Kg + o) : u32x4{0u, 0u, 0u, 0u};
-            vf[c] = ok ? ld16(Vg + o) : u32x4{0u, 0u, 0u, 0u};
-        }
-        f32x16 dk[DB], dv[DB];
-#pragma unroll
-        for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
-
         const int qs = a.causal ? kb : 0;     // the first query block that sees the key block
         const int npair = (nb - qs + 1) / 2;  // streamed pairs of query blocks
-        float lsev = 0.f, dval = 0.f;         // threads < 128: one query's log2-scaled LSE and D
-        if (npair > 0) {
+        float lsev = 0.f, dval = 0.f;         // threads < 128: one query's LSE and D
+        if (!staged && npair > 0) {
             const int row0 = qs * BKV;
             gq.load(Qg, a.ld_qkv, row0, s, st0, wave);
             go.load(dOg, a.ld_o, row0, s, st0 + 2 * TILE, wave);
             if (tid < 2 * BKV) {
                 const int q = row0 + tid;
-                reinterpret_cast<float*>(st0 + 4 * TILE)[tid] = q < s ? lseg[q] * LOG2E : 0.f;
-                reinterpret_cast<float*>(st0 + 4 * TILE + 2 * BKV * 4)[tid] = q < s ? Dg[q] : 0.f;
+                lsev = q < s ? lseg[q] : 0.f;
+                dval = q < s ? Dg[q] : 0.f;
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads and LDS stores are done
-        __syncthreads();
+        u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
+        if constexpr (!PRE) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bool ok = kw < s;
+                const int64_t o = (int64_t)kw * a.ld_qkv + 16 * c + 8 * (lane >> 5);
+                kf[c] = ok ? ld16(Kg + o) : u32x4{0u, 0u, 0u, 0u};
+                vf[c] = ok ? ld16(Vg + o) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (!staged) {
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's loads are done
+            if (npair > 0 && tid < 2 * BKV) {
+                reinterpret_cast<float*>(st0 + 4 * TILE)[tid] = lsev * LOG2E;
+                reinterpret_cast<float*>(st0 + 4 * TILE + 2 * BKV * 4)[tid] = dval;
+            }
+            __syncthreads();
+        }
+        if constexpr (PRE) {  // rows past the sequence end are zeros in the tiles
+            const char* Kt = kvt + (kb == x ? 0 : 2 * TILE);
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                kf[c] = fa.frag_rows(Kt, 32 * kg2, c);
+                vf[c] = fa.frag_rows(Kt + TILE, 32 * kg2, c);
+            }
+        }
+        f32x16 dk[DB], dv[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) dk[i] = dv[i] = zero16();
+
+        const int qs_next = a.causal ? xl : 0;  // the next phase's first query block
         for (int it = 0; it < npair; ++it) {
-            char* const cur = (it & 1) ? st1 : st0;
-            char* const nxt = (it & 1) ? st0 : st1;
+            const int slot = (it + sbase) & 1;
+            char* const cur = slot ? st1 : st0;
+            char* const nxt = slot ? st0 : st1;
             const bool more = it + 1 < npair;
-            if (more) {  // the other stage was last read in iteration it-1, before its closing barrier
-                const int row1 = (qs + 2 * (it + 1)) * BKV;
+            const bool pre1 = PRE && !more && ph + 1 < nphase;  // the next phase's first stage
+            if (more || pre1) {  // the other stage was last read in iteration it-1, before its closing barrier
+                const int row1 = more ? (qs + 2 * (it + 1)) * BKV : qs_next * BKV;
                 gq.load(Qg, a.ld_qkv, row1, s, nxt, wave);
                 go.load(dOg, a.ld_o, row1, s, nxt + 2 * TILE, wave);
                 if (tid < 2 * BKV) {  // raw values: scaling them here would wait for every load in flight
@@ -688,15 +760,21 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
                 if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0))
                     dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
             }
-            if (more && tid < 2 * BKV) {
+            if ((more || pre1) && tid < 2 * BKV) {
                 reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev * LOG2E;
                 reinterpret_cast<float*>(nxt + 4 * TILE + 2 * BKV * 4)[tid] = dval;
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
+        // the next phase's first stage (if loaded) sits in slot (npair + sbase) & 1; the
+        // merges and the output image use the other slot
+        const int nslot = (npair + sbase) & 1;
+        staged = PRE && ph + 1 < nphase && npair > 0;
+        sbase = staged ? nslot : 0;
+        char* const ep = (staged && nslot == 0) ? st1 : st0;
 
-        float* mg = reinterpret_cast<float*>(smem);
+        float* mg = reinterpret_cast<float*>(ep);
         if (NOMASK && side) {  // q0 + q1 per key group
             merge_halves<DB>(dk, mg, half, wave & 3, lane);
             merge_halves<DB>(dv, mg, half, wave & 3, lane);
@@ -709,22 +787,49 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a)
         }
 
         // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
-        if ((side ? half == 0 : qq == 0) && kw0 < s) {
-            bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
-            bf16_t* dVg = dKg + a.w;
+        bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
+        bf16_t* dVg = dKg + a.w;
+        if (!PRE || (NOMASK && side)) {  // each writer stores its values directly
+            if ((side ? half == 0 : qq == 0) && kw0 < s) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kw0 + res_row(r, lane);
-                if (key >= s) continue;
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kw0 + res_row(r, lane);
+                    if (key >= s) continue;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int c = 32 * db + (lane & 31);
-                    dKg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dk[db][r] * a.scale);
-                    dVg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dv[db][r]);
+                    for (int db = 0; db < DB; ++db) {
+                        const int c = 32 * db + (lane & 31);
+                        dKg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dk[db][r] * a.scale);
+                        dVg[(int64_t)key * a.ld_qkv + c] = Store16<ST>::from_f(dv[db][r]);
+                    }
+                }
+            }
+        } else {  // the two writers' values as a bf16 [64][D] image per tensor, then 16-byte row stores
+            if (qq == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * kg2 + res_row(r, lane);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int c = 32 * db + (lane & 31);
+                        *reinterpret_cast<uint16_t*>(ep + row * PITCH + c * 2) = Store16<ST>::from_f(dk[db][r] * a.scale);
+                        *reinterpret_cast<uint16_t*>(ep + (BKV + row) * PITCH + c * 2) = Store16<ST>::from_f(dv[db][r]);
+                    }
+                }
+            }
+            __syncthreads();
+            constexpr int CH = D / 8;  // 16-byte chunks per row
+#pragma unroll
+            for (int e0 = 0; e0 < 2 * BKV * CH; e0 += NT8) {
+                const int e = e0 + tid;
+                const int tsel = e / (BKV * CH), rr = (e / CH) % BKV, cc = e % CH;
+                const int key = kb * BKV + rr;
+                if (e < 2 * BKV * CH && key < s) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(ep + (tsel * BKV + rr) * PITCH + cc * 16);
+                    *reinterpret_cast<u32x4*>((tsel ? dVg : dKg) + (int64_t)key * a.ld_qkv + cc * 8) = v;
                 }
             }
         }
-        __syncthreads();  // the merge area is the stages of the next phase
+        __syncthreads();  // the epilogue slot is a stage of the next phase
     }
 }
 
@@ -775,6 +880,15 @@ __device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa
     }
 }
 
+// The query rows of phase ph of a dQ workgroup for one wave: its 64-query block
+// and its first query (s when the wave has none).  Causal (masked): block x,
+// then nb-1-x, 32 queries per row group rg; no mask: the forward's pair layout.
+__device__ __forceinline__ void dq_rows(bool masked, int ph, int x, int xl, int rg, const PairRows& pr, int s, int& blk,
+                                        int& qw0) {
+    blk = masked ? (ph == 0 ? x : xl) : (pr.qg < 2 ? x : xl);
+    qw0 = masked ? min(s, blk * BKV + 32 * rg) : pr.qw0;
+}
+
 // dQ for the 64-query blocks x and nb-1-x.  Causal (MASKED): one block after the
 // other, each with all 8 waves: wave = (32-query row group rg = wave & 1) x
 // (key part kq = wave >> 1: 32-key half kq % 2 of key block kq / 2 of each
@@ -788,9 +902,16 @@ __device__ __forceinline__ void dq_keys(const AttnArgs& a, const FragAddr<D>& fa
 // pair), halves added k0 + k1.  Deterministic either way.
 template <int D, typename ST, bool MASKED>
 __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2;
+    constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2, TILE = BKV * D * 2;
     constexpr int SLOT = 2 * PT;  // K pair, V pair
-    constexpr int SMEM = 2 * SLOT > DB * 16 * 4 * 64 * 4 ? 2 * SLOT : DB * 16 * 4 * 64 * 4;
+    constexpr int MERGE = DB * 16 * 4 * 64 * 4;
+    // PRE: the Q and dO tiles of both query blocks come into LDS once, at the start
+    // (each is read by the four waves that share those queries), where they fit
+    // beside the two stages (up to d = 96).
+    constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
+    constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
+    constexpr int SMEM = REG > MERGE ? REG : MERGE;
+    static_assert(MERGE <= SLOT, "the merge area fits one stage");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -813,39 +934,82 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     fa.init(lane);
     TileDMA<D, 2 * BKV> gkv;  // K and V pair rows (both stride ld_qkv) straight into LDS
     gkv.init(a.ld_qkv, wave, lane);
+    char* const st0 = smem;
+    char* const st1 = smem + SLOT;
+    char* const qdt = smem + 2 * SLOT;  // PRE: [Q | dO] of query block x, then of query block nb-1-x
+    if constexpr (PRE) load_tiles<D, 4>(Qg, a.ld_qkv, dOg, a.ld_o, x * BKV, xl * BKV, s, qdt, wave, lane);
 
     const int nphase = (MASKED && xl != x) ? 2 : 1;
-    for (int ph = 0; ph < nphase; ++ph) {
-        const int qb = ph == 0 ? x : xl;
-        const int qw0 = MASKED ? min(s, qb * BKV + 32 * rg) : pr.qw0;  // first query of the wave (s: none)
-        const int qw = qw0 + (lane & 31);                               // this lane's query
-        u32x4 qf[KC], of[KC];  // Q^T, dO^T operands: column = query, k = d
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const bool ok = qw < s;
-            qf[c] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
-            of[c] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+    int blk, qw0;
+    dq_rows(MASKED, 0, x, xl, rg, pr, s, blk, qw0);
+    float lse_raw = 0.f, d_raw = 0.f;  // this lane's query: LSE and D, loaded a phase ahead
+    {
+        const int qw = qw0 + (lane & 31);
+        if (qw < s) {
+            lse_raw = a.lse[hrow + qw];
+            d_raw = a.Dq[hrow + qw];
         }
-        const float lse2 = qw < s ? a.lse[hrow + qw] * LOG2E : 0.f;
-        const float Dv = qw < s ? a.Dq[hrow + qw] : 0.f;
+    }
+    int sbase = 0;        // slot of the phase's first stage
+    bool staged = false;  // that stage is already in LDS (loaded during the previous phase)
+    for (int ph = 0; ph < nphase; ++ph) {
+        const int qb = MASKED ? (ph == 0 ? x : xl) : x;
+        dq_rows(MASKED, ph, x, xl, rg, pr, s, blk, qw0);
+        const int qw = qw0 + (lane & 31);  // this lane's query
+        if (ph > 0 && !staged) {  // not loaded during the previous phase
+            lse_raw = qw < s ? a.lse[hrow + qw] : 0.f;
+            d_raw = qw < s ? a.Dq[hrow + qw] : 0.f;
+        }
+        const int nkb = MASKED ? (a.causal ? qb + 1 : nb) : pr.nkb;  // key blocks the phase streams
+        const int npair = (nkb + 1) / 2;
+        u32x4 qf[KC], of[KC];  // Q^T, dO^T operands: column = query, k = d
+        if constexpr (!PRE) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bool ok = qw < s;
+                qf[c] = ok ? ld16(Qg + (int64_t)qw * a.ld_qkv + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+                of[c] = ok ? ld16(dOg + (int64_t)qw * a.ld_o + 16 * c + 8 * (lane >> 5)) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (!staged) {
+            gkv.load(Kg, a.ld_qkv, 0, s, st0, wave);
+            gkv.load(Vg, a.ld_qkv, 0, s, st0 + PT, wave);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's loads are done
+            __syncthreads();
+        }
+        if constexpr (PRE) {  // rows past the sequence end are zeros in the tiles
+            const char* Qt = qdt + (blk == x ? 0 : 2 * TILE);
+            const int rb = qw0 - blk * BKV;  // 0 or 32 (anything when the wave has no queries)
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                qf[c] = fa.frag_rows(Qt, rb & 32, c);
+                of[c] = fa.frag_rows(Qt + TILE, rb & 32, c);
+            }
+        }
+        const float lse2 = lse_raw * LOG2E;
+        const float Dv = d_raw;
         f32x16 dq[DB];
 #pragma unroll
         for (int i = 0; i < DB; ++i) dq[i] = zero16();
 
-        const int nkb = MASKED ? (a.causal ? qb + 1 : nb) : pr.nkb;  // key blocks the phase streams
-        const int npair = (nkb + 1) / 2;
-        gkv.load(Kg, a.ld_qkv, 0, s, smem, wave);
-        gkv.load(Vg, a.ld_qkv, 0, s, smem + PT, wave);
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into LDS are done
-        __syncthreads();
-
         for (int it = 0; it < npair; ++it) {
-            char* const Kt = smem + (it & 1) * SLOT;
+            const int slot = (it + sbase) & 1;
+            char* const Kt = slot ? st1 : st0;
             char* const Vt = Kt + PT;
-            if (it + 1 < npair) {  // slot (it+1)&1 was last read in iteration it-1, before its closing barrier
-                char* const nxt = smem + ((it + 1) & 1) * SLOT;
-                gkv.load(Kg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt, wave);
-                gkv.load(Vg, a.ld_qkv, (it + 1) * 2 * BKV, s, nxt + PT, wave);
+            char* const nxt = slot ? st0 : st1;
+            const bool more = it + 1 < npair;
+            const bool pre1 = PRE && !more && ph + 1 < nphase;  // the next phase's first stage (keys 0 .. 127)
+            if (more || pre1) {  // slot nxt was last read in iteration it-1, before its closing barrier
+                const int row1 = more ? (it + 1) * 2 * BKV : 0;
+                gkv.load(Kg, a.ld_qkv, row1, s, nxt, wave);
+                gkv.load(Vg, a.ld_qkv, row1, s, nxt + PT, wave);
+            }
+            if (pre1) {  // the next phase's LSE and D of this lane's query
+                int nblk, nq0;
+                dq_rows(MASKED, ph + 1, x, xl, rg, pr, s, nblk, nq0);
+                const int nq = nq0 + (lane & 31);
+                lse_raw = nq < s ? a.lse[hrow + nq] : 0.f;
+                d_raw = nq < s ? a.Dq[hrow + nq] : 0.f;
             }
             if constexpr (MASKED) {  // 32 keys: half kq % 2 of block 2 it + kq / 2
                 const int kb = 2 * it + (kq >> 1), rb = BKV * (kq >> 1) + 32 * (kq & 1), k0 = 2 * it * BKV + rb;
@@ -861,8 +1025,12 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-
-        float* mg = reinterpret_cast<float*>(smem);
+        // the next phase's first stage (if loaded) sits in slot (npair + sbase) & 1; the
+        // merges use the other slot
+        const int nslot = (npair + sbase) & 1;
+        staged = PRE && ph + 1 < nphase && npair > 0;
+        sbase = staged ? nslot : 0;
+        float* mg = reinterpret_cast<float*>((staged && nslot == 0) ? st1 : st0);
         bool writer;
         if constexpr (MASKED) {  // (k0 + k1) + (k2 + k3) per row group
             merge_halves<DB>(dq, mg, kq & 1, 2 * rg + (kq >> 1), lane);
@@ -873,7 +1041,7 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
             writer = pr.kp == 0;
         }
         if (writer && qw < s) store_rowT<D, ST>(a.dqkv + ((int64_t)b * s + qw) * a.ld_qkv + g * D, dq, a.scale, lane);
-        __syncthreads();  // the merge area is the first stage of the next phase
+        __syncthreads();  // the merge area is a stage of the next phase
     }
 }
 
