@@ -139,7 +139,12 @@ int tp_check_dims(const tp_dims* dims, int shard, int degree);
 size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree);
 size_t tp_attn_saved_bytes(const tp_dims* dims, int shard, int degree);
 
-/* Bytes of the `work` buffer the backward needs (0 if the dims are invalid). */
+/* Bytes of the `work` buffer the backward needs (0 if the dims are invalid):
+ * the backward's intermediates (dU; dO and dQKV), column-sum partials and, on
+ * the 16-bit path, one fp32 slab the size of the call's weight gradients, which
+ * takes the second half's partial sums when the weight-gradient GEMM splits K
+ * in two (the halves are then added in one fixed order: results do not depend
+ * on timing). */
 size_t tp_mlp_work_bytes(const tp_dims* dims, int shard, int degree);
 size_t tp_attn_work_bytes(const tp_dims* dims, int shard, int degree);
 
@@ -172,11 +177,11 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree,
  * FFN shard backward that allocates nothing, for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses that
  * forbid allocation): the same computation, kernels and results (bitwise) as
- * tp_mlp_shard_bwd, with no `work` argument.  Its scratch (dU and the column-sum
- * partials, tp_mlp_work_bytes of them) is a static device array of
- * TP_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on until
- * the process ends; dims whose tp_mlp_work_bytes exceed it return TP_ESCRATCH
- * before any HIP call (the 8.3B-shape t = 8 shard needs 25.4 MB).  Every launch
+ * tp_mlp_shard_bwd, with no `work` argument.  Its scratch (dU, the column-sum
+ * partials and the K-split slab, tp_mlp_work_bytes of them) is a static device
+ * array of TP_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on until the process ends; dims whose tp_mlp_work_bytes exceed it return
+ * TP_ESCRATCH before any HIP call (the 8.3B-shape t = 8 shard needs 63.1 MB).  Every launch
  * runs on `stream` (no auxiliary stream, no events); no device or host memory is
  * allocated and no allocating library routine is called (the first call on a
  * device looks up the array's device address once).  All calls on one device

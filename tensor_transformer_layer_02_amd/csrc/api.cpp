@@ -114,24 +114,30 @@ AttnSaved attn_saved(const Shape& s) {
     return {0, q, q + o, q + o + l};
 }
 
+// Work buffers.  `part` (fp32, 16-bit path only) takes the second K half's partial
+// sums of the weight-gradient launch when it is split in two: one float per weight
+// gradient element of the launch.
 struct MlpWork {
-    int64_t dU, cs, total;
+    int64_t dU, cs, part, part_floats, total;
 };
 MlpWork mlp_work(const Shape& s) {
     const int64_t du = align256(s.T * s.Fs * s.e);
     const int64_t cs = align256(tp::colsum_work_floats(s.Fs) * 4);
-    return {0, du, du + cs};
+    const int64_t pf = s.h16 ? 2 * s.Fs * s.h : 0;
+    return {0, du, du + cs, pf, du + cs + align256(pf * 4)};
 }
 
 struct AttnWork {
-    int64_t dO, dQKV, Dq, cs, total;
+    int64_t dO, dQKV, Dq, cs, part, part_floats, total;
 };
 AttnWork attn_work(const Shape& s) {
     const int64_t dO = align256(s.T * s.w * s.e);
     const int64_t dq = align256(s.T * 3 * s.w * s.e);
     const int64_t D = align256(s.b * s.Hs * s.s * 4);
     const int64_t cs = align256(tp::colsum_work_floats(3 * s.w) * 4);
-    return {0, dO, dO + dq, dO + dq + D, dO + dq + D + cs};
+    const int64_t pf = s.h16 ? 4 * s.w * s.h : 0;  // dW{q,k,v}_i and dWo_i
+    const int64_t p0 = dO + dq + D + cs;
+    return {0, dO, dO + dq, dO + dq + D, p0, pf, p0 + align256(pf * 4)};
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_EHIP; }
@@ -177,13 +183,6 @@ inline tp::GemmDesc fmt_of(const Shape& s, const tp::GemmDesc& g) {
 inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
     StepTimer t(step, st);
     return s.h16 ? tp::gemm_bf16(fmt_of(s, g), st) : tp::gemm_f32(g, st);
-}
-
-// A weight-gradient GEMM (fp32 output; the bf16 path may split K in two).
-inline hipError_t gemm_w(const Shape& s, const tp::GemmDesc& g, hipStream_t st, int step) {
-    StepTimer t(step, st);
-    const tp::GemmDesc d = fmt_of(s, g);
-    return s.h16 ? tp::gemm_bf16_batch(&d, 1, true, nullptr, st) : tp::gemm_f32(g, st);
 }
 
 // Per-device auxiliary stream for launches that are independent of the main
@@ -258,13 +257,15 @@ struct AuxScope {
     }
 };
 
-// Two independent weight-gradient GEMMs of the same layout in one launch
-// (bf16 path; may split K in two with zeroed outputs), or one after the other.
-inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, hipStream_t st, int step) {
+// Two independent weight-gradient GEMMs of the same layout in one launch (16-bit
+// path; may split K in two, the second half's partial sums going to `part`), or
+// one after the other.
+inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, float* part, int64_t part_floats, hipStream_t st,
+                        int step) {
     StepTimer t(step, st);
     if (s.h16) {
         const tp::GemmDesc d[2] = {fmt_of(s, g[0]), fmt_of(s, g[1])};
-        return tp::gemm_bf16_batch(d, 2, true, nullptr, st);
+        return tp::gemm_bf16_batch(d, 2, part, part_floats, nullptr, st);
     }
     hipError_t e = tp::gemm_f32(g[0], st);
     return e != hipSuccess ? e : tp::gemm_f32(g[1], st);
@@ -328,13 +329,16 @@ int mlp_bwd_check(const void* X, const void* A, const void* B, const void* saved
 }
 
 // The FFN backward's launches: dU (GEMM with the GeLU' epilogue), db1 (column
-// sums of dU), dB and dA (one GEMM launch), dX_part.  dU and the column-sum
-// partials go to `dU` and `cs` (scratch the caller or the library provides).
+// sums of dU), dB and dA (one GEMM launch), dX_part.  dU, the column-sum
+// partials and the K-split partial sums go to `work` (laid out by mlp_work: the
+// caller's buffer or the library's static one).
 // With `aux`, the column sum runs on the auxiliary stream beside the GEMMs;
 // without, every launch runs on `st` (same kernels, same results).
 int mlp_bwd_run(const Shape& s, const void* X, const void* A, const void* B, const void* saved, const void* dZ,
-                void* dX_part, float* dA, float* db1, float* dB, void* dU, float* cs, hipStream_t st,
-                AuxScope* aux) {
+                void* dX_part, float* dA, float* db1, float* dB, void* work, hipStream_t st, AuxScope* aux) {
+    const MlpWork W = mlp_work(s);
+    void* dU = at(work, W.dU, 1);
+    float* cs = static_cast<float*>(at(work, W.cs, 1));
     const MlpSaved L = mlp_saved(s);
     const void* U = at(saved, L.U, 1);
     const void* Y = at(saved, L.Y, 1);
@@ -371,7 +375,8 @@ int mlp_bwd_run(const Shape& s, const void* X, const void* A, const void* B, con
     ga.A = X; ga.lda = s.h; ga.a_kcontig = false;
     ga.B[0] = dU; ga.ldb = s.Fs; ga.b_kcontig = false;
     ga.C[0] = dA + c0; ga.ldc = s.F; ga.out_f32 = true;
-    if (gemm2(s, gw, st, TP_STEP_MLP_DW) != hipSuccess) return TP_EHIP;
+    if (gemm2(s, gw, static_cast<float*>(at(work, W.part, 1)), W.part_floats, st, TP_STEP_MLP_DW) != hipSuccess)
+        return TP_EHIP;
 
     tp::GemmDesc gx;  // dX_part = dU A[:, C_i]^T
     gx.M = (int)s.T; gx.N = (int)s.h; gx.K = (int)s.Fs;
@@ -493,8 +498,7 @@ int tp_mlp_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X, 
     if (work_bytes < (size_t)W.total) return TP_ESIZE;
     AuxScope aux;
     if (aux.err != hipSuccess) return TP_EHIP;
-    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, at(work, W.dU, 1),
-                       static_cast<float*>(at(work, W.cs, 1)), static_cast<hipStream_t>(stream), &aux);
+    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, work, static_cast<hipStream_t>(stream), &aux);
 }
 
 int tp_mlp_shard_bwd_noalloc(const tp_dims* dims, int shard, int degree, const void* X, const void* A,
@@ -508,8 +512,8 @@ int tp_mlp_shard_bwd_noalloc(const tp_dims* dims, int shard, int degree, const v
     if (W.total > tp::NOALLOC_SCRATCH_BYTES) return TP_ESCRATCH;
     void* scratch = nullptr;  // the device address of this device's static array
     if (tp::noalloc_scratch(&scratch) != hipSuccess) return TP_EHIP;
-    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, at(scratch, W.dU, 1),
-                       static_cast<float*>(at(scratch, W.cs, 1)), static_cast<hipStream_t>(stream), nullptr);
+    return mlp_bwd_run(s, X, A, B, saved, dZ, dX_part, dA, db1, dB, scratch, static_cast<hipStream_t>(stream),
+                       nullptr);
 }
 
 int tp_attn_shard_fwd(const tp_dims* dims, int shard, int degree, const void* X, const void* Wq, const void* Wk,
@@ -628,7 +632,8 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
     gw[1] = go;
-    if (gemm2(s, gw, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
+    if (gemm2(s, gw, static_cast<float*>(at(work, W.part, 1)), W.part_floats, st, TP_STEP_ATTN_DW) != hipSuccess)
+        return TP_EHIP;
     return aux.to_main(st, 1) != hipSuccess ? TP_EHIP : TP_OK;
 }
 

@@ -55,9 +55,10 @@
 //    which every thread stores 16 bytes of a row; fp32 outputs and the GeLU'
 //    epilogue (which reads U) stage half a tile at a time as fp32.
 //  * Two independent problems of one layout (the two weight gradients of a
-//    sublayer) share a launch; fp32 outputs may split K in two, both halves
-//    adding into a zeroed block (0 + a + b == 0 + b + a exactly, so the result
-//    is deterministic).
+//    sublayer) share a launch; fp32 outputs may split K in two.  The first
+//    split writes the output, the second its partial sums to a slab of the
+//    caller's work buffer with plain stores, and a reduction kernel adds the
+//    slab into the output (one fixed order: deterministic, and no atomics).
 #include "tp_common.h"
 #include "tp_kernels.h"
 
@@ -99,7 +100,10 @@ struct GemmBatch {
     int n;         // problems
     int tiles0;    // tiles of problem 0
     int tiles;     // tiles of all problems
-    int ksplit;    // 1, or 2 (fp32 outputs only: partial tiles are added atomically)
+    int ksplit;    // 1, or 2 (fp32 outputs only)
+    float* part;   // K split: split s > 0 writes slab s - 1, problem i at poff[i] (dense [M][N])
+    int64_t pslab;
+    int64_t poff[2];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -897,7 +901,12 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
             // issued before its first use, so their latencies overlap instead of
             // adding up item by item.
             constexpr int G = ITEMS < 4 ? ITEMS : 4;
-            if (epi_wave && (!OUTF32 || batch.ksplit == 1)) {
+            // A K split's first part goes to the output, part s > 0 to its slab (dense [M][N]).
+            float* const obase = split == 0 ? reinterpret_cast<float*>(p.C[csg])
+                                            : batch.part + (int64_t)(split - 1) * batch.pslab + batch.poff[prob];
+            const int64_t old = split == 0 ? p.ldc : p.N;
+            const int ocol = split == 0 ? cofs : 0;
+            if (epi_wave) {
 #pragma unroll
                 for (int g0 = 0; g0 < ITEMS; g0 += G) {
                     f32x4 lo[G], hi[G];
@@ -929,7 +938,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                         const int lr = e / GPR, cg = e % GPR;
                         const int m = m0 + half * EROWS + lr, nl = n0 + cg * 8 - cofs;
                         if constexpr (OUTF32) {
-                            float* c = reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + nl;
+                            float* c = obase + (int64_t)m * old + (n0 + cg * 8 - ocol);
                             *reinterpret_cast<f32x4*>(c) = lo[k];
                             *reinterpret_cast<f32x4*>(c + 4) = hi[k];
                         } else {  // EPI_GELU_BWD: dU = dY * GeLU'(U)
@@ -944,23 +953,6 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                             for (int q = 0; q < 4; ++q) o[q] = Store16<ST>::pack2(v[2 * q], v[2 * q + 1]);
                             *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m * p.ldc + nl) = o;
                         }
-                    }
-                }
-            }
-            if constexpr (OUTF32) {
-                if (batch.ksplit > 1) {
-                    // The two K halves add into a zeroed block (0 + a + b == 0 + b + a
-                    // exactly, so the result does not depend on their order); consecutive
-                    // lanes take consecutive columns so each atomic covers whole lines.
-                    constexpr int AITEMS = EROWS * BN / NT;
-#pragma unroll 4
-                    for (int it = 0; it < AITEMS; ++it) {
-                        const int e = tid + it * NT;
-                        const int lr = e / BN, c = e % BN;
-                        const int m = m0 + half * EROWS + lr, n = n0 + c;
-                        if (epi_wave && m < p.M && n < p.N)
-                            atomicAdd(reinterpret_cast<float*>(p.C[csg]) + (int64_t)m * p.ldc + (n - cofs),
-                                      stage[lr * ELD + c]);
                     }
                 }
             }
@@ -1100,15 +1092,26 @@ int gemm_tile_count() { return (int)(sizeof(kCands) / sizeof(kCands[0])); }
 // overhead (prologue and epilogue, larger with GeLU math) being hidden by the
 // other resident tiles.
 // Every N-segment must hold whole tiles; the 192 x 192 tile and the K split
-// serve only the fp32 weight-gradient GEMMs (split outputs are zeroed first).
-hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s) {
+// serve only the fp32 weight-gradient GEMMs.  The split needs a partial-sum
+// slab of sum(M N) floats in `part` (part_floats of them available).
+hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_floats, int* ksplit_out,
+                           hipStream_t s) {
     if (n < 1 || n > 2) return hipErrorInvalidValue;
     GemmBatch b;
     b.n = 0;
+    b.part = part;
+    b.pslab = 0;
+    const GemmDesc* live[2];
     for (int i = 0; i < n; ++i)
-        if (d[i].M > 0 && d[i].N > 0 && d[i].K > 0) b.g[b.n++] = make_args(d[i]);
+        if (d[i].M > 0 && d[i].N > 0 && d[i].K > 0) {
+            b.poff[b.n] = b.pslab;
+            b.pslab += (int64_t)d[i].M * d[i].N;
+            live[b.n] = &d[i];
+            b.g[b.n++] = make_args(d[i]);
+        }
     if (ksplit_out) *ksplit_out = 1;
     if (b.n == 0) return hipSuccess;
+    const bool allow_split = part && part_floats >= b.pslab && (reinterpret_cast<uintptr_t>(part) & 15u) == 0;
     const bool tn32 = !d[0].a_kcontig && !d[0].b_kcontig && !d[0].b_kseg && d[0].out_f32;
     int best = -1, best_split = 1;
     double best_cost = 1e300;
@@ -1150,28 +1153,29 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* kspl
     if (best < 0) return hipErrorInvalidValue;
     b.ksplit = best_split;
     if (ksplit_out) *ksplit_out = best_split;
-    if (best_split > 1) {  // the K halves add into zeroed output blocks (one launch for all of them)
-        const float* zp[ZMAX];
-        int64_t zr[ZMAX], zc[ZMAX], zl[ZMAX];
-        int nz = 0;
-        for (int i = 0; i < n; ++i) {
-            const GemmDesc& g = d[i];
-            if (g.M <= 0 || g.N <= 0 || g.K <= 0) continue;
-            const int seg = g.cseg < (1 << 30) ? g.cseg : g.N;
-            for (int z = 0; z * seg < g.N && z < 3; ++z) {
-                zp[nz] = static_cast<const float*>(g.C[z] ? g.C[z] : g.C[0]);
-                zr[nz] = g.M;
-                zc[nz] = g.N - z * seg < seg ? g.N - z * seg : seg;
-                zl[nz] = g.ldc;
-                ++nz;
-            }
+    hipError_t e = d[0].fp16 ? dispatch_idx<f16_t>(best, d[0], b, s) : dispatch_idx<bf16_t>(best, d[0], b, s);
+    if (e != hipSuccess || best_split == 1) return e;
+    // The second K half's slab into the outputs (each N-segment its own block).
+    float* dst[ZMAX];
+    const float* src[ZMAX];
+    int64_t rows[ZMAX], cols[ZMAX], ld[ZMAX], lds[ZMAX];
+    int nr = 0;
+    for (int i = 0; i < b.n; ++i) {
+        const GemmDesc& g = *live[i];
+        const int seg = g.cseg < (1 << 30) ? g.cseg : g.N;
+        for (int z = 0; z * seg < g.N && z < 3; ++z) {
+            dst[nr] = static_cast<float*>(g.C[z] ? g.C[z] : g.C[0]);
+            src[nr] = part + b.poff[i] + (int64_t)z * seg;
+            rows[nr] = g.M;
+            cols[nr] = g.N - z * seg < seg ? g.N - z * seg : seg;
+            ld[nr] = g.ldc;
+            lds[nr] = g.N;
+            ++nr;
         }
-        hipError_t e = zero_f32_2d(zp, zr, zc, zl, nz, s);
-        if (e != hipSuccess) return e;
     }
-    return d[0].fp16 ? dispatch_idx<f16_t>(best, d[0], b, s) : dispatch_idx<bf16_t>(best, d[0], b, s);
+    return add_f32_2d(dst, src, rows, cols, ld, lds, nr, s);
 }
 
-hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s) { return gemm_bf16_batch(&d, 1, false, nullptr, s); }
+hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s) { return gemm_bf16_batch(&d, 1, nullptr, 0, nullptr, s); }
 
 }  // namespace tp

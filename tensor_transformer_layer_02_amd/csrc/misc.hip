@@ -73,18 +73,22 @@ __global__ void __launch_bounds__(256) colsum_final_kernel(const float* __restri
 
 // Zero up to ZMAX row-major fp32 blocks in one launch; thread item i covers 4
 // floats of one row (f32x4 store when aligned).
-__global__ void __launch_bounds__(256) zero_f32_2d_kernel(const ZeroRegions z) {
+// dst[k] += src[k] over n row-major fp32 blocks (rows[k] x cols[k]; row strides
+// ld[k] and lds[k]), four columns per item where both rows are 16-byte aligned.
+__global__ void __launch_bounds__(256) add_f32_2d_kernel(const AddRegions z) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < z.total; i += (int64_t)gridDim.x * 256) {
         int k = 0;
         while (k + 1 < z.n && i >= z.start[k + 1]) ++k;
         const int64_t j = i - z.start[k];
         const int64_t c4 = (z.cols[k] + 3) / 4;
         const int64_t r = j / c4, c = (j % c4) * 4;
-        float* q = z.p[k] + r * z.ld[k] + c;
-        if (c + 4 <= z.cols[k] && ((reinterpret_cast<uintptr_t>(q) & 15) == 0)) {
-            *reinterpret_cast<f32x4*>(q) = f32x4{0.f, 0.f, 0.f, 0.f};
+        float* q = z.dst[k] + r * z.ld[k] + c;
+        const float* a = z.src[k] + r * z.lds[k] + c;
+        if (c + 4 <= z.cols[k] && ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(a)) & 15) == 0) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(q), y = *reinterpret_cast<const f32x4*>(a);
+            *reinterpret_cast<f32x4*>(q) = f32x4{x[0] + y[0], x[1] + y[1], x[2] + y[2], x[3] + y[3]};
         } else {
-            for (int64_t e = c; e < z.cols[k] && e < c + 4; ++e) z.p[k][r * z.ld[k] + e] = 0.f;
+            for (int64_t e = 0; c + e < z.cols[k] && e < 4; ++e) q[e] += a[e];
         }
     }
 }
@@ -131,24 +135,26 @@ hipError_t colsum(int fmt, const void* X, int64_t rows, int64_t cols, int64_t ld
     return hipGetLastError();
 }
 
-hipError_t zero_f32_2d(const float* const* p, const int64_t* rows, const int64_t* cols, const int64_t* ld, int n,
-                       hipStream_t s) {
+hipError_t add_f32_2d(float* const* dst, const float* const* src, const int64_t* rows, const int64_t* cols,
+                      const int64_t* ld, const int64_t* lds, int n, hipStream_t s) {
     if (n < 0 || n > ZMAX) return hipErrorInvalidValue;
-    ZeroRegions z;
+    AddRegions z;
     z.n = 0;
     z.total = 0;
     for (int k = 0; k < n; ++k) {
         if (rows[k] <= 0 || cols[k] <= 0) continue;
-        z.p[z.n] = const_cast<float*>(p[k]);
+        z.dst[z.n] = dst[k];
+        z.src[z.n] = src[k];
         z.cols[z.n] = cols[k];
         z.ld[z.n] = ld[k];
+        z.lds[z.n] = lds[k];
         z.start[z.n] = z.total;
         z.total += rows[k] * ((cols[k] + 3) / 4);
         ++z.n;
     }
     if (z.total == 0) return hipSuccess;
     const int64_t blocks = (z.total + 255) / 256;
-    hipLaunchKernelGGL(zero_f32_2d_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, z);
+    hipLaunchKernelGGL(add_f32_2d_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, z);
     count_launch();
     return hipGetLastError();
 }

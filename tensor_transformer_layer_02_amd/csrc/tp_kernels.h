@@ -55,28 +55,30 @@ struct GemmDesc {
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
 hipError_t gemm_bf16(const GemmDesc& d, hipStream_t s);
 // One launch for n (1 or 2) independent problems of the same layout and
-// epilogue.  With allow_split, fp32-output (weight-gradient) problems may be
-// split in two along K (*ksplit_out reports it); the output blocks are then
-// zeroed first by a kernel on the same stream and the halves added atomically.
-hipError_t gemm_bf16_batch(const GemmDesc* d, int n, bool allow_split, int* ksplit_out, hipStream_t s);
+// epilogue.  fp32-output (weight-gradient) problems may be split in two along
+// K when `part` (16-byte aligned) holds at least sum(M N) floats (*ksplit_out
+// reports the split): the first half writes the outputs, the second its
+// partial sums to `part`, and a kernel on the same stream then adds them in.
+hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_floats, int* ksplit_out,
+                           hipStream_t s);
 // Test hook: every later 16-bit GEMM for which tile `tile` (0 .. gemm_tile_count()-1)
 // is valid uses it, with a K split of `ksplit` (2: fp32-output GEMMs split in two;
 // else no split); tile < 0 restores the cost model.  Process-wide, not thread-safe.
 void gemm_force_tile(int tile, int ksplit);
 int gemm_tile_count();
 
-// Zero a [rows, cols] fp32 block with row stride ld (a kernel, so it can be captured).
-// Zero n (<= ZMAX) row-major fp32 blocks (p[k]: rows[k] x cols[k], row stride
-// ld[k]) in one launch.
+// dst[k] += src[k] for n (<= ZMAX) row-major fp32 blocks (rows[k] x cols[k],
+// row strides ld[k] and lds[k]) in one launch.
 constexpr int ZMAX = 6;
-struct ZeroRegions {
-    float* p[ZMAX];
-    int64_t cols[ZMAX], ld[ZMAX], start[ZMAX];
+struct AddRegions {
+    float* dst[ZMAX];
+    const float* src[ZMAX];
+    int64_t cols[ZMAX], ld[ZMAX], lds[ZMAX], start[ZMAX];
     int64_t total;
     int n;
 };
-hipError_t zero_f32_2d(const float* const* p, const int64_t* rows, const int64_t* cols, const int64_t* ld, int n,
-                       hipStream_t s);
+hipError_t add_f32_2d(float* const* dst, const float* const* src, const int64_t* rows, const int64_t* cols,
+                      const int64_t* ld, const int64_t* lds, int n, hipStream_t s);
 // fp32 operands and outputs, fp32 FMA arithmetic.
 hipError_t gemm_f32(const GemmDesc& d, hipStream_t s);
 
