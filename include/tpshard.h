@@ -129,7 +129,8 @@ int tp_check_dims(const tp_dims* dims, int shard, int degree);
 /*
  * Bytes of the `saved` buffer.  Layout (each region 256-byte aligned, in
  * this order, elements of dims.act unless noted):
- *   MLP:       U [T, F/t]  (pre-GeLU),  Y [T, F/t]  (post-GeLU)
+ *   MLP:       Gp [T, F/t] = GeLU'(U) (all the backward needs of the
+ *              pre-GeLU U, which is not kept),  Y [T, F/t] = GeLU(U)
  *   attention: QKV [T, 3w] (columns [0,w) = Q, [w,2w) = K, [2w,3w) = V of
  *              the shard's heads, w = (H/t)*d, head-local column c of
  *              local head g at g*d + c), O [T, w], LSE [batch, H/t, seq]
@@ -152,7 +153,7 @@ size_t tp_attn_work_bytes(const tp_dims* dims, int shard, int degree);
  * FFN shard forward ("How transformer layers actually decompose"):
  *   U = X A[:, C_i] + b1[C_i],  Y = GeLU(U),  Z_part = Y B[C_i, :].
  * X [T, h]; A [h, F]; b1 [F] or NULL (zero); B [F, h]; Z_part [T, h] out;
- * saved: see tp_mlp_saved_bytes.
+ * saved: see tp_mlp_saved_bytes (Gp = GeLU'(U) and Y, both from the fp32 U).
  */
 int tp_mlp_shard_fwd(const tp_dims* dims, int shard, int degree,
                      const void* X, const void* A, const void* b1, const void* B,
@@ -160,7 +161,7 @@ int tp_mlp_shard_fwd(const tp_dims* dims, int shard, int degree,
 
 /*
  * FFN shard backward, given G = dZ [T, h] (the same G reaches every shard):
- *   dY = G B[C_i, :]^T,  dU = dY * GeLU'(U),
+ *   dY = G B[C_i, :]^T,  dU = dY * GeLU'(U) (the saved Gp),
  *   dB[C_i, :] = Y^T G,  dA[:, C_i] = X^T dU,  db1[C_i] = column sums of dU,
  *   dX_part = dU A[:, C_i]^T.
  * dA [h, F], db1 [F] (NULL: skipped), dB [F, h] are full-size fp32 buffers;
@@ -230,12 +231,12 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree,
  * Measurement hook.  Steps of the path, in launch order:
  */
 enum {
-    TP_STEP_MLP_UP = 0,      /* U = X A_i + b1, Y = GeLU(U)         (column-parallel GEMM) */
+    TP_STEP_MLP_UP = 0,      /* U = X A_i + b1; GeLU'(U), GeLU(U)   (column-parallel GEMM) */
     TP_STEP_MLP_DOWN = 1,    /* Z_part = Y B_i                      (row-parallel GEMM)    */
     TP_STEP_QKV = 2,         /* QKV = X W{q,k,v}_i + b               (column-parallel GEMM) */
     TP_STEP_ATTN_CORE = 3,   /* softmax attention forward -> O, LSE                          */
     TP_STEP_ATTN_OUT = 4,    /* Z_part = O Wo_i                     (row-parallel GEMM)    */
-    TP_STEP_MLP_DU = 5,      /* dU = (dZ B_i^T) * GeLU'(U)                                  */
+    TP_STEP_MLP_DU = 5,      /* dU = (dZ B_i^T) * GeLU'(U)  (GeLU'(U) saved by the forward) */
     TP_STEP_MLP_DW = 6,      /* dB_i = Y^T dZ and dA_i = X^T dU (one launch)                */
     TP_STEP_MLP_DB1 = 7,     /* db1_i = column sums of dU                                   */
     TP_STEP_MLP_DX = 8,      /* dX_part = dU A_i^T                                          */
@@ -254,7 +255,7 @@ enum {
  * "What actually limits throughput in production": activation checkpointing
  * recomputes the forward's activations in the backward instead of keeping
  * them).  They take no `saved` buffer: the forward steps whose outputs the
- * backward reads (MLP: U and Y, one GEMM; attention: QKV and the attention
+ * backward reads (MLP: GeLU'(U) and Y, one GEMM; attention: QKV and the attention
  * core, O and LSE) run again from X into the front of `work`, then the
  * backward runs exactly as tp_*_shard_bwd, so the results are bitwise those of
  * the saved-activation path.  The caller need not keep `saved` from the

@@ -3,8 +3,8 @@
 // Each entry point validates every argument on the host first (no HIP call
 // before validation passes, nothing written on failure), then enqueues its
 // kernels on the caller's stream:
-//   tp_mlp_shard_fwd : [X*A_i + b1 -> U, GeLU -> Y]  [Y*B_i -> Z_part]
-//   tp_mlp_shard_bwd : [dZ*B_i^T (*) GeLU'(U) -> dU]  [Y^T dZ -> dB_i]
+//   tp_mlp_shard_fwd : [X*A_i + b1 -> U, GeLU'(U) -> Gp, GeLU(U) -> Y]  [Y*B_i -> Z_part]
+//   tp_mlp_shard_bwd : [dZ*B_i^T (*) Gp -> dU]  [Y^T dZ -> dB_i]
 //                      [X^T dU -> dA_i]  [colsum dU -> db1_i]  [dU*A_i^T -> dX_part]
 //   tp_attn_shard_fwd: [X*[Wq|Wk|Wv]_i + b -> QKV]  [fused attention -> O, LSE]
 //                      [O*Wo_i -> Z_part]
@@ -97,7 +97,7 @@ inline P* at(P* base, int64_t elems, int64_t esize) {
 }
 
 struct MlpSaved {
-    int64_t U, Y, total;
+    int64_t Gp, Y, total;
 };
 MlpSaved mlp_saved(const Shape& s) {
     const int64_t u = align256(s.T * s.Fs * s.e);
@@ -272,7 +272,8 @@ inline hipError_t gemm2(const Shape& s, const tp::GemmDesc* g, float* part, int6
 }
 
 // The forward steps whose outputs the backward needs, into `saved`:
-// U = X A[:, C_i] + b1[C_i] and Y = GeLU(U) (one GEMM with a fused epilogue).
+// Gp = GeLU'(U) and Y = GeLU(U) of U = X A[:, C_i] + b1[C_i] (one GEMM with a fused
+// epilogue).  U itself is not kept: the backward needs only GeLU'(U).
 hipError_t mlp_fwd_saved(const Shape& s, const void* X, const void* A, const void* b1, void* saved,
                          hipStream_t st) {
     const MlpSaved L = mlp_saved(s);
@@ -281,7 +282,7 @@ hipError_t mlp_fwd_saved(const Shape& s, const void* X, const void* A, const voi
     g1.M = (int)s.T; g1.N = (int)s.Fs; g1.K = (int)s.h;
     g1.A = X; g1.lda = s.h; g1.a_kcontig = true;
     g1.B[0] = at(A, c0, s.e); g1.ldb = s.F; g1.b_kcontig = false;
-    g1.C[0] = at(saved, L.U, 1); g1.ldc = s.Fs; g1.C2 = at(saved, L.Y, 1); g1.ldc2 = s.Fs;
+    g1.C[0] = at(saved, L.Gp, 1); g1.ldc = s.Fs; g1.C2 = at(saved, L.Y, 1); g1.ldc2 = s.Fs;
     g1.bias[0] = b1 ? at(b1, c0, s.e) : nullptr;
     g1.epi = tp::EPI_BIAS_GELU;
     g1.gelu_tanh = s.gelu_tanh;
@@ -340,15 +341,15 @@ int mlp_bwd_run(const Shape& s, const void* X, const void* A, const void* B, con
     void* dU = at(work, W.dU, 1);
     float* cs = static_cast<float*>(at(work, W.cs, 1));
     const MlpSaved L = mlp_saved(s);
-    const void* U = at(saved, L.U, 1);
+    const void* Gp = at(saved, L.Gp, 1);
     const void* Y = at(saved, L.Y, 1);
     const int64_t c0 = s.i * s.Fs;
 
-    tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * GeLU'(U)
+    tp::GemmDesc g;  // dU = (dZ B[C_i, :]^T) * Gp, Gp = GeLU'(U)
     g.M = (int)s.T; g.N = (int)s.Fs; g.K = (int)s.h;
     g.A = dZ; g.lda = s.h; g.a_kcontig = true;
     g.B[0] = at(B, c0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
-    g.C[0] = dU; g.ldc = s.Fs; g.aux = U; g.ldaux = s.Fs;
+    g.C[0] = dU; g.ldc = s.Fs; g.aux = Gp; g.ldaux = s.Fs;
     g.epi = tp::EPI_GELU_BWD;
     g.gelu_tanh = s.gelu_tanh;
     if (gemm(s, g, st, TP_STEP_MLP_DU) != hipSuccess) return TP_EHIP;

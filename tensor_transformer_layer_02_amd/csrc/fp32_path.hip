@@ -92,10 +92,11 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmArgsF p) {
                 *c = v + (p.bias[sg] ? p.bias[sg][nl] : 0.f);
             } else if constexpr (EPI == EPI_BIAS_GELU) {
                 const float u = v + (p.bias[sg] ? p.bias[sg][nl] : 0.f);
-                *c = u;
-                p.C2[(int64_t)m * p.ldc2 + nl] = gelu_sel(u, p.gelu_tanh != 0);
+                float d;
+                p.C2[(int64_t)m * p.ldc2 + nl] = gelu_and_prime(u, p.gelu_tanh != 0, d);
+                *c = d;  // Gp = GeLU'(U), what the backward needs of U
             } else {
-                *c = v * gelu_prime_sel(p.aux[(int64_t)m * p.ldaux + nl], p.gelu_tanh != 0);
+                *c = v * p.aux[(int64_t)m * p.ldaux + nl];  // dU = dY * Gp
             }
         }
     }

@@ -701,13 +701,13 @@ struct GemmCore {
     }
 };
 
-// bf16 epilogue, first half: the tile's values (plus bias, through GeLU when
-// GELU) as bf16 into a [BM][SP bytes] LDS image.  Each lane writes 8 bytes (4
+// bf16 epilogue, first half: the tile's values plus bias as bf16 into a
+// [BM][SP bytes] LDS image.  Each lane writes 8 bytes (4
 // columns of one row) per store; a row pitch of SP = 2*BN + 8 bytes (an odd
 // number of 8-byte pairs) puts the 32 rows of a half-wave on distinct banks.
-template <typename ST, int FM, int FN, int WTM, int WTN, int SP, bool GELU>
+template <typename ST, int FM, int FN, int WTM, int WTN, int SP>
 __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN], const bf16_t* bias, int ncols,
-                                           int wm, int wn, int lane, bool tanh_form = false) {
+                                           int wm, int wn, int lane) {
     // The wave's bias words, all loaded before the first is used (a lane past the valid
     // columns reads the first word instead and takes zeros).
     u32x2 bws[FN][4];
@@ -737,13 +737,41 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
             for (int i = 0; i < FM; ++i) {
                 float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = acc[i][j][4 * q + e] + b4[e];
-                    if constexpr (GELU) v[e] = gelu_sel(v[e], tanh_form);
-                }
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + b4[e];
                 const u32x2 o = {Store16<ST>::pack2(v[0], v[1]), Store16<ST>::pack2(v[2], v[3])};
                 *reinterpret_cast<u32x2*>(st + (wm * WTM + i * 32 + (lane & 31)) * SP + nl * 2) = o;
             }
+        }
+}
+
+// The GeLU epilogue, one 32-row fragment row i of every wave at a time: Gp =
+// GeLU'(u) and Y = GeLU(u) of u = value + bias as bf16 into two [NWR * 32][SP
+// bytes] images (wave row wm at image rows 32 wm ..), so that the stores of one
+// chunk are in flight while the next chunk's exponentials and reciprocals run.
+template <typename ST, int FM, int FN, int WTN, int SP>
+__device__ __forceinline__ void stage_gelu_chunk(char* gimg, char* yimg, const f32x16 (&acc)[FM][FN],
+                                                 const bf16_t* bias, int ncols, int wm, int wn, int lane,
+                                                 bool tanh_form, int i) {
+    const int r = wm * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);  // first of the 4 columns
+            u32x2 bw = u32x2{0u, 0u};
+            if (bias) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(bias + (nl < ncols ? nl : 0));
+                bw = nl < ncols ? w : u32x2{0u, 0u};
+            }
+            const float b4[4] = {Store16<ST>::lo(bw[0]), Store16<ST>::hi(bw[0]), Store16<ST>::lo(bw[1]),
+                                 Store16<ST>::hi(bw[1])};
+            float g[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = gelu_and_prime(acc[i][j][4 * q + e] + b4[e], tanh_form, g[e]);
+            *reinterpret_cast<u32x2*>(gimg + r * SP + nl * 2) = u32x2{Store16<ST>::pack2(g[0], g[1]),
+                                                                     Store16<ST>::pack2(g[2], g[3])};
+            *reinterpret_cast<u32x2*>(yimg + r * SP + nl * 2) = u32x2{Store16<ST>::pack2(y[0], y[1]),
+                                                                     Store16<ST>::pack2(y[2], y[3])};
         }
 }
 
@@ -753,8 +781,11 @@ __device__ __forceinline__ void stage_bf16(char* st, const f32x16 (&acc)[FM][FN]
 // the L2 does not hold dirty need no write-back when the kernel ends (measured:
 // the gap to the next launch 4.0 -> 2.5 us, the bf16-output GEMMs 1-2 us
 // faster; the fp32 weight-gradient stores stay plain, they slowed down).
-template <int BM, int BN, int SP, int NTH>
-__device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ldc, int rows, int ncols, int tid) {
+// With RSTRIDE, the image holds one 32-row block per wave row (a chunk of the
+// tile): image row lr is tile row (lr / 32) * RSTRIDE + roff + lr % 32.
+template <int BM, int BN, int SP, int NTH, int RSTRIDE = 0>
+__device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ldc, int rows, int ncols, int tid,
+                                           int roff = 0) {
     constexpr int GPR = BN / 8;  // 8-column groups per row
     constexpr int ITEMS = BM * GPR / NTH;
     static_assert((BM * GPR) % NTH == 0, "epilogue split");
@@ -779,8 +810,9 @@ __device__ __forceinline__ void store_bf16(const char* st, bf16_t* C, int64_t ld
         for (int k = 0; k < G; ++k) {
             const int e = tid + (g0 + k) * NTH;
             const int lr = e / GPR, cg = e % GPR;
-            if (g0 + k < ITEMS && lr < rows && cg * 8 < ncols)
-                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(C + (int64_t)lr * ldc + cg * 8));
+            const int tr = RSTRIDE ? (lr >> 5) * RSTRIDE + roff + (lr & 31) : lr;
+            if (g0 + k < ITEMS && tr < rows && cg * 8 < ncols)
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(C + (int64_t)tr * ldc + cg * 8));
         }
     }
 }
@@ -862,20 +894,34 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const int rows = p.M - m0, ncols = p.N - n0;  // valid extent of the tile
     static_assert(F32STAGE || KG == 1, "bf16 epilogues assume every thread holds final sums");
     if constexpr (!F32STAGE) {
-        // Bias (and GeLU) on the accumulators; the output image goes through
-        // LDS once (twice with GeLU: U, then Y).
+        // Bias on the accumulators; the output image goes through LDS once.  With
+        // GeLU, Gp = GeLU'(U) (saved for the backward, which needs only that of U)
+        // and Y = GeLU(U) go through two images, one fragment row at a time.
         const bf16_t* bias = nullptr;
         if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias = p.bias[csg] ? p.bias[csg] + (n0 - cofs) : nullptr;
         bf16_t* C = reinterpret_cast<bf16_t*>(p.C[csg]) + (int64_t)m0 * p.ldc + (n0 - cofs);
         __syncthreads();  // every wave is done with the operand ring
-        stage_bf16<ST, FM, FN, WTM, WTN, SP, false>(smem, acc, bias, ncols, wm, wn, lane);
-        __syncthreads();
-        store_bf16<BM, BN, SP, NT>(smem, C, p.ldc, rows, ncols, tid);
         if constexpr (EPI == EPI_BIAS_GELU) {
+            constexpr int CR = BM / FM;  // image rows per chunk
+            static_assert(2 * CR * SP <= SMEM, "two chunk images must fit the LDS of the tile");
+            bf16_t* const C2 = p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (i > 0) {  // every thread has read the previous chunk's images (its stores may be in flight)
+                    wait_lgkm();
+                    stage_barrier();
+                }
+                stage_gelu_chunk<ST, FM, FN, WTN, SP>(smem, smem + CR * SP, acc, bias, ncols, wm, wn, lane,
+                                                      p.gelu_tanh != 0, i);
+                wait_lgkm();
+                stage_barrier();
+                store_bf16<CR, BN, SP, NT, WTM>(smem, C, p.ldc, rows, ncols, tid, i * 32);
+                store_bf16<CR, BN, SP, NT, WTM>(smem + CR * SP, C2, p.ldc2, rows, ncols, tid, i * 32);
+            }
+        } else {
+            stage_bf16<ST, FM, FN, WTM, WTN, SP>(smem, acc, bias, ncols, wm, wn, lane);
             __syncthreads();
-            stage_bf16<ST, FM, FN, WTM, WTN, SP, true>(smem, acc, bias, ncols, wm, wn, lane, p.gelu_tanh != 0);
-            __syncthreads();
-            store_bf16<BM, BN, SP, NT>(smem, p.C2 + (int64_t)m0 * p.ldc2 + (n0 - cofs), p.ldc2, rows, ncols, tid);
+            store_bf16<BM, BN, SP, NT>(smem, C, p.ldc, rows, ncols, tid);
         }
     } else {
         // fp32 staging, half a tile (the rows of wave rows wm / HR == half) at a time,
@@ -945,12 +991,12 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                             float* c = obase + (int64_t)m * old + (n0 + cg * 8 - ocol);
                             *reinterpret_cast<f32x4*>(c) = lo[k];
                             *reinterpret_cast<f32x4*>(c + 4) = hi[k];
-                        } else {  // EPI_GELU_BWD: dU = dY * GeLU'(U)
+                        } else {  // EPI_GELU_BWD: dU = dY * Gp, Gp = GeLU'(U) saved by the forward
                             float v[8] = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
-                                v[2 * q] *= gelu_prime_sel(Store16<ST>::lo(uw[k][q]), p.gelu_tanh != 0);
-                                v[2 * q + 1] *= gelu_prime_sel(Store16<ST>::hi(uw[k][q]), p.gelu_tanh != 0);
+                                v[2 * q] *= Store16<ST>::lo(uw[k][q]);
+                                v[2 * q + 1] *= Store16<ST>::hi(uw[k][q]);
                             }
                             u32x4 o;
 #pragma unroll

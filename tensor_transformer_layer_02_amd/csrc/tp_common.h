@@ -81,6 +81,21 @@ __device__ __forceinline__ float gelu_tanh_prime_f(float u) {
 }
 
 __device__ __forceinline__ float gelu_sel(float u, bool tanh_form) { return tanh_form ? gelu_tanh_f(u) : gelu_f(u); }
+
+// GeLU(u) and, in `d`, GeLU'(u) from one evaluation of Phi and phi (erf form) or
+// of s (tanh form): the values gelu_sel and gelu_prime_sel return.
+__device__ __forceinline__ float gelu_and_prime(float u, bool tanh_form, float& d) {
+    if (tanh_form) {
+        const float sg = gelu_tanh_s(u);
+        const float dz = 0.7978845608028654f * fmaf(0.134145f * u, u, 1.0f);
+        d = fmaf(2.0f * u * sg * (1.0f - sg), dz, sg);
+        return u * sg;
+    }
+    float pdf;
+    const float Phi = normal_cdf_pdf(u, pdf);
+    d = fmaf(u, pdf, Phi);
+    return u * Phi;
+}
 __device__ __forceinline__ float gelu_prime_sel(float u, bool tanh_form) {
     return tanh_form ? gelu_tanh_prime_f(u) : gelu_prime_f(u);
 }

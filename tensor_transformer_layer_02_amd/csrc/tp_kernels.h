@@ -17,8 +17,8 @@ enum Fmt : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_F16 = 2 };
 enum Epi : int {
     EPI_STORE = 0,      // C = acc (act dtype, or fp32 when out_f32)
     EPI_BIAS = 1,       // C = acc + bias[n]
-    EPI_BIAS_GELU = 2,  // C = U = acc + bias[n]; C2 = Y = GeLU(U)
-    EPI_GELU_BWD = 3,   // C = acc * GeLU'(aux[m, n])
+    EPI_BIAS_GELU = 2,  // U = acc + bias[n]; C = Gp = GeLU'(U); C2 = Y = GeLU(U)
+    EPI_GELU_BWD = 3,   // C = acc * aux[m, n] (aux: Gp of EPI_BIAS_GELU)
 };
 
 // C[M, N] (+epilogue) = sum_k A(m, k) B(k, n).
@@ -44,7 +44,7 @@ struct GemmDesc {
     void* C2 = nullptr;           // Y of EPI_BIAS_GELU
     int64_t ldc2 = 0;
     const void* bias[3] = {nullptr, nullptr, nullptr};
-    const void* aux = nullptr;    // U of EPI_GELU_BWD
+    const void* aux = nullptr;    // Gp of EPI_GELU_BWD
     int64_t ldaux = 0;
     int epi = EPI_STORE;
     bool gelu_tanh = false;       // EPI_BIAS_GELU / EPI_GELU_BWD: the tanh form of GeLU

@@ -223,7 +223,7 @@ def saved_layout(dims, shard, degree):
     w = Hs * d
     e = 4 if dims.act == TP_FP32 else 2
     a = lambda x: (x + 255) // 256 * 256
-    mlp = {"U": (0, (T, Fs)), "Y": (a(T * Fs * e), (T, Fs))}
+    mlp = {"Gp": (0, (T, Fs)), "Y": (a(T * Fs * e), (T, Fs))}  # Gp = GeLU'(U), Y = GeLU(U)
     attn = {"QKV": (0, (T, 3 * w)), "O": (a(T * 3 * w * e), (T, w)),
             "LSE": (a(T * 3 * w * e) + a(T * w * e), (dims.batch, Hs, dims.seq))}
     return mlp, attn

@@ -30,6 +30,11 @@ def oracle_inputs(inp: dict) -> dict:
     return {k: as_f64(v) for k, v in inp.items()}
 
 
+def gelu_prime_of(cfg: LayerConfig, U: np.ndarray) -> np.ndarray:
+    """The oracle's GeLU'(U) in the config's form: what the forward saves of U."""
+    return oracle.gelu_tanh_prime(U) if cfg.gelu == "tanh" else oracle.gelu_prime(U)
+
+
 def oracle_shard(cfg: LayerConfig, p: dict, i: int, degree: int | None = None,
                  grads: dict | None = None) -> dict:
     """Oracle forward + backward of shard i (float64)."""
@@ -38,7 +43,7 @@ def oracle_shard(cfg: LayerConfig, p: dict, i: int, degree: int | None = None,
     args = [p[n] for n in ("X", "Wq", "Wk", "Wv", "bq", "bk", "bv", "Wo")]
     mf = oracle.mlp_shard_fwd(d, i, t, p["X"], p["A"], p["b1"], p["B"])
     af = oracle.attn_shard_fwd(d, i, t, *args)
-    out = {"Z_mlp": mf["Z"], "U": mf["U"], "Y": mf["Y"], "Z_attn": af["Z"],
+    out = {"Z_mlp": mf["Z"], "Gp": gelu_prime_of(cfg, mf["U"]), "Y": mf["Y"], "Z_attn": af["Z"],
            "QKV": np.concatenate([af["Q"], af["K"], af["V"]], axis=1), "O": af["O"], "LSE": af["lse"]}
     if cfg.backward or grads is not None:
         g = grads if grads is not None else {}
@@ -136,7 +141,7 @@ def run_all_shards(cfg: LayerConfig, bias_std: float, report, **input_kw):
         torch.cuda.synchronize()
         o = oracle_shard(cfg.with_(backward=True), p, i, grads=grads)
         sv = run.saved(i)
-        for k in ("U", "Y", "QKV", "O"):
+        for k in ("Gp", "Y", "QKV", "O"):
             check(f"shard{i}.{k}", sv[k], o[k], tol, report)
         check_lse(sv["LSE"], sv["QKV"], o["LSE"], o["QKV"][:, :w], o["QKV"][:, w:2 * w], cfg, report)
         for k in ("Z_mlp", "Z_attn", "dX_mlp", "dX_attn"):
