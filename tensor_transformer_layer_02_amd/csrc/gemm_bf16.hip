@@ -951,11 +951,10 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
             // issued before its first use, so their latencies overlap instead of
             // adding up item by item.
             constexpr int G = ITEMS < 4 ? ITEMS : 4;
-            // A K split's first part goes to the output, part s > 0 to its slab (dense [M][N]).
-            float* const obase = split == 0 ? reinterpret_cast<float*>(p.C[csg])
-                                            : batch.part + (int64_t)(split - 1) * batch.pslab + batch.poff[prob];
-            const int64_t old = split == 0 ? p.ldc : p.N;
-            const int ocol = split == 0 ? cofs : 0;
+            // A K split's first part goes to the output, part s > 0 to its slab (dense
+            // [M][N]).  fp32 output tiles may straddle N-segments: each 8-column item
+            // (segments are multiples of 8 columns wide) finds its own.
+            float* const slab = batch.part + (int64_t)(split > 0 ? split - 1 : 0) * batch.pslab + batch.poff[prob];
             if (epi_wave) {
 #pragma unroll
                 for (int g0 = 0; g0 < ITEMS; g0 += G) {
@@ -988,7 +987,17 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                         const int lr = e / GPR, cg = e % GPR;
                         const int m = m0 + half * EROWS + lr, nl = n0 + cg * 8 - cofs;
                         if constexpr (OUTF32) {
-                            float* c = obase + (int64_t)m * old + (n0 + cg * 8 - ocol);
+                            float* c;
+                            if (split == 0) {
+                                int seg = csg, off = n0 + cg * 8 - cofs;
+                                while (off >= p.cseg && seg < 2) {
+                                    off -= p.cseg;
+                                    ++seg;
+                                }
+                                c = reinterpret_cast<float*>(p.C[seg]) + (int64_t)m * p.ldc + off;
+                            } else {
+                                c = slab + (int64_t)m * p.N + (n0 + cg * 8);
+                            }
                             *reinterpret_cast<f32x4*>(c) = lo[k];
                             *reinterpret_cast<f32x4*>(c + 4) = hi[k];
                         } else {  // EPI_GELU_BWD: dU = dY * Gp, Gp = GeLU'(U) saved by the forward
@@ -1101,6 +1110,10 @@ const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {
                        {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false},
                        {192, 192, 1, 0.975, true}};
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
+// The K split's reduction kernel in the same units (a CU's MACs at ~2.2 M per us):
+// three fp32 passes over the outputs at ~5 TB/s, plus a launch (~3 us).
+constexpr double RED_PER_ELEM = 5.3;
+constexpr double RED_FIXED = 6.6e6;
 constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
 
 template <typename ST>
@@ -1140,10 +1153,10 @@ int gemm_tile_count() { return (int)(sizeof(kCands) / sizeof(kCands[0])); }
 // gets ceil(items / 256) tiles and runs o = min(occupancy, that) of them at
 // once; each costs BM * BN * (K per split + overhead / o) / efficiency, the
 // overhead (prologue and epilogue, larger with GeLU math) being hidden by the
-// other resident tiles.
-// Every N-segment must hold whole tiles; the 192 x 192 tile and the K split
-// serve only the fp32 weight-gradient GEMMs.  The split needs a partial-sum
-// slab of sum(M N) floats in `part` (part_floats of them available).
+// other resident tiles; a K split adds its reduction kernel.  B's N-segments
+// (and C's, for 16-bit outputs) must hold whole tiles; the 192 x 192 tile and
+// the K split serve only the fp32 weight-gradient GEMMs.  The split needs a
+// partial-sum slab of sum(M N) floats in `part` (part_floats of them available).
 hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_floats, int* ksplit_out,
                            hipStream_t s) {
     if (n < 1 || n > 2) return hipErrorInvalidValue;
@@ -1180,8 +1193,10 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
         int64_t t = 0;
         for (int i = 0; i < n; ++i) {
             const GemmDesc& g = d[i];
+            // B's N-segments must hold whole tiles; so must C's, except for fp32 outputs
+            // (their epilogue routes each 8-column item to its segment)
             ok = ok && (g.b_kseg || g.bseg >= (1 << 30) || g.bseg % k.bn == 0) &&
-                 (g.cseg >= (1 << 30) || g.cseg % k.bn == 0);
+                 (g.cseg >= (1 << 30) || g.cseg % k.bn == 0 || g.out_f32);
             t += (int64_t)((g.M + k.bm - 1) / k.bm) * ((g.N + k.bn - 1) / k.bn);
         }
         if (!ok) continue;
@@ -1195,8 +1210,8 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
             const int64_t tpc = (t * split + 255) / 256;  // tiles per CU
             const int64_t o = tpc < k.occ ? tpc : k.occ;
             const double kper = (double)((kmax + split - 1) / split);
-            const double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + kov / o) / k.eff *
-                                (split > 1 ? 1.04 : 1.0);
+            double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + kov / o) / k.eff;
+            if (split > 1) cost += RED_PER_ELEM * (double)b.pslab + RED_FIXED;
             if (cost < best_cost) { best_cost = cost; best = c; best_split = split; }
         }
     }
