@@ -19,6 +19,7 @@ Usage:
   python -m tensor_transformer_layer_02_amd.profiling traffic FETCH_DIR WRITE_DIR CFETCH_DIR CWRITE_DIR OUT
   python -m tensor_transformer_layer_02_amd.profiling durations TRACE_DIR OUT
   python -m tensor_transformer_layer_02_amd.profiling counters OUT PMC_DIR [PMC_DIR ...]
+  python -m tensor_transformer_layer_02_amd.profiling stats TRACE_DIR OUT TITLE COMMAND NOTE
 """
 from __future__ import annotations
 
@@ -31,16 +32,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # (step, kernel-name patterns in the order the steps are enqueued, either
-# stream); "zero*" is any number of zero-fill launches (outputs of a K-split
-# GEMM).
+# stream); "add*" is any number of reduction launches (the second half of a
+# K-split GEMM added into its outputs).
 STEP_ORDER = [
     ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gemm"]), ("ATTN_CORE", ["attn_fwd"]),
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
-    ("MLP_DW", ["zero*", "gemm"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
+    ("MLP_DW", ["gemm", "add*"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
     ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
-    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["zero*", "gemm"]),
+    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["gemm", "add*"]),
 ]
-KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "zero": ("zero_f32_2d",),
+KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "add": ("add_f32_2d",),
         "colsum_partial": ("colsum_partial",), "colsum_final": ("colsum_final",), "attn_rowdot": ("attn_rowdot",),
         "attn_bwd_dkdv": ("attn_bwd_dkdv",), "attn_bwd_dq": ("attn_bwd_dq",)}
 
@@ -164,9 +165,9 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
         "# HBM traffic per step launch, layer shard gpt8b (8.3B shape, t = 8, shard 0), bf16 fwd+bwd",
         "# commands (from the repository root, on the GPU host):",
         "#   rocprofv3 --pmc FETCH_SIZE --kernel-trace -d F -o f --output-format csv -- "
-        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-kernel-timing",
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-others --no-kernel-timing",
         "#   rocprofv3 --pmc WRITE_SIZE --kernel-trace -d W -o w --output-format csv -- "
-        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-kernel-timing",
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-others --no-kernel-timing",
         "#   rocprofv3 --pmc FETCH_SIZE --kernel-trace -d CF -o f --output-format csv -- python3 bench.py --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE --kernel-trace -d CW -o w --output-format csv -- python3 bench.py --copy-calibration",
         "#   python -m tensor_transformer_layer_02_amd.profiling traffic F W CF CW <this file>",
@@ -202,7 +203,7 @@ def durations(trace_dir, out):
         "# kernel durations per step, layer shard gpt8b (8.3B shape, t = 8, shard 0), bf16 fwd+bwd",
         "# command (from the repository root, on the GPU host):",
         "#   rocprofv3 --kernel-trace --stats -d T -o kt --output-format csv -- "
-        "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+        "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-others",
         "#   python -m tensor_transformer_layer_02_amd.profiling durations T <this file>",
         f"# steps found in the trace: {len(steps)} (warm-up, timed and hooked passes)",
         f"source_sha256_16 {source_hash()}",
@@ -268,7 +269,7 @@ def counters(out, *dirs):
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         names = sorted({k for e in per.values() for k in e if k not in ("name", "us")})
         lines.append(f"#   rocprofv3 --pmc {' '.join(names)} --kernel-trace -d DIR -o c --output-format csv "
-                     "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-kernel-timing")
+                     "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-others --no-kernel-timing")
         steps = split_steps([(e["name"], e) for k, e in sorted(per.items()) if _ours(e["name"])])
         mf, cu, gui = "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"
         derived = mf in names and cu in names
@@ -295,6 +296,26 @@ def counters(out, *dirs):
         f.write("\n".join(lines + body))
 
 
+def _short(name: str) -> str:
+    """Kernel name without namespaces and the parameter list's struct qualifiers."""
+    for q in ("tp::(anonymous namespace)::", "tp::"):
+        name = name.replace(q, "")
+    return name[5:] if name.startswith("void ") else name
+
+
+def stats(trace_dir, out, title, command, note):
+    """Markdown table of rocprofv3's --stats kernel summary (every kernel of the run)."""
+    rows = _read(_one(trace_dir, "_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics: {title}", "", "Command (from the repository root, on one MI355X):",
+             "", f"    {command}", "", note, "", f"source_sha256_16 {source_hash()}", "",
+             "| calls | avg us | min us | max us | % time | kernel |", "|---:|---:|---:|---:|---:|---|"]
+    for r in rows:
+        lines.append(f"| {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} | `{_short(r['Name'])}` |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) == 7 and sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
@@ -302,5 +323,7 @@ if __name__ == "__main__":
         durations(*sys.argv[2:4])
     elif len(sys.argv) >= 4 and sys.argv[1] == "counters":
         counters(sys.argv[2], *sys.argv[3:])
+    elif len(sys.argv) == 7 and sys.argv[1] == "stats":
+        stats(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
