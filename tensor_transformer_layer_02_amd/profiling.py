@@ -255,8 +255,9 @@ def counters(out, *dirs):
     SQ_VALU_MFMA_BUSY_CYCLES and SQ_BUSY_CU_CYCLES, the matrix-core utilisation
     MFMA-busy / (4 SIMDs x CU-busy cycles) of the busy CUs and cu_busy_GHz = CU-busy /
     (256 CUs x time), which is the clock times the fraction of CUs that are busy (lower than
-    the clock where a launch leaves CUs idle).  Where a run holds GRBM_GUI_ACTIVE (GPU-busy
-    cycles of the dispatch), gui_GHz = GRBM_GUI_ACTIVE / time is the clock itself."""
+    the clock where a launch leaves CUs idle).  GRBM_GUI_ACTIVE is listed raw: it counts the
+    GPU-busy cycles of the whole counter window around a dispatch (summed over the XCDs), which
+    is longer than the kernel, so it gives no clock per kernel."""
     lines = ["# hardware counters per step launch, layer shard gpt8b (8.3B shape, t = 8, shard 0), bf16 fwd+bwd",
              "# commands (from the repository root, on the GPU host), one per counter group:"]
     body = []
@@ -271,11 +272,9 @@ def counters(out, *dirs):
         lines.append(f"#   rocprofv3 --pmc {' '.join(names)} --kernel-trace -d DIR -o c --output-format csv "
                      "-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-others --no-kernel-timing")
         steps = split_steps([(e["name"], e) for k, e in sorted(per.items()) if _ours(e["name"])])
-        mf, cu, gui = "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"
+        mf, cu = "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES"
         derived = mf in names and cu in names
-        has_gui = gui in names
-        body.append("# step  kernel_us  " + ("mfma_util  cu_busy_GHz  " if derived else "") +
-                    ("gui_GHz  " if has_gui else "") + "  ".join(names))
+        body.append("# step  kernel_us  " + ("mfma_util  cu_busy_GHz  " if derived else "") + "  ".join(names))
         for step, _ in STEP_ORDER:
             launches = [st[step] for st in steps if step in st]
             if not launches:
@@ -286,8 +285,6 @@ def counters(out, *dirs):
             txt = f"{step:<14} {us:9.2f}  "
             if derived:
                 txt += f"{vals[mf] / (4 * vals[cu]) if vals[cu] else 0.0:9.3f}  {vals[cu] / 256 / us / 1e3:9.2f}  "
-            if has_gui:
-                txt += f"{vals[gui] / us / 1e3:7.2f}  "
             body.append(txt + "  ".join(f"{vals[n]:.4g}" for n in names))
         body.append("")
     lines.append("#   python -m tensor_transformer_layer_02_amd.profiling counters <this file> DIR [DIR ...]")
