@@ -134,7 +134,12 @@ int tp_check_dims(const tp_dims* dims, int shard, int degree);
  *   attention: QKV [T, 3w] (columns [0,w) = Q, [w,2w) = K, [2w,3w) = V of
  *              the shard's heads, w = (H/t)*d, head-local column c of
  *              local head g at g*d + c), O [T, w], LSE [batch, H/t, seq]
- *              fp32 (natural-log log-sum-exp of each query's scaled scores)
+ *              fp32 (natural-log log-sum-exp of each query's scaled scores);
+ *              16-bit path with w a multiple of neither 192 nor 256 only:
+ *              then Wst [h, 3w] and bst [3w], the shard's Wq|Wk|Wv column
+ *              slices and bq|bk|bv side by side (a staging copy the forward
+ *              makes so that its QKV GEMM takes wide tiles; not read by the
+ *              backward)
  * Returns 0 if the dims are invalid.
  */
 size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree);

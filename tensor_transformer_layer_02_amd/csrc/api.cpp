@@ -104,14 +104,23 @@ MlpSaved mlp_saved(const Shape& s) {
     return {0, u, 2 * u};
 }
 
+// Where a tile 192 or 256 columns wide does not fit a Q|K|V segment (w = H/t d
+// a multiple of neither), the QKV GEMM would be held to narrow tiles (its B loader
+// takes one segment per tile); the forward then first copies the three weight
+// slices [h, w] (and biases) side by side into a staging region of `saved`, and
+// the GEMM reads one contiguous [h, 3w] operand.
+bool qkv_staged(const Shape& s) { return s.h16 && s.w % 192 != 0 && s.w % 256 != 0; }
+
 struct AttnSaved {
-    int64_t QKV, O, LSE, total;
+    int64_t QKV, O, LSE, Wst, bst, total;
 };
 AttnSaved attn_saved(const Shape& s) {
     const int64_t q = align256(s.T * 3 * s.w * s.e);
     const int64_t o = align256(s.T * s.w * s.e);
     const int64_t l = align256(s.b * s.Hs * s.s * 4);
-    return {0, q, q + o, q + o + l};
+    const int64_t w = qkv_staged(s) ? align256(s.h * 3 * s.w * s.e) : 0;
+    const int64_t b = qkv_staged(s) ? align256(3 * s.w * s.e) : 0;
+    return {0, q, q + o, q + o + l, q + o + l + w, q + o + l + w + b};
 }
 
 // Work buffers.  `part` (fp32, 16-bit path only) takes the second K half's partial
@@ -300,15 +309,37 @@ hipError_t attn_fwd_saved(const Shape& s, const void* X, const void* Wq, const v
     g.A = X; g.lda = s.h; g.a_kcontig = true;
     const void* W3[3] = {Wq, Wk, Wv};
     const void* b3[3] = {bq, bk, bv};
+    const void* Ws[3];
+    const void* bs[3];
     for (int z = 0; z < 3; ++z) {
-        g.B[z] = at(W3[z], col0, s.e);
-        g.C[z] = at(QKV, z * s.w, s.e);
-        g.bias[z] = b3[z] ? at(b3[z], col0, s.e) : nullptr;
+        Ws[z] = at(W3[z], col0, s.e);
+        bs[z] = b3[z] ? at(b3[z], col0, s.e) : nullptr;
     }
-    g.ldb = s.h; g.b_kcontig = false; g.bseg = (int)s.w;
-    g.ldc = 3 * s.w; g.cseg = (int)s.w;
+    g.b_kcontig = false;
     g.epi = tp::EPI_BIAS;
-    hipError_t e = gemm(s, g, st, TP_STEP_QKV);
+    hipError_t e;
+    {
+        StepTimer qt(TP_STEP_QKV, st);  // the staging copy counts with the GEMM
+        if (qkv_staged(s)) {  // one [h, 3w] operand, one [3w] bias, one output block
+            void* Wst = at(saved, L.Wst, 1);
+            void* bst = at(saved, L.bst, 1);
+            const bool any_bias = bs[0] || bs[1] || bs[2];
+            e = tp::gather3(Ws, s.h, s.h, s.w, Wst, bs, any_bias ? bst : nullptr, st);
+            if (e != hipSuccess) return e;
+            g.B[0] = Wst; g.ldb = 3 * s.w;
+            g.C[0] = QKV; g.ldc = 3 * s.w;
+            g.bias[0] = any_bias ? bst : nullptr;
+        } else {
+            for (int z = 0; z < 3; ++z) {
+                g.B[z] = Ws[z];
+                g.C[z] = at(QKV, z * s.w, s.e);
+                g.bias[z] = bs[z];
+            }
+            g.ldb = s.h; g.bseg = (int)s.w;
+            g.ldc = 3 * s.w; g.cseg = (int)s.w;
+        }
+        e = s.h16 ? tp::gemm_bf16(fmt_of(s, g), st) : tp::gemm_f32(g, st);
+    }
     if (e != hipSuccess) return e;
     tp::AttnDesc ad;
     ad.batch = (int)s.b; ad.seq = (int)s.s; ad.heads = (int)s.Hs; ad.dh = (int)s.d; ad.causal = s.causal;

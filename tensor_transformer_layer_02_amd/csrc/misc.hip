@@ -135,6 +135,48 @@ hipError_t colsum(int fmt, const void* X, int64_t rows, int64_t cols, int64_t ld
     return hipGetLastError();
 }
 
+struct Gather3 {
+    const u32x4* src[3];
+    const u32x4* bsrc[3];
+    int64_t lds8, rows, w8;  // row stride and width in 8-element (16-byte) units
+    u32x4* dst;
+    u32x4* bdst;
+};
+
+// One 16-byte item per thread and step: rows first, then the bias row.
+__global__ void __launch_bounds__(256) gather3_kernel(const Gather3 g) {
+    const int64_t per_row = 3 * g.w8, n = g.rows * per_row + (g.bdst ? per_row : 0);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / per_row, c = i % per_row;
+        const int z = (int)(c / g.w8);
+        const int64_t cc = c - z * g.w8;
+        if (r < g.rows) {
+            g.dst[r * per_row + c] = g.src[z][r * g.lds8 + cc];
+        } else {
+            g.bdst[c] = g.bsrc[z] ? g.bsrc[z][cc] : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+hipError_t gather3(const void* const* src, int64_t lds, int64_t rows, int64_t w, void* dst,
+                   const void* const* bsrc, void* bdst, hipStream_t s) {
+    if (rows <= 0 || w <= 0 || w % 8 || lds % 8) return hipErrorInvalidValue;
+    Gather3 g;
+    for (int z = 0; z < 3; ++z) {
+        g.src[z] = static_cast<const u32x4*>(src[z]);
+        g.bsrc[z] = bsrc ? static_cast<const u32x4*>(bsrc[z]) : nullptr;
+    }
+    g.lds8 = lds / 8;
+    g.rows = rows;
+    g.w8 = w / 8;
+    g.dst = static_cast<u32x4*>(dst);
+    g.bdst = static_cast<u32x4*>(bdst);
+    const int64_t n = (rows + 1) * 3 * g.w8, blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(gather3_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, g);
+    count_launch();
+    return hipGetLastError();
+}
+
 hipError_t add_f32_2d(float* const* dst, const float* const* src, const int64_t* rows, const int64_t* cols,
                       const int64_t* ld, const int64_t* lds, int n, hipStream_t s) {
     if (n < 0 || n > ZMAX) return hipErrorInvalidValue;

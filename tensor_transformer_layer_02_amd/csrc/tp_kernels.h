@@ -79,6 +79,12 @@ struct AddRegions {
 };
 hipError_t add_f32_2d(float* const* dst, const float* const* src, const int64_t* rows, const int64_t* cols,
                       const int64_t* ld, const int64_t* lds, int n, hipStream_t s);
+// 16-bit gather of three column blocks side by side: dst[r][z w + c] =
+// src[z][r lds + c] for r < rows, c < w (z = 0, 1, 2), and, when bdst is set,
+// bdst[z w + c] = bsrc[z][c] (0 where bsrc[z] is null).  w and lds multiples of 8,
+// pointers 16-byte aligned.
+hipError_t gather3(const void* const* src, int64_t lds, int64_t rows, int64_t w, void* dst,
+                   const void* const* bsrc, void* bdst, hipStream_t s);
 // fp32 operands and outputs, fp32 FMA arithmetic.
 hipError_t gemm_f32(const GemmDesc& d, hipStream_t s);
 

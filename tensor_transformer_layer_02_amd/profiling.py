@@ -32,16 +32,18 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # (step, kernel-name patterns in the order the steps are enqueued, either
-# stream); "add*" is any number of reduction launches (the second half of a
+# stream); "gather*" is the forward's Q|K|V weight-staging copy where it makes one, "add*"
+# any number of reduction launches (the second half of a
 # K-split GEMM added into its outputs).
 STEP_ORDER = [
-    ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gemm"]), ("ATTN_CORE", ["attn_fwd"]),
+    ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gather*", "gemm"]), ("ATTN_CORE", ["attn_fwd"]),
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
     ("MLP_DW", ["gemm", "add*"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
     ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
     ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["gemm", "add*"]),
 ]
 KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "add": ("add_f32_2d",),
+        "gather": ("gather3",),
         "colsum_partial": ("colsum_partial",), "colsum_final": ("colsum_final",), "attn_rowdot": ("attn_rowdot",),
         "attn_bwd_dkdv": ("attn_bwd_dkdv",), "attn_bwd_dq": ("attn_bwd_dq",)}
 

@@ -79,8 +79,11 @@ def test_saved_and_work_sizes_follow_documented_layout(L):
         T, Fs, w, e = cfg.tokens, cfg.ffn_per_shard, cfg.attn_width, (4 if cfg.dtype == "fp32" else 2)
         a = lambda x: (x + 255) // 256 * 256
         assert tp.tp_mlp_saved_bytes(dims, 0, cfg.degree) == 2 * a(T * Fs * e), name
+        staged = e == 2 and w % 192 != 0 and w % 256 != 0  # Wq|Wk|Wv slices and biases side by side
         assert tp.tp_attn_saved_bytes(dims, 0, cfg.degree) == (a(T * 3 * w * e) + a(T * w * e)
-                                                               + a(cfg.batch * cfg.heads_per_shard * cfg.seq * 4))
+                                                               + a(cfg.batch * cfg.heads_per_shard * cfg.seq * 4)
+                                                               + (a(cfg.hidden * 3 * w * e) + a(3 * w * e)
+                                                                  if staged else 0)), name
         assert tp.tp_mlp_work_bytes(dims, 0, cfg.degree) >= T * Fs * e
         assert tp.tp_attn_work_bytes(dims, 0, cfg.degree) >= 4 * T * w * e
     bad = d(heads=3)
