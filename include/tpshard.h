@@ -146,11 +146,11 @@ size_t tp_mlp_saved_bytes(const tp_dims* dims, int shard, int degree);
 size_t tp_attn_saved_bytes(const tp_dims* dims, int shard, int degree);
 
 /* Bytes of the `work` buffer the backward needs (0 if the dims are invalid):
- * the backward's intermediates (dU; dO and dQKV), column-sum partials and, on
- * the 16-bit path, one fp32 slab the size of the call's weight gradients, which
- * takes the second half's partial sums when the weight-gradient GEMM splits K
- * in two (the halves are then added in one fixed order: results do not depend
- * on timing). */
+ * the backward's intermediates (dU; dO and dQKV), column-sum partials and, for
+ * the FFN on the 16-bit path, one fp32 slab the size of its weight gradients,
+ * which takes the second half's partial sums when the weight-gradient GEMM
+ * splits K in two (the halves are then added in one fixed order: results do not
+ * depend on timing). */
 size_t tp_mlp_work_bytes(const tp_dims* dims, int shard, int degree);
 size_t tp_attn_work_bytes(const tp_dims* dims, int shard, int degree);
 

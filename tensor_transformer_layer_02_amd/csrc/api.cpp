@@ -124,8 +124,9 @@ AttnSaved attn_saved(const Shape& s) {
 }
 
 // Work buffers.  `part` (fp32, 16-bit path only) takes the second K half's partial
-// sums of the weight-gradient launch when it is split in two: one float per weight
-// gradient element of the launch.
+// sums of the FFN weight-gradient launch when it is split in two: one float per
+// weight gradient element of the launch.  (The attention one never splits: the
+// auxiliary stream's launches fill the CUs its tiles leave.)
 struct MlpWork {
     int64_t dU, cs, part, part_floats, total;
 };
@@ -137,16 +138,14 @@ MlpWork mlp_work(const Shape& s) {
 }
 
 struct AttnWork {
-    int64_t dO, dQKV, Dq, cs, part, part_floats, total;
+    int64_t dO, dQKV, Dq, cs, total;
 };
 AttnWork attn_work(const Shape& s) {
     const int64_t dO = align256(s.T * s.w * s.e);
     const int64_t dq = align256(s.T * 3 * s.w * s.e);
     const int64_t D = align256(s.b * s.Hs * s.s * 4);
     const int64_t cs = align256(tp::colsum_work_floats(3 * s.w) * 4);
-    const int64_t pf = s.h16 ? 4 * s.w * s.h : 0;  // dW{q,k,v}_i and dWo_i
-    const int64_t p0 = dO + dq + D + cs;
-    return {0, dO, dO + dq, dO + dq + D, p0, pf, p0 + align256(pf * 4)};
+    return {0, dO, dO + dq, dO + dq + D, dO + dq + D + cs};
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_EHIP; }
@@ -633,10 +632,24 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
             return TP_EHIP;
     }
 
-    // On the auxiliary stream: db{q,k,v}[cols of G_i] = column sums of dQKV, then
-    // dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T, beside the weight-gradient GEMM
-    // (whose tiles leave CUs idle).
+    // One launch on the caller's stream: dW{q,k,v}[:, cols of G_i] = X^T dQKV and dWo (same
+    // layout: transposed operands, fp32 output, K = T; dWo needs only forward outputs, but run
+    // beside dO and the core it took CUs from the core's one-workgroup-per-CU grid).  Its tiles
+    // (without a K split) hold part of the CUs for the whole launch; enqueued before the
+    // auxiliary stream's launches, so that it takes its CUs first, while on the auxiliary stream
+    // db{q,k,v}[cols of G_i] = column sums of dQKV and dX_part = dQKV [Wq|Wk|Wv][:, cols of G_i]^T
+    // run on the rest.
     if (aux.to_aux(st, 0) != hipSuccess) return TP_EHIP;
+    tp::GemmDesc gw[2];
+    tp::GemmDesc& gq = gw[0];
+    gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
+    gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
+    gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
+    float* dW3[3] = {dWq, dWk, dWv};
+    for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
+    gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
+    gw[1] = go;
+    if (gemm2(s, gw, nullptr, 0, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
     if (bias_grads) {
         float* outs[3] = {dbq + col0, dbk + col0, dbv + col0};
         StepTimer t(TP_STEP_ATTN_DBIAS, aux.a->st);
@@ -651,21 +664,6 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     gx.ldb = s.h; gx.b_kcontig = true; gx.b_kseg = true; gx.bseg = (int)s.w;
     gx.C[0] = dX_part; gx.ldc = s.h;
     if (gemm(s, gx, aux.a->st, TP_STEP_ATTN_DX) != hipSuccess) return TP_EHIP;
-
-    // One launch: dW{q,k,v}[:, cols of G_i] = X^T dQKV and dWo (same layout: transposed
-    // operands, fp32 output, K = T).  dWo needs only forward outputs, but running it beside the
-    // attention core took CUs from the core's one-workgroup-per-CU grid and slowed both.
-    tp::GemmDesc gw[2];
-    tp::GemmDesc& gq = gw[0];
-    gq.M = (int)s.h; gq.N = (int)(3 * s.w); gq.K = (int)s.T;
-    gq.A = X; gq.lda = s.h; gq.a_kcontig = false;
-    gq.B[0] = dQKV; gq.ldb = 3 * s.w; gq.b_kcontig = false;
-    float* dW3[3] = {dWq, dWk, dWv};
-    for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
-    gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
-    gw[1] = go;
-    if (gemm2(s, gw, static_cast<float*>(at(work, W.part, 1)), W.part_floats, st, TP_STEP_ATTN_DW) != hipSuccess)
-        return TP_EHIP;
     return aux.to_main(st, 1) != hipSuccess ? TP_EHIP : TP_OK;
 }
 
