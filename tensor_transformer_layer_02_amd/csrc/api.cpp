@@ -648,6 +648,7 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     float* dW3[3] = {dWq, dWk, dWv};
     for (int z = 0; z < 3; ++z) gq.C[z] = dW3[z] + col0;
     gq.ldc = s.h; gq.cseg = (int)s.w; gq.out_f32 = true;
+    gq.cus = 128;  // tiles for half the CUs (the K-group tile at the 8.3B and BERT shapes)
     gw[1] = go;
     if (gemm2(s, gw, nullptr, 0, st, TP_STEP_ATTN_DW) != hipSuccess) return TP_EHIP;
     if (bias_grads) {

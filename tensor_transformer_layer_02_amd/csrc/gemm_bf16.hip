@@ -1149,7 +1149,8 @@ void gemm_force_tile(int tile, int ksplit) {
 
 int gemm_tile_count() { return (int)(sizeof(kCands) / sizeof(kCands[0])); }
 
-// Tile shape (and K split) with the least estimated time on 256 CUs.  A CU
+// Tile shape (and K split) with the least estimated time on 256 CUs (or the
+// share `cus` of them the launch is given beside other work).  A CU
 // gets ceil(items / 256) tiles and runs o = min(occupancy, that) of them at
 // once; each costs BM * BN * (K per split + overhead / o) / efficiency, the
 // overhead (prologue and epilogue, larger with GeLU math) being hidden by the
@@ -1183,12 +1184,10 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
     const double kov = (d[0].epi == EPI_BIAS_GELU || d[0].epi == EPI_GELU_BWD) ? K_OVERHEAD_GELU : K_OVERHEAD;
     const int ncand = (int)(sizeof(kCands) / sizeof(kCands[0]));
     const bool forced = g_force_tile >= 0 && g_force_tile < ncand;
+    const int cus = d[0].cus > 0 && d[0].cus < 256 ? d[0].cus : 256;
     for (int c = 0; c < ncand; ++c) {
         const Cand& k = kCands[c];
         if (k.f32_tn_only && !tn32) continue;
-        // The 8-wave tiles take a whole CU's registers; beside another launch the
-        // co-resident 4-wave tiles do better (attention dX beside dWqkv: +1% per step).
-        if ((c == 8 || c == 9) && d[0].concurrent && !forced) continue;
         bool ok = true;
         int64_t t = 0;
         for (int i = 0; i < n; ++i) {
@@ -1207,7 +1206,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
             break;
         }
         for (int split = 1; split <= ((allow_split && tn32) ? 2 : 1); ++split) {
-            const int64_t tpc = (t * split + 255) / 256;  // tiles per CU
+            const int64_t tpc = (t * split + cus - 1) / cus;  // tiles per CU
             const int64_t o = tpc < k.occ ? tpc : k.occ;
             const double kper = (double)((kmax + split - 1) / split);
             double cost = (double)((tpc + o - 1) / o) * o * k.bm * k.bn * (kper + kov / o) / k.eff;

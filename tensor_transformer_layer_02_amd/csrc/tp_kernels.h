@@ -48,7 +48,8 @@ struct GemmDesc {
     int64_t ldaux = 0;
     int epi = EPI_STORE;
     bool gelu_tanh = false;       // EPI_BIAS_GELU / EPI_GELU_BWD: the tanh form of GeLU
-    bool concurrent = false;      // runs beside another launch (tile choice: co-resident tiles)
+    int cus = 0;                  // CUs the tile choice may count on (0: all 256); a launch that
+                                  // shares the GPU with another stream's work plans for its share
     bool fp16 = false;            // 16-bit operands / outputs are IEEE half (else bfloat16)
 };
 

@@ -40,7 +40,7 @@ STEP_ORDER = [
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
     ("MLP_DW", ["gemm", "add*"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
     ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq"]),
-    ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]), ("ATTN_DW", ["gemm", "add*"]),
+    ("ATTN_DW", ["gemm", "add*"]), ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]),
 ]
 KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "add": ("add_f32_2d",),
         "gather": ("gather3",),
