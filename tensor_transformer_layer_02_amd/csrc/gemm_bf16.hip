@@ -268,15 +268,18 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs; the
-// first step makes the ids each XCD receives contiguous, the second walks the
-// tiles in groups of GM tile-rows so that an XCD's tiles share A rows and B
-// columns in its L2.
-__device__ __forceinline__ void tile_of(int b, int mt, int nt, int& mtile, int& ntile) {
-    constexpr int GM = 8;
-    const int nwg = mt * nt;
+// Workgroup -> tile, in two steps.  Workgroups are dealt round-robin to the 8
+// XCDs; xcd_id makes the ids each XCD receives contiguous over all the tiles of
+// a launch (so with two problems each XCD works on one of them, or on the end of
+// one and the start of the other), and tile_of walks a problem's tiles in groups
+// of GM tile-rows so that an XCD's tiles share A rows and B columns in its L2.
+__device__ __forceinline__ int xcd_id(int b, int nwg) {
     const int per = (nwg + 7) / 8, r = nwg % 8, x = b % 8, q = b / 8;
-    const int id = (r == 0 || x < r) ? x * per + q : r * per + (x - r) * (per - 1) + q;
+    return (r == 0 || x < r) ? x * per + q : r * per + (x - r) * (per - 1) + q;
+}
+
+__device__ __forceinline__ void tile_of(int id, int mt, int nt, int& mtile, int& ntile) {
+    constexpr int GM = 8;
     const int gsize = GM * nt;
     const int first_m = (id / gsize) * GM;
     const int gm = min(mt - first_m, GM);
@@ -839,7 +842,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const bool epi_wave = wave < NWV / KG;  // the waves that hold the final sums
     // workgroup -> (K split, problem, tile)
     const int split = (int)blockIdx.x / batch.tiles;
-    int t = (int)blockIdx.x - split * batch.tiles;
+    int t = xcd_id((int)blockIdx.x - split * batch.tiles, batch.tiles);
     const int prob = (batch.n > 1 && t >= batch.tiles0) ? 1 : 0;
     if (prob) t -= batch.tiles0;
     const GemmArgs& p = batch.g[prob];
