@@ -199,7 +199,11 @@ inline hipError_t gemm(const Shape& s, const tp::GemmDesc& g, hipStream_t st, in
 // everything enqueued on it (k: one of the call's events, each used once per
 // call).  The lock is held from the first to the last of these in one call,
 // so the shared events are never re-recorded by another host thread in
-// between.
+// between.  The events only order the two streams (nothing waits for them on
+// the host), and every kernel launch already carries the acquire and release
+// fences that make one kernel's writes visible to the next on the device, so
+// they are created without the system-scope fence a recorded event otherwise
+// adds (a cache write-back and invalidation at each fork and join).
 constexpr int AUX_EVENTS = 6;
 struct Aux {
     hipStream_t st = nullptr;
@@ -228,7 +232,7 @@ struct AuxScope {
                 hipEvent_t ev[AUX_EVENTS] = {};
                 if ((err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return;
                 for (int k = 0; k < AUX_EVENTS && err == hipSuccess; ++k)
-                    err = hipEventCreateWithFlags(&ev[k], hipEventDisableTiming);
+                    err = hipEventCreateWithFlags(&ev[k], hipEventDisableTiming | hipEventDisableSystemFence);
                 if (err != hipSuccess) {
                     for (int k = 0; k < AUX_EVENTS; ++k)
                         if (ev[k]) hipEventDestroy(ev[k]);
