@@ -628,11 +628,13 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     auto core = [&](int part, hipStream_t q) {
         return s.h16 ? tp::attn_bwd_bf16(ad, part, q) : tp::attn_bwd_f32(ad, part, q);
     };
-    {   // D = rowsum(dO * O), the dK/dV pass, the dQ pass (running the last two
-        // concurrently measured slower: their workgroups compete for the same CUs)
+    {   // D = rowsum(dO * O), then the dK/dV and dQ passes: on the 16-bit path as one
+        // launch, the dQ workgroups queued behind the dK/dV ones (on two streams side by
+        // side they measured slower: their workgroups compete for the same CUs)
         StepTimer t(TP_STEP_ATTN_CORE_BWD, st);
-        if (core(tp::ATTN_BWD_ROWDOT, st) != hipSuccess || core(tp::ATTN_BWD_DKDV, st) != hipSuccess ||
-            core(tp::ATTN_BWD_DQ, st) != hipSuccess)
+        if (core(tp::ATTN_BWD_ROWDOT, st) != hipSuccess) return TP_EHIP;
+        if (s.h16 ? core(tp::ATTN_BWD_DKDV_DQ, st) != hipSuccess
+                  : (core(tp::ATTN_BWD_DKDV, st) != hipSuccess || core(tp::ATTN_BWD_DQ, st) != hipSuccess))
             return TP_EHIP;
     }
 

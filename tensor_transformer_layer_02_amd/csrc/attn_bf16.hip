@@ -257,13 +257,14 @@ __device__ __forceinline__ void store_rowT(bf16_t* __restrict__ row, const f32x1
 // by linear id; this numbering gives each XCD a contiguous range of (bh, x), so the
 // pair workgroups of one (sequence, head) run on one XCD and share its L2 for that
 // head's Q, K, V and dO (dealt over all XCDs, every L2 would hold every head).
-__device__ __forceinline__ void xcd_map(int& x, int& bh) {
-    const int nx = (int)gridDim.x, n = (int)(gridDim.x * gridDim.y);
-    const int L = (int)(blockIdx.x + blockIdx.y * gridDim.x);
+__device__ __forceinline__ void xcd_map_n(int L, int n, int nx, int& x, int& bh) {
     const int per = (n + 7) / 8, r = n % 8, xc = L % 8, q = L / 8;
     const int id = (r == 0 || xc < r) ? xc * per + q : r * per + (xc - r) * (per - 1) + q;
     x = id % nx;
     bh = id / nx;
+}
+__device__ __forceinline__ void xcd_map(int& x, int& bh) {
+    xcd_map_n((int)(blockIdx.x + blockIdx.y * gridDim.x), (int)(gridDim.x * gridDim.y), (int)gridDim.x, x, bh);
 }
 
 // Rows of a forward / dQ workgroup: the 64-row blocks x and nb-1-x of the
@@ -637,27 +638,32 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
 // each pair), halves added q0 + q1; larger heads without a mask take the
 // one-block-at-a-time form, whose registers fit.  Q and dO pairs go straight into LDS (two stages), the LSE and D
 // of their queries through registers.  Deterministic either way.
-template <int D, typename ST, bool NOMASK>
-__global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
-    constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
-    constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for four groups
+// LDS of the dK/dV pass.
+template <int D>
+struct DkdvLds {
+    static constexpr int TILE = BKV * D * 2, DB = D / 32;
+    static constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
+    static constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for four groups
     // PRE: the K and V tiles of both key blocks come into LDS once, at the start
     // (the fragments of a key group are then read from LDS by each of the four
     // waves that use them, instead of four times from memory), where they fit
     // beside the two stages (up to d = 96).
-    constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
-    constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
-    constexpr int SMEM = REG > MERGE ? REG : MERGE;
+    static constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
+    static constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
+    static constexpr int SMEM = REG > MERGE ? REG : MERGE;
+};
+
+template <int D, typename ST, bool NOMASK>
+__device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ smem, int x, int bh) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = DkdvLds<D>::TILE;
+    constexpr int SLOT = DkdvLds<D>::SLOT, MERGE = DkdvLds<D>::MERGE;
+    constexpr bool PRE = DkdvLds<D>::PRE;
     constexpr int PITCH = D * 2 + 16;  // row pitch of the bf16 dK / dV image (rows 4 apart on other banks)
     static_assert(2 * BKV * PITCH <= SLOT && MERGE <= SLOT, "epilogue areas fit one stage");
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: derived conditions are scalar branches
     const int s = a.seq;
-    int x, bh;
-    xcd_map(x, bh);
     const int nb = (s + BKV - 1) / BKV, xl = nb - 1 - x;
     const bool side = NOMASK && xl != x;  // both key blocks over one query stream
     const int kg2 = wave & 1, qq = side ? 2 * (wave >> 2) : wave >> 1;
@@ -900,25 +906,30 @@ __device__ __forceinline__ void dq_rows(bool masked, int ph, int x, int xl, int 
 // see every key, so they run side by side over one stream (the forward's
 // layout: the two waves of a row group take alternate 64-key blocks of each
 // pair), halves added k0 + k1.  Deterministic either way.
-template <int D, typename ST, bool MASKED>
-__global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
-    constexpr int KC = D / 16, DB = D / 32, PT = 2 * BKV * D * 2, TILE = BKV * D * 2;
-    constexpr int SLOT = 2 * PT;  // K pair, V pair
-    constexpr int MERGE = DB * 16 * 4 * 64 * 4;
+// LDS of the dQ pass.
+template <int D>
+struct DqLds {
+    static constexpr int TILE = BKV * D * 2, PT = 2 * BKV * D * 2, DB = D / 32;
+    static constexpr int SLOT = 2 * PT;  // K pair, V pair
+    static constexpr int MERGE = DB * 16 * 4 * 64 * 4;
     // PRE: the Q and dO tiles of both query blocks come into LDS once, at the start
     // (each is read by the four waves that share those queries), where they fit
     // beside the two stages (up to d = 96).
-    constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
-    constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
-    constexpr int SMEM = REG > MERGE ? REG : MERGE;
+    static constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
+    static constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
+    static constexpr int SMEM = REG > MERGE ? REG : MERGE;
+};
+
+template <int D, typename ST, bool MASKED>
+__device__ __forceinline__ void dq_body(const AttnArgs& a, char* __restrict__ smem, int x, int bh) {
+    constexpr int KC = D / 16, DB = D / 32, PT = DqLds<D>::PT, TILE = DqLds<D>::TILE;
+    constexpr int SLOT = DqLds<D>::SLOT, MERGE = DqLds<D>::MERGE;
+    constexpr bool PRE = DqLds<D>::PRE;
     static_assert(MERGE <= SLOT, "the merge area fits one stage");
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: derived conditions are scalar branches
     const int s = a.seq;
-    int x, bh;
-    xcd_map(x, bh);
     const int nb = (s + BKV - 1) / BKV, xl = nb - 1 - x;
     const int b = bh / a.heads, g = bh % a.heads;
     const PairRows pr(x, s, wave, a.causal);  // the side-by-side layout (no mask)
@@ -1045,6 +1056,43 @@ __global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
     }
 }
 
+template <int D, typename ST, bool NOMASK>
+__global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_kernel(const AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[DkdvLds<D>::SMEM];
+    int x, bh;
+    xcd_map(x, bh);
+    dkdv_body<D, ST, NOMASK>(a, smem, x, bh);
+}
+
+template <int D, typename ST, bool MASKED>
+__global__ void __launch_bounds__(NT8, 1) attn_bwd_dq_kernel(const AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[DqLds<D>::SMEM];
+    int x, bh;
+    xcd_map(x, bh);
+    dq_body<D, ST, MASKED>(a, smem, x, bh);
+}
+
+// The dK/dV and dQ passes (independent of each other) as one launch: grid rows
+// 0 .. bh-1 are the dK/dV workgroups, the rest the dQ ones, numbered for the
+// XCDs as two grids of their own.  The dK/dV workgroups come first in dispatch
+// order; a dQ workgroup starts on a CU as soon as a dK/dV one leaves it, with no
+// kernel boundary in between.
+template <int D, typename ST, bool NOMASK, bool MASKED>
+__global__ void __launch_bounds__(NT8, 1) attn_bwd_dkdv_dq_kernel(const AttnArgs a) {
+    constexpr int SM = DkdvLds<D>::SMEM > DqLds<D>::SMEM ? DkdvLds<D>::SMEM : DqLds<D>::SMEM;
+    __shared__ __attribute__((aligned(1024))) char smem[SM];
+    const int nx = (int)gridDim.x, n = (int)(gridDim.x * gridDim.y) / 2;
+    const int L = (int)(blockIdx.x + blockIdx.y * gridDim.x);
+    int x, bh;
+    if (L < n) {
+        xcd_map_n(L, n, nx, x, bh);
+        dkdv_body<D, ST, NOMASK>(a, smem, x, bh);
+    } else {
+        xcd_map_n(L - n, n, nx, x, bh);
+        dq_body<D, ST, MASKED>(a, smem, x, bh);
+    }
+}
+
 AttnArgs make_args(const AttnDesc& d) {
     AttnArgs a;
     a.batch = d.batch; a.seq = d.seq; a.heads = d.heads; a.causal = d.causal;
@@ -1092,6 +1140,21 @@ hipError_t bwd_d(const AttnArgs& a, int part, hipStream_t s) {
             hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST, true>), grid_pair, dim3(NT8), 0, s, a);
         else
             hipLaunchKernelGGL((attn_bwd_dq_kernel<D, ST, false>), grid_pair, dim3(NT8), 0, s, a);
+    } else if (part == ATTN_BWD_DKDV_DQ) {
+        const dim3 grid2(grid_pair.x, 2 * grid_pair.y);
+        bool side = false;  // the side-by-side dK/dV form (unmasked, up to d = 64, as above)
+        if constexpr (D <= 64) {
+            if (!a.causal) {
+                hipLaunchKernelGGL((attn_bwd_dkdv_dq_kernel<D, ST, true, false>), grid2, dim3(NT8), 0, s, a);
+                side = true;
+            }
+        }
+        if (!side) {
+            if (a.causal)
+                hipLaunchKernelGGL((attn_bwd_dkdv_dq_kernel<D, ST, false, true>), grid2, dim3(NT8), 0, s, a);
+            else
+                hipLaunchKernelGGL((attn_bwd_dkdv_dq_kernel<D, ST, false, false>), grid2, dim3(NT8), 0, s, a);
+        }
     }
     else
         return hipErrorInvalidValue;

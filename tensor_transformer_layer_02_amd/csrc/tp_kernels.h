@@ -107,7 +107,8 @@ struct AttnDesc {
 
 // The backward is three launches: D = rowsum(dO * O) first, then the dK/dV
 // and dQ passes, which are independent of each other (both read D).
-enum AttnBwdPart { ATTN_BWD_ROWDOT = 0, ATTN_BWD_DKDV = 1, ATTN_BWD_DQ = 2 };
+// ATTN_BWD_DKDV_DQ runs the last two as one launch (16-bit storage only).
+enum AttnBwdPart { ATTN_BWD_ROWDOT = 0, ATTN_BWD_DKDV = 1, ATTN_BWD_DQ = 2, ATTN_BWD_DKDV_DQ = 3 };
 hipError_t attn_fwd_bf16(const AttnDesc& a, hipStream_t s);
 hipError_t attn_bwd_bf16(const AttnDesc& a, int part, hipStream_t s);
 hipError_t attn_fwd_f32(const AttnDesc& a, hipStream_t s);
