@@ -861,7 +861,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     if constexpr (KG == 2) {
         // the second K group adds its partial sums into the first's, one 32-column
         // block of the wave tile at a time (fixed order: deterministic)
-        static_assert(OUTF32, "the K-group split serves the fp32 weight gradients");
+        static_assert(OUTF32 || EPI == EPI_STORE, "the K-group split serves plain stores");
         float* mg = reinterpret_cast<float*>(smem);
         const int wl = wave % 4, g = wave / 4;
 #pragma unroll
@@ -895,7 +895,7 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const int csg = n0 / p.cseg;
     const int cofs = csg * p.cseg;
     const int rows = p.M - m0, ncols = p.N - n0;  // valid extent of the tile
-    static_assert(F32STAGE || KG == 1, "bf16 epilogues assume every thread holds final sums");
+    static_assert(F32STAGE || KG == 1 || EPI == EPI_STORE, "bf16 epilogues with K groups: plain stores only");
     if constexpr (!F32STAGE) {
         // Bias on the accumulators; the output image goes through LDS once.  With
         // GeLU, Gp = GeLU'(U) (saved for the backward, which needs only that of U)
@@ -922,9 +922,10 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                 store_bf16<CR, BN, SP, NT, WTM>(smem + CR * SP, C2, p.ldc2, rows, ncols, tid, i * 32);
             }
         } else {
-            stage_bf16<ST, FM, FN, WTM, WTN, SP>(smem, acc, bias, ncols, wm, wn, lane);
+            // with K groups only the first group holds the sums; every thread stores
+            if (epi_wave) stage_bf16<ST, FM, FN, WTM, WTN, SP>(smem, acc, bias, ncols, wm, wn, lane);
             __syncthreads();
-            store_bf16<BM, BN, SP, NT>(smem, C, p.ldc, rows, ncols, tid);
+            store_bf16<BM, BN, SP, 64 * NWV>(smem, C, p.ldc, rows, ncols, tid);
         }
     } else {
         // fp32 staging, half a tile (the rows of wave rows wm / HR == half) at a time,
@@ -1107,11 +1108,15 @@ struct Cand {
 // Index 8 is the 256 x 192 tile with 8 waves (two per SIMD): 3-16% faster than
 // with 4 waves on the same tile in a shape sweep.  Index 9 is the 192 x 192
 // fp32 weight-gradient tile with 8 waves in two K groups: 4-6% faster than its
-// 4-wave form on the MLP weight-gradient pair.
+// 4-wave form on the MLP weight-gradient pair.  Index 10 is the 64 x 192 tile
+// with 8 waves in two K groups, for plain 16-bit stores of K-contiguous
+// operands where one round of its tiles fills the CUs (dO: N = w, K = h):
+// against the 4-wave 64 x 192 tile, one workgroup per CU either way, it puts
+// two waves on each SIMD (dO 29.7 against 33.8 us at the 8.3B shape).
 const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
                        {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
                        {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false},
-                       {192, 192, 1, 0.975, true}};
+                       {192, 192, 1, 0.975, true}, {64, 192, 1, 0.80, false}};
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
 // The K split's reduction kernel in the same units (a CU's MACs at ~2.2 M per us):
 // three fp32 passes over the outputs at ~5 TB/s, plus a launch (~3 us).
@@ -1131,9 +1136,13 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
         case 6: return dispatch<64, 64, 4, ST>(d, b, s);
         case 7: return dispatch<128, 192, 4, ST>(d, b, s);
         case 8: return dispatch<256, 192, 8, ST>(d, b, s);
-        default:  // 9: fp32 weight gradients only
+        case 9:  // fp32 weight gradients only
             if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
                 return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2, ST>(b, s);
+            return hipErrorInvalidValue;
+        default:  // 10: K-contiguous operands, plain 16-bit stores only
+            if (d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 && d.epi == EPI_STORE)
+                return launch<64, 192, 8, true, true, false, EPI_STORE, false, 2, ST>(b, s);
             return hipErrorInvalidValue;
     }
 }
@@ -1180,6 +1189,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
     if (b.n == 0) return hipSuccess;
     const bool allow_split = part && part_floats >= b.pslab && (reinterpret_cast<uintptr_t>(part) & 15u) == 0;
     const bool tn32 = !d[0].a_kcontig && !d[0].b_kcontig && !d[0].b_kseg && d[0].out_f32;
+    const bool nt16 = d[0].a_kcontig && d[0].b_kcontig && !d[0].b_kseg && !d[0].out_f32 && d[0].epi == EPI_STORE;
     int best = -1, best_split = 1;
     double best_cost = 1e300;
     int kmax = 0;
@@ -1202,6 +1212,9 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
             t += (int64_t)((g.M + k.bm - 1) / k.bm) * ((g.N + k.bn - 1) / k.bn);
         }
         if (!ok) continue;
+        // the 8-wave K-group 64 x 192 tile: plain 16-bit stores of K-contiguous operands,
+        // where its tiles fill the CUs in one round (small N, long K)
+        if (c == 10 && (!nt16 || t > cus)) continue;
         if (forced && c == g_force_tile) {  // test hook: this tile wherever it is valid
             best = c;
             best_split = (g_force_split == 2 && allow_split && tn32) ? 2 : 1;

@@ -2,7 +2,9 @@
 
 The GEMMs pick a tile shape (and, for the fp32 weight gradients, a K split) with a cost model;
 at full size most of the shard runs on the 8-wave tiles, whose operand pipelines load global
-memory straight into LDS and handle the K range in rounds of six steps plus a tail.  At small
+memory straight into LDS and handle the K range in rounds of six steps plus a tail (in rounds
+of three for the two K-group tiles: the 192 x 192 fp32 weight-gradient one and the 64 x 192
+one for plain 16-bit stores, dO and the FFN's dX at these sizes).  At small
 sizes the model picks other tiles, so these tests force each tile in turn (the library's test
 hook tp_test_force_gemm_tile; every GEMM the tile is valid for uses it) and check every output
 of every shard against the float64 oracle.  The shapes make M, N and K ragged for every tile,
@@ -25,7 +27,7 @@ CASES = [
     ("T185_h640_d64_t1", 5, 37, 640, 10, 896, 1, False),
     ("T257_h1728_d96_t3", 1, 257, 1728, 18, 4608, 3, True),   # w = 576: the 192-wide tiles fit Q|K|V
 ]
-NTILES = 10
+NTILES = 11
 
 
 @pytest.mark.parametrize("ksplit", [1, 2])

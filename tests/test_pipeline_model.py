@@ -12,9 +12,10 @@ still outstanding.
   B(k+3) into the same set; then vmcnt(LA + 2 LB) lgkmcnt(0), barrier, and the first
   fragment read of step k+1.  Whole rounds of six steps (the slot pattern repeats every
   six), then a tail of 0..5 steps.
-* KG2 (the 8-wave 192 x 192 fp32 weight-gradient tile in two K groups): A and B both
-  straight into three slots, two steps ahead; step k: loads of step k+2, vmcnt(NLD)
-  lgkmcnt(0), barrier; the loop runs whole rounds of three steps.
+* KG2 (the 8-wave tiles in two K groups: 192 x 192 for the fp32 weight gradients,
+  64 x 192 for plain 16-bit stores of K-contiguous operands): A and B both straight into
+  three slots, two steps ahead; step k: loads of step k+2, vmcnt(NLD) lgkmcnt(0),
+  barrier; the loop runs whole rounds of three steps.
 
 The model replays one thread's program order (every thread of the workgroup runs the
 same sequence; a barrier publishes what each of them has completed) for every step count
@@ -227,11 +228,12 @@ def test_adirect_relies_on_order_across_kinds(tile):
     assert v and all(x[0] == "RAW" and x[1][0] == "A" for x in v)
 
 
-def test_kgroup_race_free_per_kind():
+@pytest.mark.parametrize("nld", [6, 4], ids=["192x192 (NLD 6)", "64x192 (NLD 4)"])
+def test_kgroup_race_free_per_kind(nld):
     for nk in STEPS:
         for model in ("in order", "per kind"):
-            assert check(kg2_program(nk, 6), model) == [], (nk, model)
-    assert check(kg2_program(6, 6), "any order")  # the count-based wait needs some order
+            assert check(kg2_program(nk, nld), model) == [], (nk, model)
+    assert check(kg2_program(6, nld), "any order")  # the count-based wait needs some order
 
 
 def test_model_catches_planted_mistakes():
@@ -257,15 +259,17 @@ def _pieces(rows_or_cols, nwv):
     return [(w + nwv * i) * 1024 + 16 * l for w in range(nwv) for i in range(ni) for l in range(64)]
 
 
-@pytest.mark.parametrize("tile", ADIRECT_TILES + [("192x192 w8 kg2", 192, 192, 8, 1)],
-                         ids=[t[0] for t in ADIRECT_TILES] + ["192x192 w8 kg2"])
+KG2_TILES = [("192x192 w8 kg2", 192, 192, 8, 1), ("64x192 w8 kg2", 64, 192, 8, 1)]
+
+
+@pytest.mark.parametrize("tile", ADIRECT_TILES + KG2_TILES, ids=[t[0] for t in ADIRECT_TILES + KG2_TILES])
 def test_slot_layout(tile):
     _, bm, bn, w, occ = tile
     a_bytes, b_bytes = bm * BK * 2, bn * BK * 2
     for n, size in ((bm, a_bytes), (bn, b_bytes)):
         p = sorted(_pieces(n, w))
         assert p == list(range(0, size, 16))  # the slot, each 16 bytes written by exactly one lane
-    if tile[0].endswith("kg2"):
+    if tile[0].endswith("kg2"):  # A then B in each of three slots
         slots = [(s * (a_bytes + b_bytes), (s + 1) * (a_bytes + b_bytes)) for s in range(3)]
     else:
         slots = [(s * a_bytes, (s + 1) * a_bytes) for s in range(3)]
