@@ -617,6 +617,13 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     g.A = dZ; g.lda = s.h; g.a_kcontig = true;
     g.B[0] = at(Wo, col0 * s.h, s.e); g.ldb = s.h; g.b_kcontig = true;
     g.C[0] = dO; g.ldc = s.w;
+    // D = rowsum(dO * O) per head from the dO GEMM's epilogue where its tile allows (16-bit path:
+    // one round of 64 x 192 tiles, heads that divide 192), else by its own kernel below
+    g.epi = tp::EPI_STORE_ROWDOT;
+    g.aux = O; g.ldaux = s.w;
+    g.rd = Dq; g.rd_seq = (int)s.s; g.rd_heads = (int)s.Hs; g.rd_dh = (int)s.d;
+    const bool fused_rd = s.h16 && tp::gemm_rowdot_ok(g);
+    if (!fused_rd) g.epi = tp::EPI_STORE;
     if (gemm(s, g, st, TP_STEP_ATTN_DO) != hipSuccess) return TP_EHIP;
 
 
@@ -628,11 +635,11 @@ int tp_attn_shard_bwd(const tp_dims* dims, int shard, int degree, const void* X,
     auto core = [&](int part, hipStream_t q) {
         return s.h16 ? tp::attn_bwd_bf16(ad, part, q) : tp::attn_bwd_f32(ad, part, q);
     };
-    {   // D = rowsum(dO * O), then the dK/dV and dQ passes: on the 16-bit path as one
+    {   // D = rowsum(dO * O) (unless the dO GEMM formed it), then the dK/dV and dQ passes: on the 16-bit path as one
         // launch, the dQ workgroups queued behind the dK/dV ones (on two streams side by
         // side they measured slower: their workgroups compete for the same CUs)
         StepTimer t(TP_STEP_ATTN_CORE_BWD, st);
-        if (core(tp::ATTN_BWD_ROWDOT, st) != hipSuccess) return TP_EHIP;
+        if (!fused_rd && core(tp::ATTN_BWD_ROWDOT, st) != hipSuccess) return TP_EHIP;
         if (s.h16 ? core(tp::ATTN_BWD_DKDV_DQ, st) != hipSuccess
                   : (core(tp::ATTN_BWD_DKDV, st) != hipSuccess || core(tp::ATTN_BWD_DQ, st) != hipSuccess))
             return TP_EHIP;

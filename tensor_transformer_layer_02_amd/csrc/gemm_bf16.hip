@@ -91,6 +91,8 @@ struct GemmArgs {
     const bf16_t* aux;
     int64_t ldaux;
     int gelu_tanh;
+    float* rd;  // EPI_STORE_ROWDOT
+    int rd_seq, rd_heads, rd_dh;
 };
 
 // Up to two independent problems of the same layout and epilogue in one
@@ -833,7 +835,14 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     constexpr int EROWS = BM / 2, ELD = BN + 4;  // fp32 staging: row pitch BN + 4 floats
     constexpr int SP = BN * 2 + 8;               // bf16 staging: row pitch in bytes
     constexpr int EBYTES = F32STAGE ? EROWS * ELD * 4 : BM * SP;
-    constexpr int SMEM = RING > EBYTES ? RING : EBYTES;
+    // EPI_STORE_ROWDOT: the tile of aux (O) comes straight into LDS behind the ring at the
+    // start, and the row dots' per-chunk partial sums go behind the output image
+    constexpr bool ROWDOT = EPI == EPI_STORE_ROWDOT;
+    constexpr int ABYTES = ROWDOT ? BM * BN * 2 : 0;
+    constexpr int RED_OFF = (EBYTES + 255) / 256 * 256;
+    static_assert(!ROWDOT || (RED_OFF + BM * (BN / 8) * 4 <= RING && (BM * BN * 2) % (NWV * 1024) == 0),
+                  "row-dot areas");
+    constexpr int SMEM = (RING > EBYTES ? RING : EBYTES) + ABYTES;
     constexpr int WTM = Core::WTM, WTN = Core::WTN, FM = Core::FM, FN = Core::FN;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
@@ -855,13 +864,25 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const int kb = split * kchunk;
     const int kn = min(kchunk, nk_all - kb);
 
+    if constexpr (ROWDOT) {  // the aux tile [BM][BN] (rows past M read as zeros), oldest loads in flight
+        const int64_t aoff = (int64_t)m0 * p.ldaux + n0;
+        const int64_t ext = ((int64_t)(p.M - m0 - 1) * p.ldaux + (p.N - n0)) * 2;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.aux + aoff, (uint32_t)(ext > 0x7fffffff ? 0x7fffffff : ext));
+#pragma unroll
+        for (int i = 0; i < ABYTES / (NWV * 1024); ++i) {
+            const int q = wave + NWV * i, off = q * 1024 + 16 * lane;
+            const int r = off / (BN * 2), cb = off % (BN * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem + SMEM - ABYTES + q * 1024), 16,
+                                                     m0 + r < p.M ? (uint32_t)(r * p.ldaux * 2 + cb) : OOB, 0, 0, 0);
+        }
+    }
     Core core(p, smem, m0, n0, kb, kn);
     core.run();
     auto& acc = core.acc;
     if constexpr (KG == 2) {
         // the second K group adds its partial sums into the first's, one 32-column
         // block of the wave tile at a time (fixed order: deterministic)
-        static_assert(OUTF32 || EPI == EPI_STORE, "the K-group split serves plain stores");
+        static_assert(OUTF32 || EPI == EPI_STORE || EPI == EPI_STORE_ROWDOT, "the K-group split serves plain stores");
         float* mg = reinterpret_cast<float*>(smem);
         const int wl = wave % 4, g = wave / 4;
 #pragma unroll
@@ -895,7 +916,8 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     const int csg = n0 / p.cseg;
     const int cofs = csg * p.cseg;
     const int rows = p.M - m0, ncols = p.N - n0;  // valid extent of the tile
-    static_assert(F32STAGE || KG == 1 || EPI == EPI_STORE, "bf16 epilogues with K groups: plain stores only");
+    static_assert(F32STAGE || KG == 1 || EPI == EPI_STORE || EPI == EPI_STORE_ROWDOT,
+                  "bf16 epilogues with K groups: plain stores only");
     if constexpr (!F32STAGE) {
         // Bias on the accumulators; the output image goes through LDS once.  With
         // GeLU, Gp = GeLU'(U) (saved for the backward, which needs only that of U)
@@ -926,6 +948,42 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
             if (epi_wave) stage_bf16<ST, FM, FN, WTM, WTN, SP>(smem, acc, bias, ncols, wm, wn, lane);
             __syncthreads();
             store_bf16<BM, BN, SP, 64 * NWV>(smem, C, p.ldc, rows, ncols, tid);
+            if constexpr (ROWDOT) {
+                // each 8-column chunk of the rounded image times the aux tile, then per row
+                // and head the chunks' sums in chunk order (deterministic)
+                constexpr int GPR = BN / 8, NTA = 64 * NWV;
+                static_assert((BM * GPR) % NTA == 0, "row-dot split");
+                float* red = reinterpret_cast<float*>(smem + RED_OFF);
+                const char* at = smem + SMEM - ABYTES;
+                __builtin_amdgcn_s_waitcnt(0);  // this thread's aux loads (long done: oldest in flight)
+                __syncthreads();                // ... and every thread's
+#pragma unroll
+                for (int k = 0; k < BM * GPR / NTA; ++k) {
+                    const int e = tid + k * NTA, lr = e / GPR, cg = e % GPR;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(smem + lr * SP + cg * 16);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(smem + lr * SP + cg * 16 + 8);
+                    const u32x4 av = *reinterpret_cast<const u32x4*>(at + lr * (BN * 2) + cg * 16);
+                    const uint32_t cv[4] = {lo[0], lo[1], hi[0], hi[1]};
+                    float sum = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        sum += Store16<ST>::lo(av[q]) * Store16<ST>::lo(cv[q]);
+                        sum += Store16<ST>::hi(av[q]) * Store16<ST>::hi(cv[q]);
+                    }
+                    red[e] = sum;  // e = lr GPR + cg
+                }
+                __syncthreads();
+                const int cph = p.rd_dh / 8, hpt = BN / p.rd_dh;  // chunks per head, heads per tile
+                if (tid < BM * hpt) {
+                    const int r = tid / hpt, hh = tid % hpt, m = m0 + r;
+                    if (m < p.M && n0 + (hh + 1) * p.rd_dh <= p.N) {
+                        float d = 0.f;
+                        for (int c = 0; c < cph; ++c) d += red[r * GPR + hh * cph + c];
+                        const int b = m / p.rd_seq, j = m % p.rd_seq, g = n0 / p.rd_dh + hh;
+                        p.rd[((int64_t)b * p.rd_heads + g) * p.rd_seq + j] = d;
+                    }
+                }
+            }
         }
     } else {
         // fp32 staging, half a tile (the rows of wave rows wm / HR == half) at a time,
@@ -1097,6 +1155,7 @@ GemmArgs make_args(const GemmDesc& d) {
     a.C2 = static_cast<bf16_t*>(d.C2); a.ldc2 = d.ldc2;
     a.aux = static_cast<const bf16_t*>(d.aux); a.ldaux = d.ldaux;
     a.gelu_tanh = d.gelu_tanh ? 1 : 0;
+    a.rd = d.rd; a.rd_seq = d.rd_seq; a.rd_heads = d.rd_heads; a.rd_dh = d.rd_dh;
     return a;
 }
 
@@ -1140,9 +1199,11 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
             if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
                 return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2, ST>(b, s);
             return hipErrorInvalidValue;
-        default:  // 10: K-contiguous operands, plain 16-bit stores only
+        default:  // 10: K-contiguous operands, plain 16-bit stores (and their row dots) only
             if (d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 && d.epi == EPI_STORE)
                 return launch<64, 192, 8, true, true, false, EPI_STORE, false, 2, ST>(b, s);
+            if (d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 && d.epi == EPI_STORE_ROWDOT)
+                return launch<64, 192, 8, true, true, false, EPI_STORE_ROWDOT, false, 2, ST>(b, s);
             return hipErrorInvalidValue;
     }
 }
@@ -1160,6 +1221,16 @@ void gemm_force_tile(int tile, int ksplit) {
 }
 
 int gemm_tile_count() { return (int)(sizeof(kCands) / sizeof(kCands[0])); }
+
+bool gemm_rowdot_ok(const GemmDesc& d) {
+    const int cus = d.cus > 0 && d.cus < 256 ? d.cus : 256;
+    const int64_t tiles = (int64_t)((d.M + 63) / 64) * ((d.N + 191) / 192);
+    return d.M > 0 && d.N > 0 && d.K > 0 && d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 &&
+           d.bseg >= (1 << 30) && d.cseg >= (1 << 30) && tiles <= cus && d.rd && d.aux && d.rd_dh > 0 &&
+           d.rd_dh % 8 == 0 && 192 % d.rd_dh == 0 && d.N % d.rd_dh == 0 && d.rd_seq > 0 && d.rd_heads > 0 &&
+           (int64_t)d.rd_heads * d.rd_dh >= d.N && d.M % d.rd_seq == 0 && d.ldaux % 8 == 0 && d.ldaux >= d.N &&
+           (reinterpret_cast<uintptr_t>(d.aux) & 15u) == 0;
+}
 
 // Tile shape (and K split) with the least estimated time on 256 CUs (or the
 // share `cus` of them the launch is given beside other work).  A CU
@@ -1189,7 +1260,10 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
     if (b.n == 0) return hipSuccess;
     const bool allow_split = part && part_floats >= b.pslab && (reinterpret_cast<uintptr_t>(part) & 15u) == 0;
     const bool tn32 = !d[0].a_kcontig && !d[0].b_kcontig && !d[0].b_kseg && d[0].out_f32;
-    const bool nt16 = d[0].a_kcontig && d[0].b_kcontig && !d[0].b_kseg && !d[0].out_f32 && d[0].epi == EPI_STORE;
+    const bool nt16 = d[0].a_kcontig && d[0].b_kcontig && !d[0].b_kseg && !d[0].out_f32 &&
+                      (d[0].epi == EPI_STORE || d[0].epi == EPI_STORE_ROWDOT);
+    const bool rowdot = d[0].epi == EPI_STORE_ROWDOT;  // only the 64 x 192 K-group tile has it
+    if (rowdot && (n != 1 || !gemm_rowdot_ok(d[0]))) return hipErrorInvalidValue;
     int best = -1, best_split = 1;
     double best_cost = 1e300;
     int kmax = 0;
@@ -1215,6 +1289,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
         // the 8-wave K-group 64 x 192 tile: plain 16-bit stores of K-contiguous operands,
         // where its tiles fill the CUs in one round (small N, long K)
         if (c == 10 && (!nt16 || t > cus)) continue;
+        if (rowdot && c != 10) continue;
         if (forced && c == g_force_tile) {  // test hook: this tile wherever it is valid
             best = c;
             best_split = (g_force_split == 2 && allow_split && tn32) ? 2 : 1;

@@ -19,6 +19,10 @@ enum Epi : int {
     EPI_BIAS = 1,       // C = acc + bias[n]
     EPI_BIAS_GELU = 2,  // U = acc + bias[n]; C = Gp = GeLU'(U); C2 = Y = GeLU(U)
     EPI_GELU_BWD = 3,   // C = acc * aux[m, n] (aux: Gp of EPI_BIAS_GELU)
+    // C = acc (16-bit), and per row m and head h (columns h rd_dh .. +rd_dh-1):
+    // rd[(b rd_heads + h) rd_seq + j] = sum over the head's columns of C[m, n] aux[m, n],
+    // m = b rd_seq + j, from the rounded C (the attention backward's D = rowsum(dO * O))
+    EPI_STORE_ROWDOT = 4,
 };
 
 // C[M, N] (+epilogue) = sum_k A(m, k) B(k, n).
@@ -51,6 +55,8 @@ struct GemmDesc {
     int cus = 0;                  // CUs the tile choice may count on (0: all 256); a launch that
                                   // shares the GPU with another stream's work plans for its share
     bool fp16 = false;            // 16-bit operands / outputs are IEEE half (else bfloat16)
+    float* rd = nullptr;          // EPI_STORE_ROWDOT: the row dots and their layout
+    int rd_seq = 0, rd_heads = 0, rd_dh = 0;
 };
 
 // bf16 operands, fp32 MFMA accumulation.  Returns hipSuccess or the launch error.
@@ -67,6 +73,10 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
 // else no split); tile < 0 restores the cost model.  Process-wide, not thread-safe.
 void gemm_force_tile(int tile, int ksplit);
 int gemm_tile_count();
+// Whether gemm_bf16 can run d with EPI_STORE_ROWDOT: plain 16-bit output of
+// K-contiguous operands, one round of 64 x 192 tiles (ceil(M/64) ceil(N/192) <= the
+// CUs), heads that divide 192 and N, aux 16-byte aligned with ldaux a multiple of 8.
+bool gemm_rowdot_ok(const GemmDesc& d);
 
 // dst[k] += src[k] for n (<= ZMAX) row-major fp32 blocks (rows[k] x cols[k],
 // row strides ld[k] and lds[k]) in one launch.

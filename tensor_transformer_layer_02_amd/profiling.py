@@ -39,7 +39,7 @@ STEP_ORDER = [
     ("MLP_UP", ["gemm"]), ("MLP_DOWN", ["gemm"]), ("QKV", ["gather*", "gemm"]), ("ATTN_CORE", ["attn_fwd"]),
     ("ATTN_OUT", ["gemm"]), ("MLP_DU", ["gemm"]), ("MLP_DB1", ["colsum_partial", "colsum_final"]),
     ("MLP_DW", ["gemm", "add*"]), ("MLP_DX", ["gemm"]), ("ATTN_DO", ["gemm"]),
-    ("ATTN_CORE_BWD", ["attn_rowdot", "attn_bwd_dkdv", "attn_bwd_dq*"]),  # dK/dV and dQ: one launch (16-bit)
+    ("ATTN_CORE_BWD", ["attn_rowdot*", "attn_bwd_dkdv", "attn_bwd_dq*"]),  # 16-bit: D from the dO GEMM, dK/dV + dQ one launch
     ("ATTN_DW", ["gemm", "add*"]), ("ATTN_DBIAS", ["colsum_partial", "colsum_final"]), ("ATTN_DX", ["gemm"]),
 ]
 KEYS = {"gemm": ("gemm_bf16_kernel", "gemm_f32_kernel"), "attn_fwd": ("attn_fwd",), "add": ("add_f32_2d",),
