@@ -624,6 +624,85 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
     }
 }
 
+// The same at d = 128 (KVL): K^T and V^T fragments of the wave's key group from the
+// phase's K/V tiles in LDS (kvt: K [64][D], then V), and the LSE and D of the
+// wave's queries straight from memory (buffer ranges lrs / drs over this
+// (sequence, head)'s rows; past the sequence end they read zeros), issued first
+// so that their latency overlaps the S and dP products.
+template <int D, typename ST>
+__device__ __forceinline__ void dkdv_block_kvl(const AttnArgs& a, const FragAddr<D>& fa, const char* __restrict__ cur,
+                                               const char* __restrict__ kvt, __amdgpu_buffer_rsrc_t lrs,
+                                               __amdgpu_buffer_rsrc_t drs, f32x16 (&dk)[D / 32],
+                                               f32x16 (&dv)[D / 32], int q0, int j, int half, int kg2, int kw0,
+                                               int kw, int lane) {
+    constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    const int s = a.seq;
+    const char* Qt = cur;
+    const char* dOt = cur + 2 * TILE;
+    const int rb = BKV * j;           // first row of block j in the tiles
+    const int qh0 = q0 + 32 * half;   // this wave's 32 queries
+    f32x4 L[4], Dd[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const int q = qh0 + 8 * r4 + 4 * (lane >> 5);
+        L[r4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, q * 4, 0, 0));
+        Dd[r4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, q * 4, 0, 0));
+    }
+    f32x16 sacc = zero16(), pacc = zero16();
+    u32x4 fq = fa.frag_rows(Qt, rb + 32 * half, 0), fo = fa.frag_rows(dOt, rb + 32 * half, 0);
+    u32x4 fk = fa.frag_rows(kvt, 32 * kg2, 0), fv = fa.frag_rows(kvt + TILE, 32 * kg2, 0);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+        u32x4 nq = fq, no = fo, nk = fk, nv = fv;
+        if (c + 1 < KC) {
+            nq = fa.frag_rows(Qt, rb + 32 * half, c + 1);
+            no = fa.frag_rows(dOt, rb + 32 * half, c + 1);
+            nk = fa.frag_rows(kvt, 32 * kg2, c + 1);
+            nv = fa.frag_rows(kvt + TILE, 32 * kg2, c + 1);
+        }
+        sacc = Store16<ST>::mfma(fq, fk, sacc);
+        pacc = Store16<ST>::mfma(fo, fv, pacc);
+        fq = nq;
+        fo = no;
+        fk = nk;
+        fv = nv;
+    }
+    // rows = queries qh0 + res_row(r), column = this lane's key
+    const bool edge = (a.causal && qh0 < kw0 + 31) || q0 + BKV > s || kw0 + 32 > s;  // wave-uniform
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            sacc[4 * r4 + e] = ex2(fmaf(sacc[4 * r4 + e], a.scale_log2, -L[r4][e] * LOG2E));
+    if (edge) {  // blocks that cross the diagonal or an end of the sequence only
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 32 * half + res_row(r, lane);
+            if (!(q < s && kw < s && (!a.causal || kw <= q))) sacc[r] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - Dd[r / 4][r % 4]);
+    u32x4 to = fa.frag_tr(dOt, rb, 0, 2 * half), tq = fa.frag_tr(Qt, rb, 0, 2 * half);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const u32x4 pf = pack_chunk<ST>(sacc, hh), sf = pack_chunk<ST>(pacc, hh);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            u32x4 no = to, nq = tq;  // the next (chunk, d block) pair's fragments
+            const int nd = db + 1 < DB ? db + 1 : 0, nk = 2 * half + (db + 1 < DB ? hh : hh + 1);
+            if (db + 1 < DB || hh == 0) {
+                no = fa.frag_tr(dOt, rb, nd, nk);
+                nq = fa.frag_tr(Qt, rb, nd, nk);
+            }
+            dv[db] = Store16<ST>::mfma(pf, to, dv[db]);
+            dk[db] = Store16<ST>::mfma(sf, tq, dk[db]);
+            to = no;
+            tq = nq;
+        }
+    }
+}
+
 // dK, dV for the 64-key blocks x and nb-1-x.  Causal: one block after the
 // other, each with all 8 waves: wave = (32-key group kg2 = wave & 1) x (query
 // quarter qq = wave >> 1: block qq / 2 of each streamed pair of 64-query
@@ -642,22 +721,27 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
 template <int D>
 struct DkdvLds {
     static constexpr int TILE = BKV * D * 2, DB = D / 32;
-    static constexpr int SLOT = 4 * TILE + 4 * BKV * 4;  // Q pair, dO pair, LSE pair, D pair
+    // KVL (d = 128): the K and V fragments of the phase's key block are read from LDS in every
+    // block instead of being held in registers through the stream (which spilled), and the LSE
+    // and D of the queries come from memory, so a stage is just the Q and dO pairs.
+    static constexpr bool KVL = D == 128;
+    static constexpr int SLOT = 4 * TILE + (KVL ? 0 : 4 * BKV * 4);  // Q pair, dO pair[, LSE pair, D pair]
     static constexpr int MERGE = 4 * DB * 16 * 64 * 4;   // one of dK / dV for four groups
     // PRE: the K and V tiles of both key blocks come into LDS once, at the start
     // (the fragments of a key group are then read from LDS by each of the four
     // waves that use them, instead of four times from memory), where they fit
     // beside the two stages (up to d = 96).
-    static constexpr bool PRE = 2 * SLOT + 4 * TILE <= 160 * 1024;
-    static constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : 0);
+    static constexpr bool PRE = !KVL && 2 * SLOT + 4 * TILE <= 160 * 1024;
+    static constexpr int REG = 2 * SLOT + (PRE ? 4 * TILE : KVL ? 2 * TILE : 0);
     static constexpr int SMEM = REG > MERGE ? REG : MERGE;
+    static_assert(REG <= 160 * 1024, "the stages and K/V tiles fit the LDS");
 };
 
 template <int D, typename ST, bool NOMASK>
 __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ smem, int x, int bh) {
     constexpr int KC = D / 16, DB = D / 32, TILE = DkdvLds<D>::TILE;
     constexpr int SLOT = DkdvLds<D>::SLOT, MERGE = DkdvLds<D>::MERGE;
-    constexpr bool PRE = DkdvLds<D>::PRE;
+    constexpr bool PRE = DkdvLds<D>::PRE, KVL = DkdvLds<D>::KVL;
     constexpr int PITCH = D * 2 + 16;  // row pitch of the bf16 dK / dV image (rows 4 apart on other banks)
     static_assert(2 * BKV * PITCH <= SLOT && MERGE <= SLOT, "epilogue areas fit one stage");
 
@@ -684,8 +768,16 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
     go.init(a.ld_o, wave, lane);
     char* const st0 = smem;
     char* const st1 = smem + SLOT;
-    char* const kvt = smem + 2 * SLOT;  // PRE: [K | V] of key block x, then of key block nb-1-x
+    char* const kvt = smem + 2 * SLOT;  // PRE: [K | V] of key block x, then of key block nb-1-x;
+                                        // KVL: [K | V] of the phase's key block
     if constexpr (PRE) load_tiles<D, 4>(Kg, a.ld_qkv, Vg, a.ld_qkv, x * BKV, xl * BKV, s, kvt, wave, lane);
+    TileDMA<D, KVL ? BKV : 2 * BKV> gkv1;  // KVL: one 64-row K or V tile (unused otherwise)
+    __amdgpu_buffer_rsrc_t lrs, drs;  // KVL: this (sequence, head)'s LSE and D rows
+    if constexpr (KVL) {
+        gkv1.init(a.ld_qkv, wave, lane);
+        lrs = make_rsrc(lseg, (uint32_t)s * 4u);
+        drs = make_rsrc(Dg, (uint32_t)s * 4u);
+    }
 
     const int nphase = (xl != x && !side) ? 2 : 1;
     int sbase = 0;        // slot of the phase's first stage
@@ -701,14 +793,18 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
             const int row0 = qs * BKV;
             gq.load(Qg, a.ld_qkv, row0, s, st0, wave);
             go.load(dOg, a.ld_o, row0, s, st0 + 2 * TILE, wave);
-            if (tid < 2 * BKV) {
+            if (!KVL && tid < 2 * BKV) {
                 const int q = row0 + tid;
                 lsev = q < s ? lseg[q] : 0.f;
                 dval = q < s ? Dg[q] : 0.f;
             }
         }
-        u32x4 kf[KC], vf[KC];  // K^T, V^T operands: column = key, k = d
-        if constexpr (!PRE) {
+        if constexpr (KVL) {  // the phase's K and V tiles (the previous phase's reads ended at its last barrier)
+            gkv1.load(Kg, a.ld_qkv, kb * BKV, s, kvt, wave);
+            gkv1.load(Vg, a.ld_qkv, kb * BKV, s, kvt + TILE, wave);
+        }
+        u32x4 kf[KC], vf[KC];  // K^T, V^T operands (not KVL): column = key, k = d
+        if constexpr (!PRE && !KVL) {
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
                 const bool ok = kw < s;
@@ -719,7 +815,7 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
         }
         if (!staged) {
             __builtin_amdgcn_s_waitcnt(0);  // this thread's loads are done
-            if (npair > 0 && tid < 2 * BKV) {
+            if (!KVL && npair > 0 && tid < 2 * BKV) {
                 reinterpret_cast<float*>(st0 + 4 * TILE)[tid] = lsev * LOG2E;
                 reinterpret_cast<float*>(st0 + 4 * TILE + 2 * BKV * 4)[tid] = dval;
             }
@@ -748,7 +844,7 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
                 const int row1 = more ? (qs + 2 * (it + 1)) * BKV : qs_next * BKV;
                 gq.load(Qg, a.ld_qkv, row1, s, nxt, wave);
                 go.load(dOg, a.ld_o, row1, s, nxt + 2 * TILE, wave);
-                if (tid < 2 * BKV) {  // raw values: scaling them here would wait for every load in flight
+                if (!KVL && tid < 2 * BKV) {  // raw values: scaling them here would wait for every load in flight
                     const int q = row1 + tid;
                     lsev = q < s ? lseg[q] : 0.f;
                     dval = q < s ? Dg[q] : 0.f;
@@ -763,10 +859,14 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
             } else {
                 const int q0 = (qs + 2 * it + jb) * BKV;  // this wave's query block
                 // skip when the key group or the query block is empty, or every query precedes every key
-                if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0))
-                    dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
+                if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0)) {
+                    if constexpr (KVL)
+                        dkdv_block_kvl<D, ST>(a, fa, cur, kvt, lrs, drs, dk, dv, q0, jb, half, kg2, kw0, kw, lane);
+                    else
+                        dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
+                }
             }
-            if ((more || pre1) && tid < 2 * BKV) {
+            if (!KVL && (more || pre1) && tid < 2 * BKV) {
                 reinterpret_cast<float*>(nxt + 4 * TILE)[tid] = lsev * LOG2E;
                 reinterpret_cast<float*>(nxt + 4 * TILE + 2 * BKV * 4)[tid] = dval;
             }
@@ -795,7 +895,7 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
         // dk/dv: rows = keys kw0 + res_row(r), column = d 32db + lane%32
         bf16_t* dKg = a.dqkv + (int64_t)b * s * a.ld_qkv + a.w + g * D;
         bf16_t* dVg = dKg + a.w;
-        if (!PRE || (NOMASK && side)) {  // each writer stores its values directly
+        if (!(PRE || KVL) || (NOMASK && side)) {  // each writer stores its values directly
             if ((side ? half == 0 : qq == 0) && kw0 < s) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
