@@ -182,22 +182,35 @@ __device__ __forceinline__ void load_tiles(const bf16_t* A, int64_t lda, const b
 template <int D>
 struct FragAddr {
     static constexpr int ROWB = D * 2, KC = D / 16, DB = D / 32;
-    int rows[KC];
-    int tr[2][DB];
+    // d = 128: rows are 256 bytes and a lane's offsets within a row stay below 256, so
+    // every offset is rows[0] or tr[0][0] XOR a constant (chunk c: c << 5; d block db:
+    // db << 6; read h = 1: eight rows further, 2048, and the swizzle's bit 1, 32); only
+    // those two are held, leaving registers to the streams' accumulators.
+    static constexpr bool XOR = D == 128;
+    int rows[XOR ? 1 : KC];
+    int tr[XOR ? 1 : 2][XOR ? 1 : DB];
     __device__ __forceinline__ void init(int lane) {
         const int lr = lane & 31, l5 = lane >> 5, G = lane >> 4, j = lane & 15;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) rows[c] = toff<D>(lr, 16 * c + 8 * l5);
+        for (int c = 0; c < (XOR ? 1 : KC); ++c) rows[c] = toff<D>(lr, 16 * c + 8 * l5);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < (XOR ? 1 : 2); ++h)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < (XOR ? 1 : DB); ++db)
                 tr[h][db] = toff<D>(8 * h + 4 * (G >> 1) + (j >> 2), 32 * db + 16 * (G & 1) + 4 * (j & 3));
+    }
+    __device__ __forceinline__ int row_off(int c) const {
+        if constexpr (XOR) return rows[0] ^ (c << 5);
+        else return rows[c];
+    }
+    __device__ __forceinline__ int tr_off(int h, int db) const {
+        if constexpr (XOR) return tr[0][0] ^ (h ? 2048 + 32 : 0) ^ (db << 6);
+        else return tr[h][db];
     }
     // Operand fragment of rows rb .. rb+31 (rb % 16 == 0), k = d chunk c:
     // lane l gets row rb + l%32, d = 16c + 8*(l/32) .. +7.
     __device__ __forceinline__ u32x4 frag_rows(const char* tile, int rb, int c) const {
-        return *reinterpret_cast<const u32x4*>(tile + rb * ROWB + rows[c]);
+        return *reinterpret_cast<const u32x4*>(tile + rb * ROWB + row_off(c));
     }
     // Operand fragment with rows = d (32db .. +31) and k = tile rows
     // rb + 16kc .. +15 (rb % 16 == 0) in the relabelled order: slot s of lane
@@ -208,7 +221,7 @@ struct FragAddr {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(base + tr[h][db]));
+                (__attribute__((address_space(3))) v4i16*)(base + tr_off(h, db)));
             const u32x2 w = __builtin_bit_cast(u32x2, t);
             out[2 * h] = w[0];
             out[2 * h + 1] = w[1];
@@ -630,12 +643,18 @@ __device__ __forceinline__ void dkdv_block(const AttnArgs& a, const FragAddr<D>&
 // (sequence, head)'s rows; past the sequence end they read zeros), issued first
 // so that their latency overlaps the S and dP products.
 template <int D, typename ST>
-__device__ __forceinline__ void dkdv_block_kvl(const AttnArgs& a, const FragAddr<D>& fa, const char* __restrict__ cur,
+__device__ __forceinline__ void dkdv_block_kvl(const AttnArgs& a, const char* __restrict__ cur,
                                                const char* __restrict__ kvt, __amdgpu_buffer_rsrc_t lrs,
                                                __amdgpu_buffer_rsrc_t drs, f32x16 (&dk)[D / 32],
                                                f32x16 (&dv)[D / 32], int q0, int j, int half, int kg2, int kw0,
-                                               int kw, int lane) {
+                                               int kw, int lane, const FragAddr<D>& fa0) {
     constexpr int KC = D / 16, DB = D / 32, TILE = BKV * D * 2;
+    static_assert(FragAddr<D>::XOR, "offsets derived from two registers");
+    // The two base offsets pass through an empty asm statement, so that the compiler
+    // derives the others here in each block instead of holding them (or their
+    // spills) through the stream.
+    FragAddr<D> fa = fa0;
+    asm volatile("" : "+v"(fa.rows[0]), "+v"(fa.tr[0][0]));
     const int s = a.seq;
     const char* Qt = cur;
     const char* dOt = cur + 2 * TILE;
@@ -861,7 +880,7 @@ __device__ __forceinline__ void dkdv_body(const AttnArgs& a, char* __restrict__ 
                 // skip when the key group or the query block is empty, or every query precedes every key
                 if (kw0 < s && q0 < s && !(a.causal && q0 + 32 * half + 31 < kw0)) {
                     if constexpr (KVL)
-                        dkdv_block_kvl<D, ST>(a, fa, cur, kvt, lrs, drs, dk, dv, q0, jb, half, kg2, kw0, kw, lane);
+                        dkdv_block_kvl<D, ST>(a, cur, kvt, lrs, drs, dk, dv, q0, jb, half, kg2, kw0, kw, lane, fa);
                     else
                         dkdv_block<D, ST>(a, fa, cur, kf, vf, dk, dv, q0, jb, half, kw0, kw, lane);
                 }
