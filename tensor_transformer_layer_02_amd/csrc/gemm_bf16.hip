@@ -988,7 +988,10 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
     } else {
         // fp32 staging, half a tile (the rows of wave rows wm / HR == half) at a time,
         // 16 bytes per lane and store; every thread then handles 8 consecutive
-        // columns of a row (16-byte loads of U and stores of the outputs).
+        // columns of a row (16-byte loads of U and stores of the outputs).  The
+        // outputs are stored non-temporal, as the bf16 ones: whole 32-byte runs per
+        // thread that no later step of the launch reads, so they need not sit dirty
+        // in L2 to be written back when the launch ends.
         float* stage = reinterpret_cast<float*>(smem);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -1060,8 +1063,8 @@ __global__ void __launch_bounds__(64 * NWV, (tile_occupancy<BM, BN, NWV>())) gem
                             } else {
                                 c = slab + (int64_t)m * p.N + (n0 + cg * 8);
                             }
-                            *reinterpret_cast<f32x4*>(c) = lo[k];
-                            *reinterpret_cast<f32x4*>(c + 4) = hi[k];
+                            __builtin_nontemporal_store(lo[k], reinterpret_cast<f32x4*>(c));
+                            __builtin_nontemporal_store(hi[k], reinterpret_cast<f32x4*>(c + 4));
                         } else {  // EPI_GELU_BWD: dU = dY * Gp, Gp = GeLU'(U) saved by the forward
                             float v[8] = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
 #pragma unroll
@@ -1171,17 +1174,25 @@ struct Cand {
 // with 8 waves in two K groups, for plain 16-bit stores of K-contiguous
 // operands where one round of its tiles fills the CUs (dO: N = w, K = h):
 // against the 4-wave 64 x 192 tile, one workgroup per CU either way, it puts
-// two waves on each SIMD (dO 29.7 against 33.8 us at the 8.3B shape).
+// two waves on each SIMD (dO 29.7 against 33.8 us at the 8.3B shape).  Index
+// 11 is the 256 x 128 tile with 8 waves (wave tiles 64 x 64), for N where it
+// fills the CUs in one round and the 192-column tile does not (BERT's QKV: N =
+// 960 gives 256 tiles of 128 columns against 160 of 192).
 const Cand kCands[] = {{256, 256, 1, 1.0, false},  {256, 192, 1, 0.98, false}, {192, 192, 1, 0.93, true},
                        {256, 128, 1, 0.84, false}, {128, 128, 2, 0.835, false}, {64, 192, 2, 0.72, false},
                        {64, 64, 4, 0.4, false},    {128, 192, 2, 0.92, false}, {256, 192, 1, 1.10, false},
-                       {192, 192, 1, 0.975, true}, {64, 192, 1, 0.80, false}};
+                       {192, 192, 1, 0.975, true}, {64, 192, 1, 0.80, false}, {256, 128, 1, 0.80, false}};
 constexpr double K_OVERHEAD = 384.0;       // prologue + epilogue of a tile, in units of K
 // The K split's reduction kernel in the same units (a CU's MACs at ~2.2 M per us):
 // three fp32 passes over the outputs at ~5 TB/s, plus a launch (~3 us).
 constexpr double RED_PER_ELEM = 5.3;
 constexpr double RED_FIXED = 6.6e6;
 constexpr double K_OVERHEAD_GELU = 1024.0;  // the same with a GeLU / GeLU' epilogue
+
+// Operands and epilogues the 8-wave 256 x 128 tile (index 11) is built for.
+bool tile11_ok(const GemmDesc& d) {
+    return d.a_kcontig && !d.b_kcontig && !d.b_kseg && !d.out_f32 && (d.epi == EPI_BIAS || d.epi == EPI_STORE);
+}
 
 template <typename ST>
 hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_t s) {
@@ -1199,11 +1210,17 @@ hipError_t dispatch_idx(int c, const GemmDesc& d, const GemmBatch& b, hipStream_
             if (!d.a_kcontig && !d.b_kcontig && !d.b_kseg && d.out_f32 && d.epi == EPI_STORE)
                 return launch<192, 192, 8, false, false, false, EPI_STORE, true, 2, ST>(b, s);
             return hipErrorInvalidValue;
-        default:  // 10: K-contiguous operands, plain 16-bit stores (and their row dots) only
+        case 10:  // K-contiguous operands, plain 16-bit stores (and their row dots) only
             if (d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 && d.epi == EPI_STORE)
                 return launch<64, 192, 8, true, true, false, EPI_STORE, false, 2, ST>(b, s);
             if (d.a_kcontig && d.b_kcontig && !d.b_kseg && !d.out_f32 && d.epi == EPI_STORE_ROWDOT)
                 return launch<64, 192, 8, true, true, false, EPI_STORE_ROWDOT, false, 2, ST>(b, s);
+            return hipErrorInvalidValue;
+        default:  // 11: K-contiguous A, B with N contiguous, 16-bit output with or without bias
+            if (tile11_ok(d) && d.epi == EPI_BIAS)
+                return launch<256, 128, 8, true, false, false, EPI_BIAS, false, 1, ST>(b, s);
+            if (tile11_ok(d) && d.epi == EPI_STORE)
+                return launch<256, 128, 8, true, false, false, EPI_STORE, false, 1, ST>(b, s);
             return hipErrorInvalidValue;
     }
 }
@@ -1289,6 +1306,7 @@ hipError_t gemm_bf16_batch(const GemmDesc* d, int n, float* part, int64_t part_f
         // the 8-wave K-group 64 x 192 tile: plain 16-bit stores of K-contiguous operands,
         // where its tiles fill the CUs in one round (small N, long K)
         if (c == 10 && (!nt16 || t > cus)) continue;
+        if (c == 11 && (n != 1 || !tile11_ok(d[0]))) continue;
         if (rowdot && c != 10) continue;
         if (forced && c == g_force_tile) {  // test hook: this tile wherever it is valid
             best = c;

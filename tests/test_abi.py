@@ -164,7 +164,7 @@ def test_matrices_of_2gib_or_more_are_refused(L, kw, degree, code):
 
 def test_force_tile_hook_rejects_bad_arguments(L):
     n = tp.tp_test_gemm_tile_count()
-    assert n == 11
+    assert n == 12
     for bad in ((-2, 0), (n, 0), (0, 3), (0, -1)):
         with pytest.raises(tp.TpError) as e:
             tp.tp_test_force_gemm_tile(*bad)

@@ -27,7 +27,7 @@ CASES = [
     ("T185_h640_d64_t1", 5, 37, 640, 10, 896, 1, False),
     ("T257_h1728_d96_t3", 1, 257, 1728, 18, 4608, 3, True),   # w = 576: the 192-wide tiles fit Q|K|V
 ]
-NTILES = 11
+NTILES = 12
 
 
 @pytest.mark.parametrize("ksplit", [1, 2])
