@@ -785,7 +785,7 @@ __device__ __forceinline__ void stage_gelu_chunk(char* gimg, char* yimg, const f
 // The stores are marked non-temporal: the next kernel reads C anyway, and lines
 // the L2 does not hold dirty need no write-back when the kernel ends (measured:
 // the gap to the next launch 4.0 -> 2.5 us, the bf16-output GEMMs 1-2 us
-// faster; the fp32 weight-gradient stores stay plain, they slowed down).
+// faster).
 // With RSTRIDE, the image holds one 32-row block per wave row (a chunk of the
 // tile): image row lr is tile row (lr / 32) * RSTRIDE + roff + lr % 32.
 template <int BM, int BN, int SP, int NTH, int RSTRIDE = 0>
