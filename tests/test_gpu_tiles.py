@@ -10,7 +10,8 @@ hook tp_test_force_gemm_tile; every GEMM the tile is valid for uses it) and chec
 of every shard against the float64 oracle.  The shapes make M, N and K ragged for every tile,
 and give K step counts (K / 64) with every remainder modulo 6 (the 8-wave pipeline's round):
 hidden 832 (13 steps), 640 (10), 1728 (27); FFN shard 1088 (17), 896 (14), 1536 (24); tokens
-63, 185, 257 (the weight gradients' K: 1, 3 and 5 steps).
+63, 185, 257 (the weight gradients' K: 1, 3 and 5 steps).  The IEEE-half instantiations of every
+tile run the t = 3 shape once more at the fp16 bar.
 """
 from __future__ import annotations
 
@@ -46,3 +47,20 @@ def test_forced_tile_matches_oracle(case, tile, ksplit):
     finally:
         tp.tp_test_force_gemm_tile(-1, 0)
     _say(f"[tiles] {name} tile {tile} ksplit {ksplit}: worst {max(e for _, e in report):.1e}")
+
+
+@pytest.mark.parametrize("tile", list(range(NTILES)))
+def test_forced_tile_fp16_matches_oracle(tile):
+    """The IEEE-half instantiations of every tile (fp16 MFMAs, fp32 accumulation) on the
+    ragged t = 3 shape, every output of every shard against the oracle at the fp16 bar."""
+    from tensor_transformer_layer_02_amd import tpshard as tp
+    name, b, s, h, H, F, t, causal = CASES[2]
+    cfg = LayerConfig(420, name + "_fp16", b, s, h, H, F, t, causal, "fp16", True)
+    _say(f"[tiles fp16] {name} tile {tile}")
+    report = []
+    tp.tp_test_force_gemm_tile(tile, 0)
+    try:
+        run_all_shards(cfg, 0.02, report)
+    finally:
+        tp.tp_test_force_gemm_tile(-1, 0)
+    _say(f"[tiles fp16] {name} tile {tile}: worst {max(e for _, e in report):.1e}")
