@@ -146,9 +146,10 @@ def cpu_baseline(cfg, inp, nseq):
 OTHER_WORKLOADS = [("bert4b", 30, 20), ("g30b_t4", 5, 10), ("g30b_t1", 3, 5)]
 
 
-def time_workload(name, dtype, W, K):
+def time_workload(name, dtype, W, K, keep=False):
     """ms per shard fwd+bwd step (HIP events around K steps after W warm-up steps, inputs resident)
-    and algorithmic TFLOP/s of one other workload, shard 0."""
+    and algorithmic TFLOP/s of one other workload, shard 0.  With `keep` the workload's buffers are
+    returned instead of freed (the caller frees them later, off the GPU's busy path)."""
     import torch
 
     from tensor_transformer_layer_02_amd.configs import CONFIGS, shard_flops
@@ -167,13 +168,16 @@ def time_workload(name, dtype, W, K):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     fl = shard_flops(cfg, backward=True)["total"]
-    del run
-    torch.cuda.empty_cache()
+    if not keep:
+        del run
+        torch.cuda.empty_cache()
+        run = None
     tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": f"{cfg.name}: {cfg.note}", "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads,
+    res = {"workload": f"{cfg.name}: {cfg.note}", "tokens": cfg.tokens, "hidden": cfg.hidden, "heads": cfg.heads,
             "ffn": cfg.ffn, "degree": cfg.degree, "causal": cfg.causal, "steps": K, "warmup": W,
             "ms_per_step": round(ms, 4), "flops_per_step": fl, "tflops": round(tf, 1),
             "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    return (res, run) if keep else res
 
 
 def main():
@@ -256,17 +260,21 @@ def main():
     log(f"[bench] device {prop.name} ({prop.gcnArchName}) CUs={prop.multi_processor_count} peak clock "
         f"{clock_mhz} MHz, peak(bf16 dense)={PEAK_BF16_TFLOPS} TFLOP/s")
 
-    # ---- the other model shapes first (same run; the headline below keeps its own W and K)
-    others = []
+    # ---- the other model shapes first (same run; the headline below keeps its own W and K).  The
+    # headline's buffers already exist and the last workload's are freed only after the headline's
+    # timing, so its W warm-up steps follow that workload's steps with the GPU kept busy: after even
+    # 20 ms of idle the clocks boost, overshoot and settle over ~30 steps, which a short warm-up
+    # would otherwise measure instead of the steady state.
+    others, held = [], None
     if not args.no_others and args.config == "gpt8b" and not args.recompute:
-        del run
-        torch.cuda.empty_cache()
-        for name, ow, ok in OTHER_WORKLOADS:
-            r = time_workload(name, cfg.dtype, ow, ok)
+        for i, (name, ow, ok) in enumerate(OTHER_WORKLOADS):
+            last = i + 1 == len(OTHER_WORKLOADS)
+            r = time_workload(name, cfg.dtype, ow, ok, keep=last)
+            if last:
+                r, held = r
             others.append(r)
             log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step  {r['tflops']} TFLOP/s  "
                 f"({r['pct_of_bf16_peak']}% of bf16 peak)")
-        run = ShardRun(cfg, inp, shards=[args.shard], recompute=args.recompute)
 
     for _ in range(W):
         step()
@@ -283,6 +291,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / K
+    if held is not None:
+        del held
+        torch.cuda.empty_cache()
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.4f} ms/step  {tflops:.1f} TFLOP/s  ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)"
         f"  wall {wall:.3f}s")
