@@ -84,19 +84,23 @@ def peak_clock_mhz():
 
 
 class HipEvents:
-    """hipEvent_t handles from the HIP runtime torch already loaded (same soname)."""
+    """hipEvent_t handles from the HIP runtime torch already loaded (same soname), created without
+    the system-scope fence (hipEventDisableSystemFence): a record then only timestamps, instead of
+    also writing back and invalidating the caches between the kernels it brackets."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
             if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             self.ev[i] = h
         self.n = n
 
