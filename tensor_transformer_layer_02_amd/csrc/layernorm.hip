@@ -102,6 +102,35 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
     __syncthreads();
 }
 
+// acc[k] += the nparts partial rows at row offset `base`, chunk k of this thread, added in
+// partial order (acc[k] unchanged where the chunk lies past cols).  The partials go in groups
+// of QG, each group's loads (every chunk) issued before any is added, so a thread has up to
+// QG NCH loads in flight instead of one; past nparts a group re-reads the last partial (its
+// values are not added), a thread whose chunk lies past cols re-reads the row's last chunk, and
+// chunks past cols for the whole workgroup are skipped.
+template <typename T, int NCH>
+__device__ __forceinline__ void add_parts(f32x4 (&acc)[NCH], const LnParts& P, int nparts, int64_t base, int cols,
+                                          int tid) {
+    constexpr int QG = NCH >= 4 ? 1 : NCH == 3 ? 2 : 4;  // registers: QG * NCH loads in flight
+    for (int q0 = 0; q0 < nparts; q0 += QG) {
+        f32x4 v[QG][NCH];
+#pragma unroll
+        for (int j = 0; j < QG; ++j) {
+            const T* src = static_cast<const T*>(P.p[min(q0 + j, nparts - 1)]) + base;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                if (4 * LNT * k < cols) v[j][k] = ld4<T>(src + min(4 * (tid + LNT * k), cols - 4));
+        }
+#pragma unroll
+        for (int j = 0; j < QG; ++j) {
+            if (q0 + j >= nparts) break;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                if (4 * (tid + LNT * k) < cols) acc[k] += v[j][k];
+        }
+    }
+}
+
 template <typename T, int NCH>
 __global__ void __launch_bounds__(LNT) residual_ln_kernel(int64_t rows, int cols, const LnParts parts, int nparts,
                                                           const T* __restrict__ bias,
@@ -113,6 +142,8 @@ __global__ void __launch_bounds__(LNT) residual_ln_kernel(int64_t rows, int cols
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t base = r * cols;
+    // (one workgroup per row, many resident per CU: the partials' loads one after the other
+    // keep the registers, and so the occupancy that hides their latency, low)
     f32x4 v[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -176,18 +207,21 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
     for (int64_t r = r0; r < r1; ++r) {
         const int64_t base = r * cols;
         const float mu = mean[r], rs = rstd[r];
-        f32x4 g[NCH], xh[NCH];
+        f32x4 g[NCH], xh[NCH], xv[NCH];
         float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {  // x of the row first, then the partials
+            g[k] = xh[k] = xv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (4 * LNT * k < cols) xv[k] = ld4<float>(x + base + min(4 * (tid + LNT * k), cols - 4));
+        }
+        add_parts<T, NCH>(g, dparts, nparts, base, cols, tid);
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int c = 4 * (tid + LNT * k);
-            g[k] = xh[k] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (c >= cols) continue;
-            for (int q = 0; q < nparts; ++q) g[k] += ld4<T>(static_cast<const T*>(dparts.p[q]) + base + c);
-            const f32x4 xv = ld4<float>(x + base + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xh[k][e] = (xv[e] - mu) * rs;
+                xh[k][e] = (xv[k][e] - mu) * rs;
                 const float gg = g[k][e] * gm[k][e];
                 s1 += gg;
                 s2 += gg * xh[k][e];
@@ -290,7 +324,7 @@ hipError_t launch_bwd(const LnBwdDesc& d, hipStream_t s) {
 // Chunks per thread for a row of `cols` columns (4 columns per chunk).
 int nch_for(int cols) {
     const int per = (cols / 4 + LNT - 1) / LNT;
-    return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+    return per <= 1 ? 1 : per <= 2 ? 2 : per <= 3 ? 3 : per <= 4 ? 4 : 8;
 }
 
 }  // namespace
@@ -318,6 +352,7 @@ hipError_t residual_layernorm(const LnFwdDesc& d, hipStream_t s) {
     switch (nch_for(d.cols)) {
         case 1: return fwd_fmt<1>(d, s);
         case 2: return fwd_fmt<2>(d, s);
+        case 3: return fwd_fmt<3>(d, s);
         case 4: return fwd_fmt<4>(d, s);
         default: return fwd_fmt<8>(d, s);
     }
@@ -328,6 +363,7 @@ hipError_t layernorm_bwd(const LnBwdDesc& d, hipStream_t s) {
     switch (nch_for(d.cols)) {
         case 1: return bwd_fmt<1>(d, s);
         case 2: return bwd_fmt<2>(d, s);
+        case 3: return bwd_fmt<3>(d, s);
         case 4: return bwd_fmt<4>(d, s);
         default: return bwd_fmt<8>(d, s);
     }
