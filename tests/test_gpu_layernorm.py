@@ -43,6 +43,7 @@ LN_CASES = [
     (16, 1024, 1, False, False, "bf16"),
     (37, 200, 3, True, True, "fp16"),
     (64, 3072, 8, True, False, "fp16"),
+    (48, 2560, 8, True, True, "bf16"),   # three chunks per thread, the last one partly past cols
 ]
 
 
@@ -78,7 +79,7 @@ def test_residual_layernorm_matches_oracle(case):
 
 
 BWD_CASES = [(37, 200, 3, "bf16"), (64, 3072, 8, "bf16"), (300, 520, 2, "fp32"), (9, 7168, 1, "fp32"),
-             (64, 3072, 8, "fp16")]
+             (64, 3072, 8, "fp16"), (48, 2560, 7, "bf16")]
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=[f"{c[0]}x{c[1]}p{c[2]}{c[3]}" for c in BWD_CASES])
