@@ -55,6 +55,17 @@ __device__ __forceinline__ f32x4 ld4<f16_t>(const f16_t* p) {
     return f32x4{S::lo(w[0]), S::hi(w[0]), S::lo(w[1]), S::hi(w[1])};
 }
 
+// The four values of a ld4-sized load kept as loaded.
+template <typename T>
+__device__ __forceinline__ f32x4 raw_to_f4(const f32x4& w) {
+    return w;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 raw_to_f4(const u32x2& w) {
+    using S = Store16<T>;
+    return f32x4{S::lo(w[0]), S::hi(w[0]), S::lo(w[1]), S::hi(w[1])};
+}
+
 template <typename T>
 __device__ __forceinline__ void st4(T* p, const f32x4& v);
 template <>
@@ -111,22 +122,24 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
 template <typename T, int NCH>
 __device__ __forceinline__ void add_parts(f32x4 (&acc)[NCH], const LnParts& P, int nparts, int64_t base, int cols,
                                           int tid) {
-    constexpr int QG = NCH >= 4 ? 1 : NCH == 3 ? 2 : 4;  // registers: QG * NCH loads in flight
+    // The loads stay as loaded (8 bytes for 16-bit partials) until they are added.
+    using Raw = typename std::conditional<sizeof(T) == 2, u32x2, f32x4>::type;
+    constexpr int QG = NCH >= 4 ? 1 : NCH == 3 ? 8 : 4;  // registers: QG * NCH loads in flight
     for (int q0 = 0; q0 < nparts; q0 += QG) {
-        f32x4 v[QG][NCH];
+        Raw v[QG][NCH];
 #pragma unroll
         for (int j = 0; j < QG; ++j) {
             const T* src = static_cast<const T*>(P.p[min(q0 + j, nparts - 1)]) + base;
 #pragma unroll
             for (int k = 0; k < NCH; ++k)
-                if (4 * LNT * k < cols) v[j][k] = ld4<T>(src + min(4 * (tid + LNT * k), cols - 4));
+                if (4 * LNT * k < cols) v[j][k] = *reinterpret_cast<const Raw*>(src + min(4 * (tid + LNT * k), cols - 4));
         }
 #pragma unroll
         for (int j = 0; j < QG; ++j) {
             if (q0 + j >= nparts) break;
 #pragma unroll
             for (int k = 0; k < NCH; ++k)
-                if (4 * (tid + LNT * k) < cols) acc[k] += v[j][k];
+                if (4 * (tid + LNT * k) < cols) acc[k] += raw_to_f4<T>(v[j][k]);
         }
     }
 }
@@ -194,13 +207,25 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
                                                      const LnParts dparts, int nparts, const float* __restrict__ dres,
                                                      float* __restrict__ dx, T* __restrict__ dx_act,
                                                      float* __restrict__ work, int need) {
+    // Up to 3 chunks per thread the band's column sums live in LDS (slot (q NCH + k) LNT + tid:
+    // each thread owns its slots, 16 bytes apart), so that the registers they free hold a row's
+    // loads in flight; wider rows keep them in registers.
+    constexpr bool LACC = NCH <= 3;
+    constexpr int NR = LACC ? 1 : NCH;
     __shared__ float red[8];
+    __shared__ f32x4 lacc[LACC ? 4 * NCH * LNT : 1];
     const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * band, r1 = min(rows, r0 + band);
-    f32x4 sg[NCH], sb[NCH], sr[NCH], sx[NCH], gm[NCH];
+    f32x4 sg[NR], sb[NR], sr[NR], sx[NR], gm[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        sg[k] = sb[k] = sr[k] = sx[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (LACC) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lacc[(q * NCH + k) * LNT + tid] = z;
+        } else {
+            sg[k] = sb[k] = sr[k] = sx[k] = z;
+        }
         const int c = 4 * (tid + LNT * k);
         gm[k] = (gamma && c < cols) ? ld4<float>(gamma + c) : f32x4{1.f, 1.f, 1.f, 1.f};
     }
@@ -234,14 +259,23 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
             const int c = 4 * (tid + LNT * k);
             if (c >= cols) continue;
             const f32x4 dr = dres ? ld4<float>(dres + base + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 o;
+            f32x4 o, gx;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o[e] = dr[e] + rs * (g[k][e] * gm[k][e] - m1 - xh[k][e] * m2);
-                sg[k][e] += g[k][e] * xh[k][e];
-                sb[k][e] += g[k][e];
-                sr[k][e] += dr[e];
-                sx[k][e] += o[e];
+                gx[e] = g[k][e] * xh[k][e];
+            }
+            if constexpr (LACC) {
+                f32x4* a = lacc + k * LNT + tid;
+                a[0] += gx;
+                a[NCH * LNT] += g[k];
+                a[2 * NCH * LNT] += dr;
+                a[3 * NCH * LNT] += o;
+            } else {
+                sg[k] += gx;
+                sb[k] += g[k];
+                sr[k] += dr;
+                sx[k] += o;
             }
             st4<float>(dx + base + c, o);
             if (dx_act) st4<T>(dx_act + base + c, o);
@@ -252,10 +286,14 @@ __global__ void __launch_bounds__(LNT) ln_bwd_kernel(int64_t rows, int cols, int
     for (int k = 0; k < NCH; ++k) {
         const int c = 4 * (tid + LNT * k);
         if (c >= cols) continue;
-        if (need & 1) st4<float>(work + (0 * nb + blockIdx.x) * cols + c, sg[k]);
-        if (need & 2) st4<float>(work + (1 * nb + blockIdx.x) * cols + c, sb[k]);
-        if (need & 4) st4<float>(work + (2 * nb + blockIdx.x) * cols + c, sr[k]);
-        if (need & 8) st4<float>(work + (3 * nb + blockIdx.x) * cols + c, sx[k]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (!((need >> q) & 1)) continue;
+            f32x4 v;
+            if constexpr (LACC) v = lacc[(q * NCH + k) * LNT + tid];
+            else v = q == 0 ? sg[k] : q == 1 ? sb[k] : q == 2 ? sr[k] : sx[k];
+            st4<float>(work + (q * nb + blockIdx.x) * cols + c, v);
+        }
     }
 }
 
