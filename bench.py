@@ -153,7 +153,7 @@ OTHER_WORKLOADS = [("g30b_t4", 5, 10), ("g30b_t1", 3, 5), ("bert4b", 30, 20)]  #
 def time_workload(name, dtype, W, K, keep=False):
     """ms per shard fwd+bwd step (HIP events around K steps after W warm-up steps, inputs resident)
     and algorithmic TFLOP/s of one other workload, shard 0.  With `keep` the workload's buffers are
-    returned instead of freed (the caller frees them later, off the GPU's busy path)."""
+    returned instead of freed, so that no free idles the GPU before the caller's next launches."""
     import torch
 
     from tensor_transformer_layer_02_amd.configs import CONFIGS, shard_flops
@@ -268,10 +268,9 @@ def main():
         ev = HipEvents(2 * len(tp.STEPS) * K)  # for the per-kernel pass below
     # ---- the other model shapes first (same run; the headline below keeps its own W and K).  The
     # headline's buffers already exist and the last workload's are kept until the process ends (a
-    # free would idle the GPU), so its W warm-up steps follow that workload's steps with the GPU kept
-    # busy: after even
-    # 20 ms of idle the clocks boost, overshoot and settle over ~30 steps, which a short warm-up
-    # would otherwise measure instead of the steady state.
+    # free would idle the GPU), so its W warm-up steps follow that workload's steps with the GPU
+    # kept busy: after even 20 ms of idle the clocks boost, overshoot and settle over ~30 steps,
+    # which a short warm-up would otherwise measure instead of the steady state.
     others, held = [], None
     if not args.no_others and args.config == "gpt8b" and not args.recompute:
         for i, (name, ow, ok) in enumerate(OTHER_WORKLOADS):
